@@ -1,0 +1,221 @@
+"""Plain float64 CPU oracle of Quest-style query-aware sparse attention.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).  Slow and literal on
+purpose: every function follows one passage of the pages and is written so a
+reader can check it against that passage by eye.  Nothing here is blocked,
+fused or reordered beyond what the definitions state.
+
+Sources (cited by page title and section / equation):
+  [Quest]      PaperTrace knowledge page "3.1.1 · Quest" (min/max page bounds).
+  [PageWeaver] Reading notes on "PageWeaver: KV-Guided Query Unions for
+               Sparse Attention" (support semantics, query unions).
+
+Notation follows the Quest page: S = tokens per page, P = pages of a
+request, K = pages selected, m/M = per-dimension key min/max of a page,
+U_p(q) = page bound.  Query head i reads KV head i // g, where g = H_q/H_kv
+(the grouping of consecutive query heads onto one KV head).
+
+Readings taken where the pages leave a step open (each one also listed in
+the design notes of the repository):
+  * GQA: the per-KV-head score is the max over the group's query heads of
+    their bounds ([Quest] §2.1, the group-max aggregate), which keeps eq. (4)
+    true for every head of the group.
+  * The score is the unscaled bound; no 1/sqrt(d) ([Quest] §1.1 notes the
+    ranking is unchanged by that scale).
+  * Top-K ties go to the lower page index; if K >= P all P pages are taken;
+    the selected list is returned in ascending page order.
+  * Only pages j < ceil(L/S) exist; a partially filled tail page is
+    summarised over its valid tokens only ([Quest] §1.2, tail length).
+  * Softmax scale 1/sqrt(d) ([PageWeaver] eq. (1)-(2)).
+  * Decode: the current token is already appended, so c = L - 1.
+"""
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- pages ----
+
+def num_pages(L, S):
+    """Pages holding at least one valid token: ceil(L / S)."""
+    return -(-int(L) // int(S))
+
+
+def page_summaries(keys, L, S):
+    """[Quest] §1.1 eq. (1): for every page p and dimension j,
+    m_{p,j} = min_r k_j^(r) and M_{p,j} = max_r k_j^(r), taken over the page's
+    valid tokens t < L only ([Quest] §1.2, the tail page's valid length).
+
+    keys: float64 [>= L][H_kv][d] in token order.  Returns (m, M), each
+    [P][H_kv][d] with P = ceil(L / S)."""
+    P = num_pages(L, S)
+    H, d = keys.shape[1], keys.shape[2]
+    m = np.empty((P, H, d))
+    M = np.empty((P, H, d))
+    for p in range(P):
+        block = keys[p * S: min((p + 1) * S, L)]
+        m[p] = block.min(axis=0)
+        M[p] = block.max(axis=0)
+    return m, M
+
+
+def append_to_summary(m_p, M_p, k, offset):
+    """[Quest] §1.2 eq. (8) and §3 eq. (14): write one key into its page.
+    A page receiving its first token (offset 0) starts from max = -inf and
+    min = +inf, so afterwards m = M = k.  Returns the new (m_p, M_p)."""
+    if offset == 0:
+        m_p = np.full_like(k, np.inf)
+        M_p = np.full_like(k, -np.inf)
+    return np.minimum(m_p, k), np.maximum(M_p, k)
+
+
+def replay_summaries(keys, L, S):
+    """The same summaries built incrementally, one token at a time, with
+    eq. (8); used to pin page_summaries (bulk build == incremental append)."""
+    P = num_pages(L, S)
+    H, d = keys.shape[1], keys.shape[2]
+    m = np.zeros((P, H, d))
+    M = np.zeros((P, H, d))
+    for t in range(L):
+        p, off = divmod(t, S)
+        m[p], M[p] = append_to_summary(m[p], M[p], keys[t], off)
+    return m, M
+
+
+# --------------------------------------------------------------- scores ----
+
+def head_bounds(q, m, M):
+    """[Quest] §1.1 eq. (2)-(3): for query head i (reading KV head i // g) and
+    page p, u_{p,j}(q) = max(q_j m_{p,j}, q_j M_{p,j}) and U_p(q) = sum_j u_{p,j}.
+
+    q: [H_q][d]; m, M: [P][H_kv][d].  Returns U: [H_q][P]."""
+    H_q, d = q.shape
+    P, H_kv, _ = m.shape
+    g = H_q // H_kv
+    U = np.empty((H_q, P))
+    for i in range(H_q):
+        h = i // g
+        u = np.maximum(q[i][None, :] * m[:, h, :], q[i][None, :] * M[:, h, :])
+        U[i] = u.sum(axis=1)
+    return U
+
+
+def kv_head_scores(U_heads, H_kv):
+    """[Quest] §2.1 (GQA): one shared page ranking per KV head, using the
+    group maximum U_{g,p} = max_{i in group} U_{i,p}.  U_heads: [H_q][P] ->
+    [H_kv][P]."""
+    H_q, P = U_heads.shape
+    g = H_q // H_kv
+    out = np.empty((H_kv, P))
+    for h in range(H_kv):
+        out[h] = U_heads[h * g:(h + 1) * g].max(axis=0)
+    return out
+
+
+# ---------------------------------------------------------------- top-K ----
+
+def top_k_pages(scores, K):
+    """[Quest] §1 / Fig. 1: the K pages with the largest bound.  Order is by
+    (score descending, page index ascending); min(K, P) pages are taken and
+    returned in ascending page order."""
+    scores = np.asarray(scores)
+    P = scores.shape[0]
+    order = sorted(range(P), key=lambda j: (-scores[j], j))
+    return sorted(order[:min(int(K), P)])
+
+
+# ------------------------------------------------------------ attention ----
+
+def support(page_ids, L, c, S):
+    """[PageWeaver] eq. (1)-(2) (support of query i): the tokens t with
+    floor(t/S) in the page set, 0 <= t < L and t <= c.  Page IDs outside
+    [0, ceil(L/S)) are ignored and a page listed twice counts once."""
+    P = num_pages(L, S)
+    ids = np.asarray(page_ids, dtype=np.int64).ravel()
+    pages = np.unique(ids[(ids >= 0) & (ids < P)])      # valid, each once
+    t = (pages[:, None] * S + np.arange(S)[None, :]).ravel()
+    return t[(t < L) & (t <= c)]
+
+
+def attend(q, keys, values, tokens, scale):
+    """[PageWeaver] eq. (1)-(2): z_t = scale * q . k_t over the support, then
+    o = sum_t e^{z_t} v_t / sum_t e^{z_t}.  An empty support gives o = 0.
+    Also returns lse = log sum_t e^{z_t} (-inf for an empty support), the
+    quantity a log-sum-exp merge of partial results combines.
+
+    q: [d]; keys, values: [T][d] (one KV head); tokens: indices into them."""
+    d = values.shape[1]
+    if len(tokens) == 0:
+        return np.zeros(d), -np.inf
+    k = keys[tokens]
+    v = values[tokens]
+    z = scale * (k @ q)
+    zmax = z.max()
+    w = np.exp(z - zmax)
+    o = (w @ v) / w.sum()
+    return o, zmax + math.log(w.sum())
+
+
+def decode_request(q, keys, values, L, S, K, scale=None, page_ids=None):
+    """One decode step of one request, all heads: summaries (eq. (1)), head
+    bounds (eq. (2)-(3)), KV-head scores (group max), top-K, then exact
+    attention over each query head's support with c = L - 1.
+
+    q: [H_q][d]; keys, values: [>= L][H_kv][d] float64.  If ``page_ids``
+    ([H_kv][*]) is given it replaces the top-K lists (attention over given
+    page sets).  Returns a dict of every intermediate."""
+    H_q, d = q.shape
+    H_kv = keys.shape[1]
+    g = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m, M = page_summaries(keys, L, S)
+    U_heads = head_bounds(q, m, M)
+    U = kv_head_scores(U_heads, H_kv)
+    sel = [top_k_pages(U[h], K) for h in range(H_kv)]
+    lists = sel if page_ids is None else page_ids
+    out = np.zeros((H_q, d))
+    lse = np.zeros(H_q)
+    for i in range(H_q):
+        h = i // g
+        A = support(lists[h], L, L - 1, S)
+        out[i], lse[i] = attend(q[i], keys[:, h, :], values[:, h, :], A, scale)
+    return {"m": m, "M": M, "U_heads": U_heads, "U": U, "sel": sel,
+            "out": out, "lse": lse}
+
+
+# ----------------------------------------------------------- query union ---
+
+def union_with_membership(page_sets):
+    """[PageWeaver] query union: U_G = union of the group's page sets, and for
+    every row r of the group and union page p a membership bit
+    1[p in S_r].  Returns (sorted union list, membership [rows][len(U_G)])."""
+    union = sorted({int(p) for s in page_sets for p in s})
+    member = np.zeros((len(page_sets), len(union)), dtype=np.uint8)
+    for r, s in enumerate(page_sets):
+        s = {int(p) for p in s}
+        for u, p in enumerate(union):
+            member[r, u] = 1 if p in s else 0
+    return union, member
+
+
+def chunk_attention(q, keys, values, sets, L, c, S, g, scale=None):
+    """Multi-query chunk ([PageWeaver] eq. (1)-(2)): every query position n has
+    its own page set per KV head, its own length L[n] and causal limit c[n].
+    Executing queries as unions with membership masks does not change the
+    result, so the definition is applied per query and head.
+
+    q: [N][H_q][d]; keys, values: [T][H_kv][d]; sets: [N][H_kv][*].
+    Returns (out [N][H_q][d], lse [N][H_q])."""
+    N, H_q, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((N, H_q, d))
+    lse = np.zeros((N, H_q))
+    for n in range(N):
+        for i in range(H_q):
+            h = i // g
+            A = support(sets[n][h], L[n], c[n], S)
+            out[n, i], lse[n, i] = attend(q[n, i], keys[:, h, :],
+                                          values[:, h, :], A, scale)
+    return out, lse

@@ -1,0 +1,360 @@
+"""Pins of the oracle to facts the pages and the mathematics fix.
+
+Each test would fail for a plausible mistake in oracle/quest.py: swapped
+min/max or sign selection (worked example, closed form, box corners), a
+wrong GQA head mapping (per-head invariant), a padded tail page (tail pins),
+a wrong softmax scale or causal limit (library attention), a wrong tie rule
+(all-equal and brute-force top-K), duplicate or invalid pages counted
+(invariance tests)."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quest, run_decode
+from tests.conftest import load_golden
+from workloads import config1, config2, config3, figure2_case, worked_example_case
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------- the pages' examples ----
+
+def test_worked_example_summary_and_bound():
+    g = load_golden("quest_worked_example.json")
+    keys = np.array(g["keys"], float)[:, None, :]
+    m, M = quest.page_summaries(keys, len(keys), S=len(keys))
+    assert m[0, 0].tolist() == g["m"]
+    assert M[0, 0].tolist() == g["M"]
+    q = np.array([g["q"]], float)
+    U = quest.head_bounds(q, m, M)
+    assert U[0, 0] == g["U"]
+    assert (keys[:, 0] @ q[0]).tolist() == g["dots"]
+    # the alternative keys share the summary and the bound, not the max dot
+    alt = np.array(g["alt_keys"], float)[:, None, :]
+    m2, M2 = quest.page_summaries(alt, len(alt), S=len(alt))
+    assert quest.head_bounds(q, m2, M2)[0, 0] == g["alt_U"]
+    assert (alt[:, 0] @ q[0]).tolist() == g["alt_dots"]
+    assert max(g["alt_dots"]) < g["alt_U"]
+
+
+def test_figure2_two_steps():
+    g = load_golden("quest_figure2.json")
+    S = g["page_capacity"]
+    A = np.array(g["keys_A"], float)
+    B = np.array(g["keys_B"], float)
+    keys = np.concatenate([A, B])[:, None, :]
+    L = len(keys)
+    m, M = quest.page_summaries(keys, L, S)
+    q_t = np.array([g["q_t"]], float)
+    U = quest.head_bounds(q_t, m, M)[0]
+    assert U.tolist() == [g["U_A_t"], g["U_B_t"]]
+    assert quest.top_k_pages(U, 1) == [0]            # page A
+    q_t1 = np.array([g["q_t1"]], float)
+    assert quest.head_bounds(q_t1, m, M)[0, 1] == g["U_B_t1_without_append"]
+    # append (-2, 5) to B with eq. (8)
+    k_new = np.array(g["appended_to_B"], float)[None, :]
+    mB, MB = quest.append_to_summary(m[1], M[1], k_new, offset=L % S)
+    assert mB[0].tolist() == g["m_B_after"] and MB[0].tolist() == g["M_B_after"]
+    m2, M2 = m.copy(), M.copy()
+    m2[1], M2[1] = mB, MB
+    U1 = quest.head_bounds(q_t1, m2, M2)[0]
+    assert U1.tolist() == [g["U_A_t1"], g["U_B_t1"]]
+    assert quest.top_k_pages(U1, 1) == [1]           # page B
+    # bulk summaries over the three-token B agree with the append
+    keys3 = np.concatenate([keys, k_new[:, None, :]])
+    mb, Mb = quest.page_summaries(keys3, L + 1, S)
+    assert np.array_equal(mb[1], mB) and np.array_equal(Mb[1], MB)
+
+
+def test_figure2_case_padded_layout():
+    """The zero-padded d=16 / S=4 workload built from the same reading gives
+    the printed bounds through the whole-request oracle."""
+    case = figure2_case()
+    r0 = run_decode(case, step=-1)[0]
+    assert r0["U"][0].tolist() == [8.0, 0.0] and r0["sel"] == [[0]]
+    r1 = run_decode(case, step=0)[0]
+    assert r1["U"][0].tolist() == [1.0, 5.0] and r1["sel"] == [[1]]
+
+
+def test_worked_example_case_padded():
+    for second in (False, True):
+        r = run_decode(worked_example_case(second_set=second))[0]
+        assert r["U"][0, 0] == 8.0
+
+
+def test_four_page_topk():
+    g = load_golden("quest_four_pages.json")
+    bound = np.array(g["bound"], float)
+    names = g["pages"]
+    assert [names[j] for j in quest.top_k_pages(bound, 2)] == g["selected_K2"]
+    assert [names[j] for j in quest.top_k_pages(bound, 3)] == g["selected_K3"]
+    # the bound is valid (never below the true max) even where recall fails
+    assert np.all(bound >= np.array(g["true_max"]))
+
+
+def test_union_and_membership_example():
+    g = load_golden("pageweaver_union.json")
+    sets = [g["sets"]["q0"], g["sets"]["q2"]]
+    union, member = quest.union_with_membership(sets)
+    assert union == g["union"]
+    for row, name in enumerate(("q0", "q2")):
+        masked = [p for u, p in enumerate(union) if member[row, u] == 0]
+        assert masked == g["masked"][name]
+
+
+# ---------------------------------------------------- closed forms, bounds --
+
+def test_bound_closed_form():
+    """A box's support function is q.(M+m)/2 + |q|.(M-m)/2."""
+    rng = _rng(1)
+    for _ in range(20):
+        d, P = int(rng.integers(1, 40)), int(rng.integers(1, 9))
+        a, b = rng.normal(size=(2, P, 1, d))
+        m, M = np.minimum(a, b), np.maximum(a, b)
+        q = rng.normal(size=(1, d))
+        U = quest.head_bounds(q, m, M)[0]
+        closed = (m[:, 0] + M[:, 0]) @ q[0] / 2 + (M[:, 0] - m[:, 0]) @ np.abs(q[0]) / 2
+        np.testing.assert_allclose(U, closed, rtol=1e-12, atol=1e-12)
+
+
+def test_bound_equals_max_over_box_corners():
+    """Brute force: the bound equals the largest dot product over all 2^d
+    corners of the box [m, M] (the Quest page, §3.1, support function)."""
+    rng = _rng(2)
+    d = 10
+    for _ in range(5):
+        a, b = rng.normal(size=(2, 1, 1, d))
+        m, M = np.minimum(a, b), np.maximum(a, b)
+        q = rng.normal(size=(1, d))
+        best = -np.inf
+        for corner in itertools.product((0, 1), repeat=d):
+            c = np.where(np.array(corner) == 1, M[0, 0], m[0, 0])
+            best = max(best, float(c @ q[0]))
+        assert abs(quest.head_bounds(q, m, M)[0, 0] - best) < 1e-12
+
+
+def test_bound_invariant_and_tightness():
+    """eq. (4): U_p(q) >= q.k for every key of the page; a one-token page is
+    tight."""
+    rng = _rng(3)
+    for S in (1, 3, 16):
+        keys = rng.normal(size=(S * 20, 2, 32))
+        L = keys.shape[0]
+        m, M = quest.page_summaries(keys, L, S)
+        q = rng.normal(size=(4, 32))            # g = 2
+        U = quest.head_bounds(q, m, M)
+        for i in range(4):
+            h = i // 2
+            dots = (keys[:, h, :] @ q[i]).reshape(-1, S).max(axis=1)
+            assert np.all(U[i] >= dots - 1e-12)
+            if S == 1:
+                np.testing.assert_allclose(U[i], dots, rtol=1e-12, atol=1e-12)
+
+
+def test_bound_homogeneity_and_zero_query():
+    rng = _rng(4)
+    keys = rng.normal(size=(64, 1, 8))
+    m, M = quest.page_summaries(keys, 64, 16)
+    q = rng.normal(size=(1, 8))
+    U = quest.head_bounds(q, m, M)
+    np.testing.assert_allclose(quest.head_bounds(2.5 * q, m, M), 2.5 * U, rtol=1e-12)
+    assert np.all(quest.head_bounds(0 * q, m, M) == 0)
+
+
+def test_gqa_group_score_bounds_every_head():
+    """The shared per-KV-head score bounds the true max logit of every query
+    head of the group (eq. (4) per head), is attained by one of them, and
+    with g = 1 is the head's own bound."""
+    rng = _rng(5)
+    H_kv, g, S, d = 3, 4, 8, 16
+    keys = rng.normal(size=(S * 12, H_kv, d)) * np.arange(1, H_kv + 1)[None, :, None]
+    m, M = quest.page_summaries(keys, keys.shape[0], S)
+    q = rng.normal(size=(H_kv * g, d))
+    U_heads = quest.head_bounds(q, m, M)
+    U = quest.kv_head_scores(U_heads, H_kv)
+    for i in range(H_kv * g):
+        h = i // g
+        dots = (keys[:, h, :] @ q[i]).reshape(-1, S).max(axis=1)
+        assert np.all(U[h] >= dots - 1e-12)
+    for h in range(H_kv):
+        grp = U_heads[h * g:(h + 1) * g]
+        assert np.all(np.any(np.abs(grp - U[h]) == 0, axis=0))
+    one = quest.kv_head_scores(U_heads[:H_kv], H_kv)
+    assert np.array_equal(one, U_heads[:H_kv])
+
+
+# ------------------------------------------------------------- summaries ----
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 33, 100])
+def test_summaries_bulk_equals_replay(L):
+    rng = _rng(6 + L)
+    keys = rng.normal(size=(L + 5, 2, 8))
+    m, M = quest.page_summaries(keys, L, 16)
+    m2, M2 = quest.replay_summaries(keys, L, 16)
+    assert np.array_equal(m, m2) and np.array_equal(M, M2)
+    assert m.shape[0] == quest.num_pages(L, 16) == (L + 15) // 16
+
+
+def test_tail_page_uses_valid_tokens_only():
+    """Lengths 1, 15, 16, 17 at S = 16 (the Quest page, §1.2, tail length):
+    tokens at or beyond L never enter a summary."""
+    rng = _rng(7)
+    keys = rng.normal(size=(32, 1, 4))
+    poisoned = keys.copy()
+    for L, pages, last_len in ((1, 1, 1), (15, 1, 15), (16, 1, 16), (17, 2, 1)):
+        poisoned[L:] = 1e9 * np.sign(rng.normal(size=poisoned[L:].shape))
+        m, M = quest.page_summaries(poisoned, L, 16)
+        assert m.shape[0] == pages
+        tail = keys[(pages - 1) * 16:(pages - 1) * 16 + last_len]
+        assert np.array_equal(m[-1], tail.min(axis=0))
+        assert np.array_equal(M[-1], tail.max(axis=0))
+        poisoned[:] = keys
+    m, M = quest.page_summaries(keys, 17, 16)
+    assert np.array_equal(m[1], keys[16]) and np.array_equal(M[1], keys[16])
+
+
+# ----------------------------------------------------------------- top-K ----
+
+def test_topk_bruteforce_with_ties():
+    rng = _rng(8)
+    for _ in range(30):
+        P = int(rng.integers(1, 40))
+        s = rng.integers(-3, 4, size=P).astype(float)   # many exact ties
+        for K in range(1, P + 3):
+            sel = quest.top_k_pages(s, K)
+            assert len(sel) == min(K, P) and sel == sorted(sel)
+            assert len(set(sel)) == len(sel)
+            out = [j for j in range(P) if j not in sel]
+            for i in sel:
+                for j in out:
+                    assert (s[i] > s[j]) or (s[i] == s[j] and i < j)
+
+
+def test_topk_all_equal_and_all_pages():
+    assert quest.top_k_pages(np.zeros(10), 3) == [0, 1, 2]
+    assert quest.top_k_pages(np.arange(5.0), 9) == [0, 1, 2, 3, 4]
+
+
+# ------------------------------------------------------------- attention ----
+
+def _sdpa(q, k, v, scale):
+    """Library attention (torch, float64, CPU) over the whole given keys."""
+    qt = torch.tensor(q, dtype=torch.float64)[None, None, None, :]
+    kt = torch.tensor(k, dtype=torch.float64)[None, None]
+    vt = torch.tensor(v, dtype=torch.float64)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    z = (kt[0, 0] @ qt[0, 0, 0]) * scale
+    return o[0, 0, 0].numpy(), float(torch.logsumexp(z, 0))
+
+
+def test_all_pages_is_dense_attention():
+    """The Quest page, §1.2: a budget of all pages reproduces dense paged
+    attention.  Checked against torch's scaled_dot_product_attention with
+    its default 1/sqrt(d) scale."""
+    rng = _rng(9)
+    for L, S in ((64, 4), (37, 16), (1, 16)):
+        d = 16
+        keys = rng.normal(size=(L, 1, d))
+        values = rng.normal(size=(L, 1, d))
+        q = rng.normal(size=(1, d))
+        P = quest.num_pages(L, S)
+        res = quest.decode_request(q, keys, values, L, S, K=P)
+        o_ref, lse_ref = _sdpa(q[0], keys[:, 0], values[:, 0], 1 / math.sqrt(d))
+        np.testing.assert_allclose(res["out"][0], o_ref, rtol=1e-12, atol=1e-12)
+        assert abs(res["lse"][0] - lse_ref) < 1e-10
+
+
+def test_causal_limit_is_inclusive():
+    """Support keeps t <= c: equals dense attention over the first c+1 keys."""
+    rng = _rng(10)
+    L, S, d = 40, 8, 8
+    keys = rng.normal(size=(L, d))
+    values = rng.normal(size=(L, d))
+    q = rng.normal(size=d)
+    for c in (0, 7, 8, 20, 39):
+        A = quest.support(range(quest.num_pages(L, S)), L, c, S)
+        o, lse = quest.attend(q, keys, values, A, 1 / math.sqrt(d))
+        o_ref, lse_ref = _sdpa(q, keys[:c + 1], values[:c + 1], 1 / math.sqrt(d))
+        np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+        assert abs(lse - lse_ref) < 1e-10
+
+
+def test_zero_query_gives_mean_and_single_token_gives_value():
+    rng = _rng(11)
+    keys = rng.normal(size=(32, 4))
+    values = rng.normal(size=(32, 4))
+    A = quest.support([0, 2], 32, 31, 8)
+    o, _ = quest.attend(np.zeros(4), keys, values, A, 0.5)
+    np.testing.assert_allclose(o, values[A].mean(axis=0), rtol=1e-12)
+    A1 = quest.support([3], 25, 24, 8)             # page 3 holds only t = 24
+    assert list(A1) == [24]
+    o1, _ = quest.attend(rng.normal(size=4), keys, values, A1, 0.5)
+    np.testing.assert_allclose(o1, values[24], rtol=1e-12)
+
+
+def test_support_ignores_order_duplicates_invalid_and_empty_is_zero():
+    rng = _rng(12)
+    L, S, d = 50, 8, 4                              # 7 pages
+    keys = rng.normal(size=(L, d))
+    values = rng.normal(size=(L, d))
+    q = rng.normal(size=d)
+    base = quest.attend(q, keys, values, quest.support([1, 3, 6], L, L - 1, S), 0.5)
+    for ids in ([6, 1, 3], [3, 3, 1, 6, 1], [1, -1, 3, 7, 6, 2**31 - 1, -7, 12]):
+        o, lse = quest.attend(q, keys, values, quest.support(ids, L, L - 1, S), 0.5)
+        np.testing.assert_array_equal(o, base[0])
+        assert lse == base[1]
+    for ids in ([], [-1, 7, 100], [5] if False else [-3]):
+        o, lse = quest.attend(q, keys, values, quest.support(ids, L, L - 1, S), 0.5)
+        assert np.array_equal(o, np.zeros(d)) and lse == -np.inf
+
+
+def test_sparse_output_error_bound_eq7():
+    """The Quest page, §1.1 eq. (6)-(7): |o - o_C| <= 2 eps V_max, with eps the
+    dense probability mass outside C."""
+    rng = _rng(13)
+    L, S, d = 256, 16, 16
+    for _ in range(10):
+        keys = rng.normal(size=(L, d)) * 2
+        values = rng.normal(size=(L, d))
+        q = rng.normal(size=d)
+        scale = 1 / math.sqrt(d)
+        pages = rng.choice(L // S, size=5, replace=False)
+        C = quest.support(pages, L, L - 1, S)
+        o_C, _ = quest.attend(q, keys, values, C, scale)
+        o, _ = quest.attend(q, keys, values, np.arange(L), scale)
+        z = scale * keys @ q
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        eps = 1 - p[C].sum()
+        vmax = np.linalg.norm(values, axis=1).max()
+        assert np.linalg.norm(o - o_C) <= 2 * eps * vmax + 1e-12
+
+
+def test_chunk_attention_per_query_matches_decode_definition():
+    """A chunk query with c = L-1 and the request's own page list is exactly
+    the decode result; executing as a union does not change the result."""
+    case = config1()
+    keys = case.keys[0].astype(np.float64)
+    values = case.values[0].astype(np.float64)
+    q = case.q[0, 0].astype(np.float64)
+    res = quest.decode_request(q, keys, values, 64, 4, 4)
+    sets = np.array([[res["sel"][0]]])
+    out, lse = quest.chunk_attention(q[None], keys, values, sets, [64], [63], 4, 1)
+    np.testing.assert_array_equal(out[0], res["out"])
+
+
+def test_workload_cases_are_well_formed():
+    c1 = config1()
+    assert c1.keys[0].shape == (64, 1, 16) and c1.K == 4
+    assert sorted(c1.pages[0].tolist()) == sorted(set(c1.pages[0].tolist()))
+    c2 = config2(L=256, H=2)
+    assert c2.keys[0].dtype == np.float16 and c2.keys[0].shape == (256, 2, 128)
+    c3 = config3(B=2, L_min=40, L_max=70, steps=3)
+    assert all(k.shape[0] == L + 3 for k, L in zip(c3.keys, c3.seq_lens))
+    flat = np.concatenate(c3.pages)
+    assert len(set(flat.tolist())) == len(flat) and flat.max() < c3.num_pool_pages
