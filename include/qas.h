@@ -1,0 +1,216 @@
+/*
+ * qas.h - C ABI of libqas.so: query-aware sparse attention over a paged KV
+ * cache (Quest-style page selection), hand-written HIP for gfx950.
+ *
+ * Sources are cited by page title and section / equation:
+ *   [Quest]      PaperTrace knowledge page "3.1.1 · Quest".
+ *   [PageWeaver] Reading notes on "PageWeaver: KV-Guided Query Unions for
+ *                Sparse Attention".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership.  Every buffer is owned by the caller.  Pointers documented as
+ *   "device" must point to device memory of the current HIP device; the
+ *   library keeps no pointer after a call returns and allocates no memory
+ *   (scratch space is passed in as a workspace).  The library has no global
+ *   state apart from a thread-local error string, and may be called from
+ *   several threads.
+ * Execution.  Work is enqueued asynchronously on `stream` (a hipStream_t
+ *   passed as void*; NULL is the null stream).  No call synchronises.
+ * Errors.  Argument problems are reported with a non-zero qas_status
+ *   before anything is enqueued; the detail is available from
+ *   qas_last_error() on the same thread.  A failed launch returns
+ *   QAS_ERR_HIP.  No C++ exception crosses the ABI.
+ * Not errors.  Page IDs in selected lists that are negative, beyond the
+ *   request's pages, or repeated are semantics, not errors ([PageWeaver]
+ *   eq. (1)-(2): invalid IDs are ignored, duplicates count once, an empty
+ *   support gives a zero output).
+ * Caller contract.  Physical page numbers in page tables must lie in
+ *   [0, num_pool_pages); lengths must be covered by the page tables.
+ *   Violations are undefined behaviour (they are not checked on the device).
+ *
+ * Layouts (row-major, innermost last)
+ * -----------------------------------
+ *   K / V pool  [num_pool_pages][H_kv][S][d]          kv_dtype
+ *   summary     [num_pool_pages][H_kv][2][d]          kv_dtype, [..][0] = min m,
+ *                                                     [..][1] = max M ([Quest] eq. (1))
+ *   q, out      [B][H_q][d]                           q_dtype (out has q's dtype)
+ *   lse         [B][H_q]                              float, natural log of the
+ *                                                     softmax denominator
+ *   scores      request r, KV head h, logical page j at
+ *               page_indptr[r]*H_kv + h*P_r + j, P_r = page_indptr[r+1]-page_indptr[r]
+ *   selected    [B][H_kv][stride] int32 logical page IDs
+ * Query head i reads KV head i / (H_q / H_kv).
+ */
+#ifndef QAS_H
+#define QAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qas_status {
+  QAS_OK = 0,
+  QAS_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  QAS_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree        */
+  QAS_ERR_DTYPE = 3,       /* dtype not accepted for this operand             */
+  QAS_ERR_UNSUPPORTED = 4, /* valid request outside this build (e.g. head_dim) */
+  QAS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+  QAS_ERR_HIP = 6          /* a HIP runtime call or launch failed             */
+} qas_status;
+
+typedef enum qas_dtype {
+  QAS_F32 = 0,
+  QAS_F16 = 1,            /* IEEE binary16                                   */
+  QAS_BF16 = 2,           /* bfloat16                                        */
+  QAS_FP8_E4M3 = 3        /* OCP FP8 E4M3 (finite variant), with per-KV-head scale */
+} qas_dtype;
+
+/* Paged KV cache of one layer. */
+typedef struct qas_cache {
+  int32_t page_size;      /* S, tokens per page: a power of two in [1, 256]   */
+  int32_t head_dim;       /* d: 16, 64 or 128                                 */
+  int32_t num_kv_heads;   /* H_kv >= 1                                        */
+  int32_t num_pool_pages; /* physical pages in the pool                      */
+  int32_t kv_dtype;       /* qas_dtype of K, V and the summaries             */
+  int32_t reserved;
+  void* k_pool;           /* device [num_pool_pages][H_kv][S][d]              */
+  void* v_pool;           /* device [num_pool_pages][H_kv][S][d]              */
+  void* summary;          /* device [num_pool_pages][H_kv][2][d]              */
+  const float* k_scale;   /* device [H_kv] dequantisation scales (fp8 only, else NULL) */
+  const float* v_scale;   /* device [H_kv]                                    */
+} qas_cache;
+
+/* A batch of B requests (ragged, [Quest] §2.1 continuous batching). */
+typedef struct qas_batch {
+  int32_t batch;              /* B >= 1                                       */
+  int32_t total_pages;        /* page_indptr[B] (host copy, for sizing)       */
+  int32_t max_pages;          /* max_r P_r (host copy, for launch sizing)     */
+  int32_t reserved;
+  const int32_t* seq_lens;    /* device [B]: valid tokens L_r of each request */
+  const int32_t* page_indptr; /* device [B+1]: CSR offsets into page_indices  */
+  const int32_t* page_indices;/* device [total_pages]: physical page of logical
+                                 page j of request r at page_indptr[r] + j    */
+} qas_batch;
+
+/*
+ * qas_append - write new tokens' K/V rows into the pool and maintain the
+ * per-page key min/max summaries ([Quest] §1.2 eq. (8), §3 eq. (14)).
+ *
+ * batch->seq_lens are the lengths BEFORE the append; request r receives
+ * n_r = new_indptr[r+1] - new_indptr[r] tokens at positions
+ * seq_lens[r] .. seq_lens[r] + n_r - 1, whose pages must already be in the
+ * page table.  A page whose offset-0 token is among the new ones starts
+ * from max = -inf / min = +inf (so a recycled physical page never keeps
+ * stale extremes); otherwise the existing summary is extended.  Covers both
+ * the prefill bulk build (n_r = L_r on empty requests) and single-token
+ * decode appends (n_r = 1).  seq_lens is not modified.
+ *
+ *   new_indptr  device [B+1]
+ *   total_new   = new_indptr[B] (host)
+ *   max_new     >= max_r n_r (host, for launch sizing)
+ *   k_new/v_new device [total_new][H_kv][d], kv_dtype
+ */
+qas_status qas_append(const qas_cache* cache, const qas_batch* batch,
+                      const int32_t* new_indptr, int32_t total_new,
+                      int32_t max_new, const void* k_new, const void* v_new,
+                      void* stream);
+
+/*
+ * qas_score_pages - page bounds of the current queries ([Quest] §1.1
+ * eq. (2)-(3)): U_{h,j} = max over the query heads i of KV head h of
+ * sum_d max(q_{i,d} m_{j,d}, q_{i,d} M_{j,d}), unscaled, fp32 accumulate
+ * ([Quest] §2.1 group-max aggregate for GQA).  Pages j < ceil(L_r/S) are
+ * scored; allocated pages beyond them get -inf.
+ *
+ *   q        device [B][H_q][d], q_dtype == kv_dtype (f32/f16/bf16)
+ *   scores   device float, layout above (total_pages * H_kv floats)
+ */
+qas_status qas_score_pages(const qas_cache* cache, const qas_batch* batch,
+                           const void* q, int32_t q_dtype, int32_t num_q_heads,
+                           float* scores, void* stream);
+
+/*
+ * qas_topk_pages - per (request, KV head) the min(k, ceil(L_r/S)) pages with
+ * the largest score, ordered by (score descending, page index ascending);
+ * written in ascending page order and padded with -1 ([Quest] §1, Fig. 1
+ * Top-K stage).  -0.0 and +0.0 are equal scores.  NaN scores are not
+ * supported.
+ *
+ *   scores     device float, layout of qas_score_pages
+ *   sel        device [B][H_kv][k] int32
+ *   sel_count  device [B][H_kv] int32, may be NULL
+ *   Rows longer than 15360 pages return QAS_ERR_UNSUPPORTED.
+ */
+qas_status qas_topk_pages(const float* scores, const qas_batch* batch,
+                          int32_t num_kv_heads, int32_t page_size, int32_t k,
+                          int32_t* sel, int32_t* sel_count, void* stream);
+
+/*
+ * qas_sparse_decode - exact softmax attention of each query head over its
+ * support ([PageWeaver] eq. (1)-(2); [Quest] §2.1 paged sparse load):
+ * A = { t : floor(t/S) in the KV head's selected list, t < L_r } (decode,
+ * c = L_r - 1), z_t = sm_scale * q . k_t, out = sum softmax(z)_t v_t.
+ * Selected lists may hold duplicates, invalid IDs and any order; an empty
+ * support gives out = 0 and lse = -inf.  K/V are read in place through the
+ * page table (no gather copy); split-page partial softmax states are merged
+ * with log-sum-exp.
+ *
+ *   sel        device [B][H_kv][sel_stride] int32, first sel_len used per row
+ *   out        device [B][H_q][d], q_dtype
+ *   lse        device [B][H_q] float, may be NULL
+ *   workspace  device, >= qas_workspace_bytes(QAS_OP_SPARSE_DECODE, ...)
+ */
+qas_status qas_sparse_decode(const qas_cache* cache, const qas_batch* batch,
+                             const void* q, int32_t q_dtype,
+                             int32_t num_q_heads, const int32_t* sel,
+                             int32_t sel_stride, int32_t sel_len,
+                             float sm_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * qas_decode_layer - one decode-layer call of the whole path: optional
+ * append of the current token, page scores, top-k, sparse attention.
+ * If k_new/v_new (device [B][H_kv][d], kv_dtype) are given, the token at
+ * position seq_lens[r] - 1 of each request is appended first (seq_lens
+ * already count it).  sel_out (device [B][H_kv][k] int32) may be NULL;
+ * otherwise it receives the selected lists.  Other arguments as in the
+ * calls above.
+ */
+qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch,
+                            const void* q, int32_t q_dtype,
+                            int32_t num_q_heads, int32_t k, float sm_scale,
+                            const void* k_new, const void* v_new,
+                            int32_t* sel_out, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+enum { QAS_OP_SPARSE_DECODE = 1, QAS_OP_DECODE_LAYER = 2 };
+
+/*
+ * qas_workspace_bytes - workspace size an operation needs for these
+ * arguments (k = sel_len for QAS_OP_SPARSE_DECODE, the budget for
+ * QAS_OP_DECODE_LAYER).  Returns 0 for invalid arguments.
+ */
+size_t qas_workspace_bytes(int32_t op, const qas_cache* cache,
+                           const qas_batch* batch, int32_t num_q_heads,
+                           int32_t k);
+
+/* Static description of a status code. */
+const char* qas_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* qas_last_error(void);
+
+/* Library version string. */
+const char* qas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QAS_H */

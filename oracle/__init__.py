@@ -34,17 +34,28 @@ def _decoded_kv(case, r, upto=None):
     return keys, values
 
 
-def run_decode(case, step=-1, page_ids=None, requests=None):
+def decoded_kv(case, r):
+    """float64 keys and values of request r (all T_r tokens), for reuse over
+    several calls of run_decode."""
+    return _decoded_kv(case, r)
+
+
+def run_decode(case, step=-1, page_ids=None, requests=None, decoded=None):
     """Oracle of one decode call of a DecodeCase: the call before the first
     append (step=-1) or the call after step ``step``'s append.  ``page_ids``
-    ([B][H_kv][*]) replaces the top-K lists.  Returns one result dict per
-    request (see quest.decode_request)."""
+    ([B][H_kv][*]) replaces the top-K lists.  ``decoded`` optionally maps a
+    request to decoded_kv(case, r).  Returns one result dict per request (see
+    quest.decode_request)."""
     lengths = case.lengths(step)
     q_all = decode(case.q[step + 1], case.q_dtype)
     out = []
     for r in (range(case.B) if requests is None else requests):
         L = int(lengths[r])
-        keys, values = _decoded_kv(case, r, L)
+        if decoded is not None and r in decoded:
+            keys, values = decoded[r]
+            keys, values = keys[:L], values[:L]
+        else:
+            keys, values = _decoded_kv(case, r, L)
         res = quest.decode_request(q_all[r], keys, values, L, case.S, case.K,
                                    scale=case.sm_scale,
                                    page_ids=None if page_ids is None else page_ids[r])
@@ -68,4 +79,4 @@ def run_chunk(case, queries=None):
                                  case.g, scale=case.sm_scale)
 
 
-__all__ = ["formats", "quest", "decode", "run_decode", "run_chunk"]
+__all__ = ["formats", "quest", "decode", "decoded_kv", "run_decode", "run_chunk"]

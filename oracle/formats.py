@@ -57,6 +57,22 @@ def decode_e4m3fn(codes):
     return np.where(nan, np.nan, out)
 
 
+_TABLES = {}
+
+
+def _table(dtype):
+    """Every code of a 16- or 8-bit format decoded once by the decoders above;
+    decoding a large array is then a table lookup (same values)."""
+    if dtype not in _TABLES:
+        if dtype == "f16":
+            _TABLES[dtype] = decode_fp16(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16))
+        elif dtype == "bf16":
+            _TABLES[dtype] = decode_bf16(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16))
+        else:
+            _TABLES[dtype] = decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    return _TABLES[dtype]
+
+
 def decode(raw, dtype):
     """Decode a stored array of the named dtype ('f32', 'f16', 'bf16', 'e4m3')
     to float64.  'f16' arrays may be given as numpy float16 or uint16 bits."""
@@ -66,9 +82,9 @@ def decode(raw, dtype):
     if dtype == "f16":
         if raw.dtype == np.float16:
             raw = raw.view(np.uint16)
-        return decode_fp16(raw)
+        return _table("f16")[raw]
     if dtype == "bf16":
-        return decode_bf16(raw)
+        return _table("bf16")[raw.view(np.uint16)]
     if dtype == "e4m3":
-        return decode_e4m3fn(raw)
+        return _table("e4m3")[raw.view(np.uint8)]
     raise ValueError(f"unknown dtype {dtype!r}")

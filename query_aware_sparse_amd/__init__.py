@@ -1,0 +1,169 @@
+"""Python binding of libqas (query-aware sparse attention over a paged KV
+cache, HIP for gfx950).
+
+Argument marshalling only: every function below forwards torch tensors'
+device pointers and the current HIP stream to the C entry point of the same
+name declared in include/qas.h.  All computation runs in the library's HIP
+kernels; there is no fallback path, and importing this package fails loudly
+if libqas.so has not been built (``python -m query_aware_sparse_amd.build``).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqas.so")
+
+QAS_OK = 0
+QAS_F32, QAS_F16, QAS_BF16, QAS_FP8_E4M3 = 0, 1, 2, 3
+QAS_OP_SPARSE_DECODE, QAS_OP_DECODE_LAYER = 1, 2
+
+_TORCH_DTYPE = {torch.float32: QAS_F32, torch.float16: QAS_F16,
+                torch.bfloat16: QAS_BF16, torch.float8_e4m3fn: QAS_FP8_E4M3}
+
+
+class QasError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"qas status {status}: {detail}")
+        self.status = status
+
+
+class qas_cache(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("num_pool_pages", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("summary", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
+
+
+class qas_batch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("total_pages", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("page_indptr", ctypes.c_void_p),
+                ("page_indices", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGNATURES = {
+    "qas_append": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
+    "qas_score_pages": (_I, [_P, _P, _P, _I, _I, _P, _P]),
+    "qas_topk_pages": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "qas_sparse_decode": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, ctypes.c_float,
+                               _P, _P, _P, ctypes.c_size_t, _P]),
+    "qas_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
+                              _P, _P, _P, ctypes.c_size_t, _P]),
+    "qas_workspace_bytes": (ctypes.c_size_t, [_I, _P, _P, _I, _I]),
+    "qas_status_string": (ctypes.c_char_p, [_I]),
+    "qas_last_error": (ctypes.c_char_p, []),
+    "qas_version": (ctypes.c_char_p, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m query_aware_sparse_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status):
+    if status != QAS_OK:
+        raise QasError(status, lib.qas_last_error().decode())
+
+
+def dtype_code(t):
+    return _TORCH_DTYPE[t.dtype]
+
+
+def make_cache(k_pool, v_pool, summary, k_scale=None, v_scale=None):
+    """qas_cache over caller-owned tensors: pools [pages][H_kv][S][d],
+    summary [pages][H_kv][2][d].  The tensors must outlive every call."""
+    pages, H_kv, S, d = k_pool.shape
+    c = qas_cache(S, d, H_kv, pages, dtype_code(k_pool), 0, k_pool.data_ptr(),
+                  v_pool.data_ptr(), 0 if summary is None else summary.data_ptr(),
+                  0 if k_scale is None else k_scale.data_ptr(),
+                  0 if v_scale is None else v_scale.data_ptr())
+    c._keep = (k_pool, v_pool, summary, k_scale, v_scale)
+    return c
+
+
+def make_batch(seq_lens, page_indptr, page_indices, total_pages, max_pages):
+    """qas_batch over int32 device tensors; total/max pages are host ints."""
+    b = qas_batch(seq_lens.numel(), int(total_pages), int(max_pages), 0,
+                  seq_lens.data_ptr(), page_indptr.data_ptr(),
+                  0 if page_indices is None else page_indices.data_ptr())
+    b._keep = (seq_lens, page_indptr, page_indices)
+    return b
+
+
+def qas_append(cache, batch, new_indptr, total_new, max_new, k_new, v_new, stream=None):
+    _check(lib.qas_append(ctypes.byref(cache), ctypes.byref(batch), _ptr(new_indptr),
+                          int(total_new), int(max_new), _ptr(k_new), _ptr(v_new),
+                          _stream(stream)))
+
+
+def qas_score_pages(cache, batch, q, scores, stream=None):
+    _check(lib.qas_score_pages(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+                               dtype_code(q), q.shape[1], _ptr(scores), _stream(stream)))
+
+
+def qas_topk_pages(scores, batch, num_kv_heads, page_size, k, sel, sel_count=None,
+                   stream=None):
+    _check(lib.qas_topk_pages(_ptr(scores), ctypes.byref(batch), int(num_kv_heads),
+                              int(page_size), int(k), _ptr(sel), _ptr(sel_count),
+                              _stream(stream)))
+
+
+def qas_workspace_bytes(op, cache, batch, num_q_heads, k):
+    return int(lib.qas_workspace_bytes(int(op), ctypes.byref(cache), ctypes.byref(batch),
+                                       int(num_q_heads), int(k)))
+
+
+def qas_sparse_decode(cache, batch, q, sel, sel_len, sm_scale, out, lse, workspace,
+                      stream=None):
+    _check(lib.qas_sparse_decode(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+                                 dtype_code(q), q.shape[1], _ptr(sel), sel.shape[-1],
+                                 int(sel_len), float(sm_scale), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def qas_decode_layer(cache, batch, q, k, sm_scale, out, lse, workspace, k_new=None,
+                     v_new=None, sel_out=None, stream=None):
+    _check(lib.qas_decode_layer(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+                                dtype_code(q), q.shape[1], int(k), float(sm_scale),
+                                _ptr(k_new), _ptr(v_new), _ptr(sel_out), _ptr(out),
+                                _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(),
+                                _stream(stream)))
+
+
+def version():
+    return lib.qas_version().decode()
+
+
+__all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_sparse_decode",
+           "qas_decode_layer", "qas_workspace_bytes", "make_cache", "make_batch",
+           "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

@@ -1,0 +1,358 @@
+// Host side of the libqas C ABI: argument validation, workspace carving and
+// launch geometry.  Every check runs before anything is enqueued, so an
+// error status means the stream was left untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/qas.h"
+#include "qas_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qas_status fail(qas_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+qas_status ok() {
+  g_err[0] = '\0';
+  return QAS_OK;
+}
+
+qas_status hip_fail(hipError_t e, const char* what) {
+  return fail(QAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+qas_status check_cache(const qas_cache* c, bool need_pools, bool need_summary) {
+  if (!c) return fail(QAS_ERR_NULL, "cache is NULL");
+  if (!pow2_in(c->page_size, 1, 256))
+    return fail(QAS_ERR_SHAPE, "page_size %d is not a power of two in [1, 256]", c->page_size);
+  if (c->num_kv_heads < 1) return fail(QAS_ERR_SHAPE, "num_kv_heads %d < 1", c->num_kv_heads);
+  if (c->num_pool_pages < 1) return fail(QAS_ERR_SHAPE, "num_pool_pages %d < 1", c->num_pool_pages);
+  if (c->head_dim != 16 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(QAS_ERR_UNSUPPORTED, "head_dim %d not in {16, 64, 128}", c->head_dim);
+  if (c->kv_dtype != QAS_F32 && c->kv_dtype != QAS_F16 && c->kv_dtype != QAS_BF16)
+    return fail(QAS_ERR_DTYPE, "kv_dtype %d not supported by the decode path (f32/f16/bf16)",
+                c->kv_dtype);
+  if (need_pools && (!c->k_pool || !c->v_pool)) return fail(QAS_ERR_NULL, "k_pool/v_pool is NULL");
+  if (need_summary && !c->summary) return fail(QAS_ERR_NULL, "summary is NULL");
+  return QAS_OK;
+}
+
+qas_status check_batch(const qas_batch* b) {
+  if (!b) return fail(QAS_ERR_NULL, "batch is NULL");
+  if (b->batch < 1) return fail(QAS_ERR_SHAPE, "batch %d < 1", b->batch);
+  if (b->total_pages < 0 || b->max_pages < 0)
+    return fail(QAS_ERR_SHAPE, "negative total_pages / max_pages");
+  if (b->max_pages > b->total_pages)
+    return fail(QAS_ERR_SHAPE, "max_pages %d > total_pages %d", b->max_pages, b->total_pages);
+  if (!b->seq_lens || !b->page_indptr || (!b->page_indices && b->total_pages > 0))
+    return fail(QAS_ERR_NULL, "seq_lens / page_indptr / page_indices is NULL");
+  return QAS_OK;
+}
+
+qas_status check_heads(const qas_cache* c, int num_q_heads, int* g) {
+  if (num_q_heads < 1 || num_q_heads % c->num_kv_heads != 0)
+    return fail(QAS_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, c->num_kv_heads);
+  *g = num_q_heads / c->num_kv_heads;
+  if (*g != 1 && *g != 2 && *g != 4 && *g != 8)
+    return fail(QAS_ERR_UNSUPPORTED, "group size %d not in {1, 2, 4, 8}", *g);
+  return QAS_OK;
+}
+
+struct DecodePlan {
+  int n_split;
+  size_t partial_bytes;
+};
+
+DecodePlan plan_decode(const qas_cache* c, const qas_batch* b, int num_q_heads, int sel_len) {
+  DecodePlan p;
+  p.n_split = qas::decode_num_splits(b->batch * c->num_kv_heads, sel_len);
+  p.partial_bytes = align256((size_t)b->batch * num_q_heads * p.n_split *
+                             (c->head_dim + 2) * sizeof(float));
+  return p;
+}
+
+size_t layer_scores_bytes(const qas_cache* c, const qas_batch* b) {
+  return align256((size_t)b->total_pages * c->num_kv_heads * sizeof(float));
+}
+
+size_t layer_sel_bytes(const qas_cache* c, const qas_batch* b, int k) {
+  return align256((size_t)b->batch * c->num_kv_heads * k * sizeof(int32_t));
+}
+
+qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q, int num_q_heads,
+                          int g, float* scores) {
+  qas::ScoreArgs a;
+  a.summary = c->summary;
+  a.q = q;
+  a.seq_lens = b->seq_lens;
+  a.page_indptr = b->page_indptr;
+  a.page_indices = b->page_indices;
+  a.scores = scores;
+  a.B = b->batch;
+  a.H_kv = c->num_kv_heads;
+  a.H_q = num_q_heads;
+  a.d = c->head_dim;
+  a.S = c->page_size;
+  a.max_pages = b->max_pages;
+  a.kv_dtype = c->kv_dtype;
+  a.g = g;
+  a.recs_per_block = qas::score_recs_per_block(c->kv_dtype, c->head_dim,
+                                               (long)b->total_pages * c->num_kv_heads);
+  return a;
+}
+
+qas::DecodeArgs decode_args(const qas_cache* c, const qas_batch* b, const void* q,
+                            int num_q_heads, int g, const int32_t* sel, int sel_stride,
+                            int sel_len, float sm_scale, void* out, float* lse, float* partials,
+                            int n_split, int dedupe) {
+  qas::DecodeArgs a;
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  a.q = q;
+  a.seq_lens = b->seq_lens;
+  a.page_indptr = b->page_indptr;
+  a.page_indices = b->page_indices;
+  a.sel = sel;
+  a.out = out;
+  a.lse = lse;
+  a.partials = partials;
+  a.B = b->batch;
+  a.H_kv = c->num_kv_heads;
+  a.H_q = num_q_heads;
+  a.d = c->head_dim;
+  a.S = c->page_size;
+  a.kv_dtype = c->kv_dtype;
+  a.g = g;
+  a.sel_stride = sel_stride;
+  a.sel_len = sel_len;
+  a.n_split = n_split;
+  a.dedupe = dedupe;
+  a.sm_scale = sm_scale;
+  return a;
+}
+
+qas::AppendArgs append_args(const qas_cache* c, const qas_batch* b, const int32_t* new_indptr,
+                            int max_new, const void* k_new, const void* v_new) {
+  qas::AppendArgs a;
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  a.summary = c->summary;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.seq_lens = b->seq_lens;
+  a.new_indptr = new_indptr;
+  a.page_indptr = b->page_indptr;
+  a.page_indices = b->page_indices;
+  a.B = b->batch;
+  a.H_kv = c->num_kv_heads;
+  a.d = c->head_dim;
+  a.S = c->page_size;
+  a.kv_dtype = c->kv_dtype;
+  a.max_new = max_new;
+  return a;
+}
+
+}  // namespace
+
+namespace qas {
+int decode_max_dedupe_row();
+}
+
+extern "C" {
+
+const char* qas_version(void) { return "qas 0.1.0 (gfx950)"; }
+
+const char* qas_last_error(void) { return g_err; }
+
+const char* qas_status_string(int32_t s) {
+  switch (s) {
+    case QAS_OK: return "ok";
+    case QAS_ERR_NULL: return "null pointer";
+    case QAS_ERR_SHAPE: return "bad shape";
+    case QAS_ERR_DTYPE: return "unsupported dtype";
+    case QAS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QAS_ERR_WORKSPACE: return "workspace too small";
+    case QAS_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t qas_workspace_bytes(int32_t op, const qas_cache* cache, const qas_batch* batch,
+                           int32_t num_q_heads, int32_t k) {
+  if (!cache || !batch || batch->batch < 1 || cache->num_kv_heads < 1 || num_q_heads < 1 ||
+      k < 1)
+    return 0;
+  if (op == QAS_OP_SPARSE_DECODE) return plan_decode(cache, batch, num_q_heads, k).partial_bytes;
+  if (op == QAS_OP_DECODE_LAYER)
+    return layer_scores_bytes(cache, batch) + layer_sel_bytes(cache, batch, k) +
+           plan_decode(cache, batch, num_q_heads, k).partial_bytes;
+  return 0;
+}
+
+qas_status qas_append(const qas_cache* cache, const qas_batch* batch, const int32_t* new_indptr,
+                      int32_t total_new, int32_t max_new, const void* k_new, const void* v_new,
+                      void* stream) {
+  qas_status st = check_cache(cache, true, true);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  if (!new_indptr) return fail(QAS_ERR_NULL, "new_indptr is NULL");
+  if (total_new < 0 || max_new < 0 || max_new > total_new)
+    return fail(QAS_ERR_SHAPE, "total_new %d / max_new %d inconsistent", total_new, max_new);
+  if (total_new == 0) return ok();
+  if (!k_new || !v_new) return fail(QAS_ERR_NULL, "k_new / v_new is NULL");
+  if (!qas::append_supported(cache->kv_dtype, cache->head_dim))
+    return fail(QAS_ERR_UNSUPPORTED, "append: dtype %d / head_dim %d", cache->kv_dtype,
+                cache->head_dim);
+  qas::AppendArgs a = append_args(cache, batch, new_indptr, max_new, k_new, v_new);
+  hipError_t e = qas::launch_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+qas_status qas_score_pages(const qas_cache* cache, const qas_batch* batch, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, float* scores, void* stream) {
+  qas_status st = check_cache(cache, false, true);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  int g;
+  if ((st = check_heads(cache, num_q_heads, &g))) return st;
+  if (!q || !scores) return fail(QAS_ERR_NULL, "q / scores is NULL");
+  if (q_dtype != cache->kv_dtype)
+    return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
+  if (batch->max_pages == 0) return ok();
+  qas::ScoreArgs a = score_args(cache, batch, q, num_q_heads, g, scores);
+  hipError_t e = qas::launch_score(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  return ok();
+}
+
+qas_status qas_topk_pages(const float* scores, const qas_batch* batch, int32_t num_kv_heads,
+                          int32_t page_size, int32_t k, int32_t* sel, int32_t* sel_count,
+                          void* stream) {
+  qas_status st = check_batch(batch);
+  if (st) return st;
+  if (!scores || !sel) return fail(QAS_ERR_NULL, "scores / sel is NULL");
+  if (num_kv_heads < 1) return fail(QAS_ERR_SHAPE, "num_kv_heads %d < 1", num_kv_heads);
+  if (!pow2_in(page_size, 1, 256)) return fail(QAS_ERR_SHAPE, "page_size %d", page_size);
+  if (k < 1) return fail(QAS_ERR_SHAPE, "k %d < 1", k);
+  if (batch->max_pages > qas::kTopkMaxPages)
+    return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed %d", batch->max_pages,
+                qas::kTopkMaxPages);
+  qas::TopkArgs a;
+  a.scores = scores;
+  a.seq_lens = batch->seq_lens;
+  a.page_indptr = batch->page_indptr;
+  a.sel = sel;
+  a.sel_count = sel_count;
+  a.B = batch->batch;
+  a.H_kv = num_kv_heads;
+  a.S = page_size;
+  a.k = k;
+  a.max_pages = batch->max_pages;
+  hipError_t e = qas::launch_topk(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+qas_status qas_sparse_decode(const qas_cache* cache, const qas_batch* batch, const void* q,
+                             int32_t q_dtype, int32_t num_q_heads, const int32_t* sel,
+                             int32_t sel_stride, int32_t sel_len, float sm_scale, void* out,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  qas_status st = check_cache(cache, true, false);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  int g;
+  if ((st = check_heads(cache, num_q_heads, &g))) return st;
+  if (!q || !out || !sel) return fail(QAS_ERR_NULL, "q / out / sel is NULL");
+  if (q_dtype != cache->kv_dtype)
+    return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
+  if (sel_len < 1 || sel_stride < sel_len)
+    return fail(QAS_ERR_SHAPE, "sel_len %d / sel_stride %d", sel_len, sel_stride);
+  if (sel_len > qas::decode_max_dedupe_row())
+    return fail(QAS_ERR_UNSUPPORTED, "sel_len %d > %d", sel_len, qas::decode_max_dedupe_row());
+  DecodePlan p = plan_decode(cache, batch, num_q_heads, sel_len);
+  if (!workspace || workspace_bytes < p.partial_bytes)
+    return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes,
+                p.partial_bytes);
+  qas::DecodeArgs a = decode_args(cache, batch, q, num_q_heads, g, sel, sel_stride, sel_len,
+                                  sm_scale, out, lse, (float*)workspace, p.n_split, 1);
+  hipError_t e = qas::launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, const void* q,
+                            int32_t q_dtype, int32_t num_q_heads, int32_t k, float sm_scale,
+                            const void* k_new, const void* v_new, int32_t* sel_out, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  qas_status st = check_cache(cache, true, true);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  int g;
+  if ((st = check_heads(cache, num_q_heads, &g))) return st;
+  if (!q || !out) return fail(QAS_ERR_NULL, "q / out is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(QAS_ERR_NULL, "k_new and v_new must both be given or both be NULL");
+  if (q_dtype != cache->kv_dtype)
+    return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
+  if (k < 1) return fail(QAS_ERR_SHAPE, "k %d < 1", k);
+  if (batch->max_pages > qas::kTopkMaxPages)
+    return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed %d", batch->max_pages,
+                qas::kTopkMaxPages);
+  const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* scores = (float*)ws;
+  ws += layer_scores_bytes(cache, batch);
+  int32_t* sel = sel_out;
+  int32_t* sel_ws = (int32_t*)ws;
+  ws += layer_sel_bytes(cache, batch, k);
+  if (!sel) sel = sel_ws;
+  DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
+  float* partials = (float*)ws;
+
+  hipError_t e;
+  if (k_new) {
+    qas::AppendArgs aa = append_args(cache, batch, nullptr, 1, k_new, v_new);
+    if ((e = qas::launch_append(aa, s)) != hipSuccess) return hip_fail(e, "append launch");
+  }
+  if (batch->max_pages > 0) {
+    qas::ScoreArgs sa = score_args(cache, batch, q, num_q_heads, g, scores);
+    if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
+  }
+  qas::TopkArgs ta;
+  ta.scores = scores;
+  ta.seq_lens = batch->seq_lens;
+  ta.page_indptr = batch->page_indptr;
+  ta.sel = sel;
+  ta.sel_count = nullptr;
+  ta.B = batch->batch;
+  ta.H_kv = cache->num_kv_heads;
+  ta.S = cache->page_size;
+  ta.k = k;
+  ta.max_pages = batch->max_pages;
+  if ((e = qas::launch_topk(ta, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+  qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, sel, k, k, sm_scale, out, lse,
+                                   partials, p.n_split, 0);
+  if ((e = qas::launch_decode(da, s)) != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+"""Device-memory plumbing for paged KV caches: allocate the pool and summary
+tensors with torch, upload host arrays, build page tables and the ABI
+structs, and fill the cache through the library's own append entry point.
+
+Nothing here computes any part of the method; it only moves bytes and calls
+query_aware_sparse_amd's entry points.
+"""
+import numpy as np
+import torch
+
+from . import make_batch, make_cache, qas_append
+
+TORCH_KV = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "e4m3": torch.float8_e4m3fn}
+
+
+def to_device(raw, dtype, device="cuda"):
+    """Host raw storage array (see workloads) -> device tensor of `dtype`."""
+    raw = np.ascontiguousarray(raw)
+    if dtype == "bf16":
+        t = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "e4m3":
+        t = torch.from_numpy(raw.view(np.uint8)).view(torch.float8_e4m3fn)
+    elif dtype == "f16":
+        t = torch.from_numpy(raw.view(np.float16))
+    else:
+        t = torch.from_numpy(raw.astype(np.float32, copy=False))
+    return t.to(device, non_blocking=False)
+
+
+def ceil_div(a, b):
+    return -(-int(a) // int(b))
+
+
+class PagedCache:
+    """A paged K/V pool with min/max summaries for one layer on the device.
+    Unwritten slots are filled with NaN so that any read of a slot the
+    method must not touch poisons the result."""
+
+    def __init__(self, num_pool_pages, H_kv, S, d, kv_dtype, device="cuda",
+                 poison=True):
+        tdt = TORCH_KV[kv_dtype]
+        shape = (num_pool_pages, H_kv, S, d)
+        fill = float("nan") if poison else 0.0
+        self.k_pool = torch.full(shape, fill, dtype=tdt, device=device)
+        self.v_pool = torch.full(shape, fill, dtype=tdt, device=device)
+        self.summary = torch.full((num_pool_pages, H_kv, 2, d), fill, dtype=tdt,
+                                  device=device)
+        self.kv_dtype, self.S, self.H_kv, self.d = kv_dtype, S, H_kv, d
+        self.device = device
+        self.cache = make_cache(self.k_pool, self.v_pool, self.summary)
+
+
+class DeviceBatch:
+    """Page table and lengths of a batch on the device, with its qas_batch."""
+
+    def __init__(self, lengths, pages, S, device="cuda"):
+        lengths = np.asarray(lengths, dtype=np.int32)
+        counts = [ceil_div(L, S) for L in lengths]
+        indptr = np.zeros(len(lengths) + 1, dtype=np.int32)
+        indptr[1:] = np.cumsum(counts)
+        indices = np.concatenate([np.asarray(pages[r][:counts[r]], np.int32)
+                                  for r in range(len(lengths))] + [np.zeros(0, np.int32)])
+        self.lengths = lengths
+        self.indptr_host = indptr
+        self.seq_lens = torch.from_numpy(lengths).to(device)
+        self.page_indptr = torch.from_numpy(indptr).to(device)
+        self.page_indices = torch.from_numpy(
+            indices if len(indices) else np.zeros(1, np.int32)).to(device)
+        self.total_pages = int(indptr[-1])
+        self.max_pages = int(max(counts)) if counts else 0
+        self.batch = make_batch(self.seq_lens, self.page_indptr, self.page_indices,
+                                self.total_pages, self.max_pages)
+
+
+def prefill(pc, case, lengths=None, device="cuda"):
+    """Write the first lengths[r] tokens of every request of a DecodeCase into
+    the paged cache with qas_append (one call per request, so host memory
+    stays bounded)."""
+    lengths = case.seq_lens if lengths is None else np.asarray(lengths, np.int32)
+    zeros = np.zeros(case.B, np.int32)
+    before = DeviceBatch(zeros, case.pages, case.S, device)
+    # the page table must cover the new tokens, lengths stay "before"
+    full = DeviceBatch(lengths, case.pages, case.S, device)
+    full_batch = make_batch(before.seq_lens, full.page_indptr, full.page_indices,
+                            full.total_pages, full.max_pages)
+    for r in range(case.B):
+        n = int(lengths[r])
+        if n == 0:
+            continue
+        new_indptr = np.zeros(case.B + 1, np.int32)
+        new_indptr[r + 1:] = n
+        k = to_device(case.keys[r][:n], case.kv_dtype, device)
+        v = to_device(case.values[r][:n], case.kv_dtype, device)
+        qas_append(pc.cache, full_batch, torch.from_numpy(new_indptr).to(device), n, n,
+                   k, v)
+        del k, v
+    torch.cuda.synchronize()
+    return full

@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every symbol include/qas.h declares, and
+rejects bad arguments before touching the device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qas.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qas_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def qas():
+    import query_aware_sparse_amd
+    return query_aware_sparse_amd
+
+
+def test_library_exports_every_declared_symbol(qas):
+    names = _declared()
+    assert "qas_decode_layer" in names and len(names) >= 9
+    lib = ctypes.CDLL(qas.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding exposes the compute entry points under the same names
+    for n in names:
+        if n not in ("qas_status_string", "qas_last_error", "qas_version"):
+            assert hasattr(qas, n), n
+
+
+def test_status_strings_and_version(qas):
+    assert qas.lib.qas_status_string(0) == b"ok"
+    assert qas.lib.qas_status_string(5) == b"workspace too small"
+    assert qas.version().startswith("qas")
+
+
+def _cache(qas, **kw):
+    c = qas.qas_cache(16, 128, 8, 64, qas.QAS_F16, 0, 1, 1, 1, 0, 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _batch(qas, **kw):
+    b = qas.qas_batch(2, 10, 6, 0, 8, 8, 8)
+    for k, v in kw.items():
+        setattr(b, k, v)
+    return b
+
+
+def test_validation_happens_before_any_launch(qas):
+    lib = qas.lib
+    byref = ctypes.byref
+    c, b = _cache(qas), _batch(qas)
+    # NULL cache
+    assert lib.qas_score_pages(None, byref(b), 8, 1, 32, 8, None) == 1
+    # head_dim not supported
+    assert lib.qas_score_pages(byref(_cache(qas, head_dim=96)), byref(b), 8, 1, 32, 8,
+                               None) == 4
+    # page size not a power of two
+    assert lib.qas_score_pages(byref(_cache(qas, page_size=12)), byref(b), 8, 1, 32, 8,
+                               None) == 2
+    # H_q not a multiple of H_kv
+    assert lib.qas_score_pages(byref(c), byref(b), 8, 1, 30, 8, None) == 2
+    # q dtype differs from kv dtype
+    assert lib.qas_score_pages(byref(c), byref(b), 8, 2, 32, 8, None) == 3
+    assert b"q_dtype" in lib.qas_last_error()
+    # workspace too small
+    need = lib.qas_workspace_bytes(2, byref(c), byref(b), 32, 64)
+    assert need > 0
+    assert lib.qas_decode_layer(byref(c), byref(b), 8, 1, 32, 64, 0.1, None, None, None,
+                                8, None, 8, need - 1, None) == 5
+    # top-k: k < 1
+    assert lib.qas_topk_pages(8, byref(b), 8, 16, 0, 8, None, None) == 2
+    # sparse decode: sel_stride < sel_len
+    assert lib.qas_sparse_decode(byref(c), byref(b), 8, 1, 32, 8, 4, 5, 0.1, 8, None, 8,
+                                 1 << 20, None) == 2
+    # append: only one of k_new / v_new for decode layer
+    assert lib.qas_decode_layer(byref(c), byref(b), 8, 1, 32, 64, 0.1, 8, None, None, 8,
+                                None, 8, need, None) == 1
+    # batch with max_pages > total_pages
+    assert lib.qas_score_pages(byref(c), byref(_batch(qas, max_pages=11)), 8, 1, 32, 8,
+                               None) == 2
+
+
+def test_workspace_sizes_are_consistent(qas):
+    lib = qas.lib
+    c, b = _cache(qas), _batch(qas)
+    sd = lib.qas_workspace_bytes(1, ctypes.byref(c), ctypes.byref(b), 32, 64)
+    dl = lib.qas_workspace_bytes(2, ctypes.byref(c), ctypes.byref(b), 32, 64)
+    assert 0 < sd < dl
+    assert sd % 256 == 0 and dl % 256 == 0
+    assert lib.qas_workspace_bytes(9, ctypes.byref(c), ctypes.byref(b), 32, 64) == 0

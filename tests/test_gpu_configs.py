@@ -1,0 +1,225 @@
+"""End-to-end GPU parity of the decode-layer call on the workloads at their
+full sizes, in the launch configuration the bench uses: page bounds, page
+sets (exact outside near ties, valid inside them) and attention outputs
+against the oracle.  Where the oracle is too slow for every output, a seeded
+sample of requests / steps is compared; the GPU always runs the whole batch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import (assert_attn_close, assert_scores_close, check_selection,
+                            out_to_numpy, say, score_denominator)
+from workloads import (config1, config2, config3, config5, corrupt_lists, figure2_case,
+                       worked_example_case)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qas():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import query_aware_sparse_amd
+    return query_aware_sparse_amd
+
+
+class Layer:
+    """Device state of one workload plus a decode-layer call."""
+
+    def __init__(self, qas, case, lengths=None):
+        from query_aware_sparse_amd.staging import PagedCache, prefill
+        self.qas, self.case = qas, case
+        self.pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+        self.db = prefill(self.pc, case, lengths)
+
+    def call(self, step=-1, append=False):
+        from query_aware_sparse_amd.staging import DeviceBatch, to_device
+        qas, case = self.qas, self.case
+        db = DeviceBatch(case.lengths(step), case.pages, case.S)
+        kn = vn = None
+        if append:
+            L = case.lengths(step)
+            kn = to_device(np.stack([case.keys[r][L[r] - 1] for r in range(case.B)]),
+                           case.kv_dtype)
+            vn = to_device(np.stack([case.values[r][L[r] - 1] for r in range(case.B)]),
+                           case.kv_dtype)
+        q = to_device(case.q[step + 1], case.q_dtype)
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((case.B, case.H_q), float("nan"), device="cuda")
+        sel = torch.full((case.B, case.H_kv, case.K), -9, dtype=torch.int32, device="cuda")
+        ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, self.pc.cache,
+                                                 db.batch, case.H_q, case.K),
+                         dtype=torch.uint8, device="cuda")
+        qas.qas_decode_layer(self.pc.cache, db.batch, q, case.K, case.sm_scale, out, lse,
+                             ws, k_new=kn, v_new=vn, sel_out=sel)
+        torch.cuda.synchronize()
+        return out_to_numpy(out), lse.cpu().numpy().astype(np.float64), sel.cpu().numpy(), db
+
+    def scores(self, db, step=-1):
+        from query_aware_sparse_amd.staging import to_device
+        case = self.case
+        q = to_device(case.q[step + 1], case.q_dtype)
+        s = torch.full((db.total_pages * case.H_kv,), float("nan"), device="cuda")
+        self.qas.qas_score_pages(self.pc.cache, db.batch, q, s)
+        torch.cuda.synchronize()
+        return s.cpu().numpy().astype(np.float64)
+
+
+def compare(case, got_out, got_lse, got_sel, ref, requests, got_scores=None, db=None,
+            step=-1, min_exact=0.75):
+    """Compare a decode-layer call with oracle results for `requests`."""
+    rows = exact = 0
+    q_all = oracle.decode(case.q[step + 1], case.q_dtype)
+    for r, res in zip(requests, ref):
+        if got_scores is not None:
+            P = len(res["U"][0])
+            base = db.indptr_host[r] * case.H_kv
+            denom = score_denominator(q_all[r], res["m"], res["M"], case.g)
+            for h in range(case.H_kv):
+                assert_scores_close(got_scores[base + h * P: base + (h + 1) * P],
+                                    res["U"][h], denom[h], f"{case.name} r={r} h={h}")
+        for h in range(case.H_kv):
+            rows += 1
+            same = check_selection(got_sel[r, h], res["U"][h], case.K)
+            if same:
+                exact += 1
+                heads = slice(h * case.g, (h + 1) * case.g)
+                assert_attn_close(got_out[r, heads], res["out"][heads], case.kv_dtype,
+                                  f"{case.name} r={r} h={h}")
+                np.testing.assert_allclose(got_lse[r, heads], res["lse"][heads],
+                                           rtol=1e-5, atol=1e-4)
+    say(f"  {case.name} step {step}: {exact}/{rows} rows with the oracle's exact set")
+    assert exact >= min_exact * rows
+    return exact, rows
+
+
+@pytest.mark.parametrize("make", [worked_example_case, lambda: worked_example_case(True),
+                                  config1], ids=["worked", "worked-b", "config1"])
+def test_tiny_cases(qas, make):
+    case = make()
+    say(f"[e2e] {case.name}")
+    lay = Layer(qas, case)
+    out, lse, sel, db = lay.call()
+    ref = oracle.run_decode(case)
+    compare(case, out, lse, sel, ref, range(case.B), lay.scores(db), db, min_exact=1.0)
+
+
+def test_figure2_two_steps(qas):
+    """Fig. 2 of the Quest page through the library: the first call selects
+    page A; appending (-2, 5) to B and scoring q_{t+1} selects B."""
+    case = figure2_case()
+    lay = Layer(qas, case)
+    out, lse, sel, db = lay.call(step=-1)
+    assert sel[0, 0, 0] == 0
+    s0 = lay.scores(db)
+    assert s0.tolist() == [8.0, 0.0]
+    out1, lse1, sel1, db1 = lay.call(step=0, append=True)
+    assert sel1[0, 0, 0] == 1
+    assert lay.scores(db1, step=0).tolist() == [1.0, 5.0]
+    ref = oracle.run_decode(case, step=0)
+    assert_attn_close(out1[0], ref[0]["out"], "f32", "figure2 step t+1")
+
+
+def test_config2_llama_layer_full(qas):
+    """Llama-2-7B-shaped decode layer, full size (32K context, 2048 pages,
+    K=256, 32x128 heads, fp16): every score, set and output."""
+    case = config2()
+    say(f"[e2e] {case.name} L={case.seq_lens[0]}")
+    lay = Layer(qas, case)
+    out, lse, sel, db = lay.call()
+    ref = oracle.run_decode(case)
+    compare(case, out, lse, sel, ref, [0], lay.scores(db), db)
+    # repeatability: identical bits over repeated calls
+    for _ in range(3):
+        o2, l2, s2, _ = lay.call()
+        assert np.array_equal(o2, out) and np.array_equal(s2, sel)
+        assert np.array_equal(l2, lse)
+
+
+def test_config2_attention_on_oracle_sets(qas):
+    """The attention stage at full config-2 size on the oracle's own sets, so
+    every head is compared even where a near tie lets the sets differ."""
+    case = config2()
+    lay = Layer(qas, case)
+    ref = oracle.run_decode(case)
+    lists = np.array([[ref[0]["sel"][h] for h in range(case.H_kv)]], dtype=np.int32)
+    sel = torch.from_numpy(lists).cuda()
+    from query_aware_sparse_amd.staging import to_device
+    q = to_device(case.q[0], case.q_dtype)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, case.H_q), device="cuda")
+    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_SPARSE_DECODE, lay.pc.cache,
+                                             lay.db.batch, case.H_q, case.K),
+                     dtype=torch.uint8, device="cuda")
+    qas.qas_sparse_decode(lay.pc.cache, lay.db.batch, q, sel, case.K, case.sm_scale, out,
+                          lse, ws)
+    torch.cuda.synchronize()
+    assert_attn_close(out_to_numpy(out)[0], ref[0]["out"], "f16", "config2 on oracle sets")
+
+
+def test_config3_batched_gqa_with_append(qas):
+    """8 requests of 8K-64K tokens, 32/8 heads, bf16, K=128: 16 decode steps,
+    each appending one token per request (one page boundary crossed per
+    request).  The oracle checks the first call and a sample of steps; the
+    summaries after the last append are checked in full."""
+    case = config3()
+    say(f"[e2e] {case.name} lengths={case.seq_lens.tolist()}")
+    lay = Layer(qas, case)
+    decoded = {r: oracle.decoded_kv(case, r) for r in range(case.B)}
+    check_steps = {-1, 0, 7, 15}
+    for step in range(-1, case.steps):
+        out, lse, sel, db = lay.call(step=step, append=step >= 0)
+        if step in check_steps:
+            reqs = list(range(case.B)) if step == -1 else [0, 3, 6]
+            ref = oracle.run_decode(case, step=step, requests=reqs, decoded=decoded)
+            compare(case, out, lse, sel, ref, reqs,
+                    lay.scores(db, step) if step == -1 else None, db, step=step)
+    summ = lay.pc.summary.float().cpu().numpy()
+    final = case.lengths(case.steps - 1)
+    for r in range(case.B):
+        m, M = oracle.quest.page_summaries(decoded[r][0], int(final[r]), case.S)
+        phys = case.pages[r][:len(m)]
+        assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
+
+
+def test_config5_stress(qas):
+    """16 requests at 131072 tokens, 32/8 heads, S=32, K=41, Student-t keys,
+    fp16: decode-layer call checked on a seeded sample of requests; then
+    attention on corrupted lists (duplicates, invalid IDs, fully invalid
+    rows) built from the oracle's own top-K of the sampled requests."""
+    case = config5()
+    say(f"[e2e] {case.name} K={case.K}")
+    lay = Layer(qas, case)
+    out, lse, sel, db = lay.call()
+    reqs = sorted(np.random.default_rng(55).choice(case.B, size=4, replace=False).tolist())
+    decoded = {r: oracle.decoded_kv(case, r) for r in reqs}
+    ref = oracle.run_decode(case, requests=reqs, decoded=decoded)
+    compare(case, out, lse, sel, ref, reqs, lay.scores(db), db)
+    # corrupted lists: oracle top-K on sampled requests, seeded random pages elsewhere
+    P = case.seq_lens[0] // case.S
+    rng = np.random.default_rng(56)
+    lists = rng.integers(0, P, size=(case.B, case.H_kv, case.K)).astype(np.int64)
+    for r, res in zip(reqs, ref):
+        for h in range(case.H_kv):
+            lists[r, h] = res["sel"][h]
+    bad, cat = corrupt_lists(lists, [P] * case.B, seed=5)
+    from query_aware_sparse_amd.staging import to_device
+    q = to_device(case.q[0], case.q_dtype)
+    o = torch.full_like(q, float("nan"))
+    ls = torch.empty((case.B, case.H_q), device="cuda")
+    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_SPARSE_DECODE, lay.pc.cache,
+                                             lay.db.batch, case.H_q, case.K),
+                     dtype=torch.uint8, device="cuda")
+    qas.qas_sparse_decode(lay.pc.cache, lay.db.batch, q,
+                          torch.from_numpy(bad.astype(np.int32)).cuda(), case.K,
+                          case.sm_scale, o, ls, ws)
+    torch.cuda.synchronize()
+    got = out_to_numpy(o)
+    ref2 = oracle.run_decode(case, page_ids=bad, requests=reqs, decoded=decoded)
+    for r, res in zip(reqs, ref2):
+        assert_attn_close(got[r], res["out"], "f16", f"config5 corrupted r={r}")
+    empty_rows = np.argwhere(cat == 4)
+    assert len(empty_rows) > 0
+    for r, h in empty_rows:
+        assert np.all(got[r, h * case.g:(h + 1) * case.g] == 0.0)
+        assert np.all(np.isneginf(ls.cpu().numpy()[r, h * case.g:(h + 1) * case.g]))

@@ -1,0 +1,279 @@
+"""Per-kernel GPU parity against the oracle: each kernel gets the oracle's own
+inputs (summaries from the same keys, identical fp32 scores, the oracle's
+page lists) and is compared element by element."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quest
+from tests.gpu_util import (ATTN_TOL, assert_attn_close, assert_scores_close,
+                            check_selection, out_to_numpy, say, score_denominator)
+from workloads import (config1, config2, config3, config5, corrupt_lists,
+                       figure2_case, worked_example_case)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qas():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import query_aware_sparse_amd
+    return query_aware_sparse_amd
+
+
+def _stage(qas, case, lengths=None):
+    from query_aware_sparse_amd.staging import PagedCache, prefill
+    pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+    db = prefill(pc, case, lengths)
+    return pc, db
+
+
+def _q(case, step=-1):
+    from query_aware_sparse_amd.staging import to_device
+    return to_device(case.q[step + 1], case.q_dtype)
+
+
+SCORE_CASES = {
+    "worked-example": lambda: worked_example_case(),
+    "worked-example-b": lambda: worked_example_case(second_set=True),
+    "figure2": lambda: figure2_case(),
+    "config1": lambda: config1(),
+    "config2-small-shuffled": lambda: config2(L=3001, H=4, identity_table=False),
+    "config3-small-gqa": lambda: config3(B=3, L_min=300, L_max=2000, steps=0),
+    "config5-small": lambda: config5(B=2, L=4096, H_q=8, H_kv=2),
+    "d64-bf16-g8": lambda: config3(B=2, L_min=100, L_max=700, H_q=16, H_kv=2, d=64,
+                                   S=32, steps=0),
+}
+
+
+@pytest.mark.parametrize("name", list(SCORE_CASES))
+def test_summaries_and_scores(qas, name):
+    case = SCORE_CASES[name]()
+    say(f"[scores] {name}: B={case.B} H={case.H_q}/{case.H_kv} d={case.d} S={case.S}")
+    pc, db = _stage(qas, case)
+    q = _q(case)
+    scores = torch.full((db.total_pages * case.H_kv,), float("nan"), device="cuda")
+    qas.qas_score_pages(pc.cache, db.batch, q, scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    summ = pc.summary.float().cpu().numpy().astype(np.float64)
+    ref = oracle.run_decode(case)
+    for r in range(case.B):
+        res = ref[r]
+        P = len(res["U"][0])
+        phys = case.pages[r][:P]
+        # summaries are exact (min/max of stored values)
+        assert np.array_equal(summ[phys, :, 0, :], res["m"]), f"min summary r={r}"
+        assert np.array_equal(summ[phys, :, 1, :], res["M"]), f"max summary r={r}"
+        base = db.indptr_host[r] * case.H_kv
+        q_heads = oracle.decode(case.q[0][r], case.q_dtype)
+        denom = score_denominator(q_heads, res["m"], res["M"], case.g)
+        for h in range(case.H_kv):
+            row = got[base + h * P: base + (h + 1) * P]
+            assert_scores_close(row, res["U"][h], denom[h], f"{name} r={r} h={h}")
+
+
+def _topk_rows(rng, B, H, maxP):
+    lens = rng.integers(1, maxP + 1, size=B)
+    return lens
+
+
+@pytest.mark.parametrize("K", [1, 4, 64, 256, 4096])
+def test_topk_exact_on_identical_scores(qas, K):
+    """The oracle's top-K on the very fp32 scores the kernel reads: exact."""
+    from query_aware_sparse_amd.staging import DeviceBatch
+    rng = np.random.default_rng(100 + K)
+    B, H, S = 5, 3, 16
+    P = [1, 300, 2048, 4097, 1000]
+    lens = [p * S - int(rng.integers(0, S)) for p in P]
+    pages = [np.arange(p, dtype=np.int32) for p in P]
+    db = DeviceBatch(lens, pages, S)
+    total = db.total_pages * H
+    kinds = ["ints", "normal", "zeros"]
+    for kind in kinds:
+        if kind == "ints":
+            s = rng.integers(-20, 20, size=total).astype(np.float32)   # heavy ties
+        elif kind == "normal":
+            s = rng.standard_normal(total).astype(np.float32)
+        else:
+            s = np.where(rng.random(total) < 0.5, np.float32(0.0), np.float32(-0.0))
+        say(f"[topk] K={K} kind={kind}")
+        scores = torch.from_numpy(s).cuda()
+        sel = torch.full((B, H, K), 12345, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((B, H), dtype=torch.int32, device="cuda")
+        qas.qas_topk_pages(scores, db.batch, H, S, K, sel, cnt)
+        torch.cuda.synchronize()
+        sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+        for r in range(B):
+            base = db.indptr_host[r] * H
+            for h in range(H):
+                row = s[base + h * P[r]: base + (h + 1) * P[r]].astype(np.float64)
+                ref = quest.top_k_pages(row, K)
+                take = min(K, P[r])
+                assert cnt_h[r, h] == take
+                assert list(sel_h[r, h, :take]) == ref, (kind, r, h)
+                assert np.all(sel_h[r, h, take:] == -1)
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 33, 250])
+def test_append_decode_steps_and_boundaries(qas, L):
+    """Prefill L tokens, then decode-append 20 single tokens (crossing page
+    boundaries); summaries stay exactly the oracle's after every step."""
+    from query_aware_sparse_amd.staging import DeviceBatch, to_device
+    case = config3(B=2, L_min=L, L_max=L, H_q=4, H_kv=2, d=128, S=16, steps=20)
+    pc, _ = _stage(qas, case)
+    for s in range(case.steps):
+        lengths = case.lengths(s)
+        db = DeviceBatch(lengths, case.pages, case.S)
+        k_new = np.stack([case.keys[r][lengths[r] - 1] for r in range(case.B)])
+        v_new = np.stack([case.values[r][lengths[r] - 1] for r in range(case.B)])
+        kn, vn = to_device(k_new, "bf16"), to_device(v_new, "bf16")
+        out = torch.empty((case.B, case.H_q, case.d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
+                                                 case.H_q, case.K), dtype=torch.uint8,
+                         device="cuda")
+        qas.qas_decode_layer(pc.cache, db.batch, _q(case, s), case.K, case.sm_scale, out,
+                             None, ws, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    summ = pc.summary.float().cpu().numpy()
+    kp = pc.k_pool.float().cpu().numpy()
+    lengths = case.lengths(case.steps - 1)
+    for r in range(case.B):
+        keys = oracle.decode(case.keys[r][:lengths[r]], "bf16")
+        m, M = quest.page_summaries(keys, int(lengths[r]), case.S)
+        m2, M2 = quest.replay_summaries(keys, int(lengths[r]), case.S)
+        assert np.array_equal(m, m2)
+        phys = case.pages[r][:len(m)]
+        assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
+        # the pool holds the appended rows at their slots
+        t = int(lengths[r]) - 1
+        assert np.array_equal(kp[case.pages[r][t // case.S], :, t % case.S], keys[t])
+
+
+def test_recycled_page_summary_equals_fresh(qas):
+    """A physical page whose summary holds stale extremes from a previous
+    owner, reused by a new request, ends with the same summary as a fresh
+    page (the Quest page, §3, page recycling)."""
+    from query_aware_sparse_amd.staging import DeviceBatch, PagedCache, to_device
+    case = config2(L=40, H=2, d=128, identity_table=False)
+    pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+    pc.summary.fill_(1000.0)                     # stale values of a former owner
+    pc.summary[:, :, 0].fill_(-1000.0)
+    before = DeviceBatch([0], case.pages, case.S)
+    full = DeviceBatch([40], case.pages, case.S)
+    batch = qas.make_batch(before.seq_lens, full.page_indptr, full.page_indices,
+                           full.total_pages, full.max_pages)
+    new_indptr = torch.tensor([0, 40], dtype=torch.int32, device="cuda")
+    qas.qas_append(pc.cache, batch, new_indptr, 40, 40, to_device(case.keys[0], "f16"),
+                   to_device(case.values[0], "f16"))
+    torch.cuda.synchronize()
+    keys = oracle.decode(case.keys[0], "f16")
+    m, M = quest.page_summaries(keys, 40, case.S)
+    summ = pc.summary.float().cpu().numpy()
+    phys = case.pages[0][:3]
+    assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
+
+
+def _sparse_decode(qas, case, pc, db, lists, step=-1):
+    B, H, kk = lists.shape
+    sel = torch.from_numpy(np.ascontiguousarray(lists, np.int32)).cuda()
+    q = _q(case, step)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, case.H_q), float("nan"), device="cuda")
+    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_SPARSE_DECODE, pc.cache, db.batch,
+                                             case.H_q, kk), dtype=torch.uint8, device="cuda")
+    qas.qas_sparse_decode(pc.cache, db.batch, q, sel, kk, case.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out_to_numpy(out), lse.cpu().numpy().astype(np.float64)
+
+
+SPARSE_CASES = {
+    "config1": lambda: config1(),
+    "config2-small": lambda: config2(L=5000, H=4, K=40),
+    "config3-small": lambda: config3(B=3, L_min=900, L_max=3000, steps=0, K=37),
+    "config5-small": lambda: config5(B=4, L=6000, H_q=8, H_kv=2, K=12),
+}
+
+
+@pytest.mark.parametrize("name", list(SPARSE_CASES))
+def test_sparse_decode_on_corrupted_lists(qas, name):
+    """Attention over the oracle's own top-K lists after seeded corruption:
+    duplicates, invalid IDs (-1, -7, P, P+5, INT32_MAX), shuffled order and
+    fully invalid rows (zero output, lse = -inf)."""
+    case = SPARSE_CASES[name]()
+    say(f"[sparse] {name}")
+    pc, db = _stage(qas, case)
+    ref = oracle.run_decode(case)
+    lists = np.full((case.B, case.H_kv, case.K), -1, dtype=np.int64)
+    for r in range(case.B):
+        for h in range(case.H_kv):
+            s = ref[r]["sel"][h]
+            lists[r, h, :len(s)] = s
+    P = [len(ref[r]["U"][0]) for r in range(case.B)]
+    bad, cat = corrupt_lists(lists, P, seed=7, n_slots=max(1, case.K // 5))
+    rng = np.random.default_rng(3)
+    for r in range(case.B):
+        for h in range(case.H_kv):
+            bad[r, h] = bad[r, h, rng.permutation(case.K)]
+    got, lse = _sparse_decode(qas, case, pc, db, bad)
+    ref2 = oracle.run_decode(case, page_ids=bad)
+    for r in range(case.B):
+        assert_attn_close(got[r], ref2[r]["out"], case.kv_dtype, f"{name} r={r}")
+        fin = np.isfinite(ref2[r]["lse"])
+        assert np.array_equal(np.isfinite(lse[r]), fin)
+        assert np.allclose(lse[r][fin], ref2[r]["lse"][fin], atol=1e-4, rtol=1e-5)
+        for h in range(case.H_kv):
+            if cat[r, h] == 4:
+                assert np.all(got[r, h * case.g:(h + 1) * case.g] == 0.0)
+
+
+def test_dense_fallback_all_pages(qas):
+    """K = all pages reproduces dense paged attention (the Quest page, §1.2)."""
+    case = config2(L=2000, H=2, K=10000)
+    pc, db = _stage(qas, case)
+    q = _q(case)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, case.H_q), device="cuda")
+    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
+                                             case.H_q, case.K), dtype=torch.uint8,
+                     device="cuda")
+    sel = torch.empty((1, case.H_kv, case.K), dtype=torch.int32, device="cuda")
+    qas.qas_decode_layer(pc.cache, db.batch, q, case.K, case.sm_scale, out, lse, ws,
+                         sel_out=sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy()[0, :, :125], np.tile(np.arange(125), (2, 1)))
+    keys = oracle.decode(case.keys[0], "f16")
+    vals = oracle.decode(case.values[0], "f16")
+    qh = oracle.decode(case.q[0][0], "f16")
+    for i in range(case.H_q):
+        o, l = quest.attend(qh[i], keys[:, i], vals[:, i], np.arange(2000), case.sm_scale)
+        assert_attn_close(out_to_numpy(out)[0, i], o, "f16", f"head {i}")
+
+
+def test_empty_and_zero_length_requests(qas):
+    """A zero-length request in a ragged batch gets no pages, no selection and
+    a zero output; its neighbours are unaffected."""
+    from query_aware_sparse_amd.staging import DeviceBatch, PagedCache, prefill
+    case = config3(B=3, L_min=100, L_max=400, steps=0, K=8)
+    case.seq_lens[1] = 0
+    pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+    db = prefill(pc, case)
+    q = _q(case)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.empty((case.B, case.H_q), device="cuda")
+    sel = torch.empty((case.B, case.H_kv, case.K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
+                                             case.H_q, case.K), dtype=torch.uint8,
+                     device="cuda")
+    qas.qas_decode_layer(pc.cache, db.batch, q, case.K, case.sm_scale, out, lse, ws,
+                         sel_out=sel)
+    torch.cuda.synchronize()
+    got = out_to_numpy(out)
+    assert np.all(got[1] == 0) and np.all(np.isneginf(lse.cpu().numpy()[1]))
+    assert np.all(sel.cpu().numpy()[1] == -1)
+    ref = oracle.run_decode(case, requests=[0, 2])
+    for r, res in zip((0, 2), ref):
+        assert_attn_close(got[r], res["out"], "bf16", f"r={r}")

@@ -15,6 +15,7 @@ A DecodeCase is a batch of requests with a paged KV cache:
 A ChunkCase is one request with many query positions, each with its own
 page set per KV head (the multi-query chunk of the PageWeaver notes).
 """
+import concurrent.futures
 import math
 from dataclasses import dataclass, field
 from typing import List, Optional
@@ -140,6 +141,39 @@ def _normal(seed, stream, idx, shape):
     return _rng(seed, stream, idx).standard_normal(shape, dtype=np.float32)
 
 
+_CHUNK = 2048  # tokens per independent RNG stream of a token-ordered tensor
+
+
+def _tokens(seed, stream, idx, T, H, d, dtype, dist="normal", nu=3.0,
+            col_scale=None, head_scale=None):
+    """Token-ordered [T][H][d] tensor in storage dtype `dtype`.  Token chunk c
+    (tokens c*2048 ...) draws from SeedSequence([seed, stream, idx, c]), so
+    chunks are generated in parallel threads and the result does not depend
+    on the thread count.  col_scale ([H][d]) multiplies the samples before
+    the cast; head_scale ([H]) divides them (fp8 quantisation scale)."""
+    out_dt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16,
+              "e4m3": np.uint8}[dtype]
+    out = np.empty((T, H, d), dtype=out_dt)
+
+    def work(c):
+        t0, t1 = c * _CHUNK, min(T, (c + 1) * _CHUNK)
+        g = _rng(seed, stream, idx, c)
+        if dist == "normal":
+            x = g.standard_normal((t1 - t0, H, d), dtype=np.float32)
+        else:
+            x = np.clip(g.standard_t(nu, size=(t1 - t0, H, d)), -65504.0, 65504.0)
+        if col_scale is not None:
+            x = x * col_scale[None]
+        if head_scale is not None:
+            x = x / head_scale[None, :, None]
+        out[t0:t1] = cast(x, dtype)
+
+    n = ceil_div(T, _CHUNK)
+    with concurrent.futures.ThreadPoolExecutor(min(16, max(1, n))) as ex:
+        list(ex.map(work, range(n)))
+    return out
+
+
 def _pool_permutation(seed, total, extra):
     """Physical pages for `total` logical pages drawn from a shuffled pool of
     total + extra pages (the extra ones stay unallocated)."""
@@ -177,13 +211,12 @@ def config2(seed=2, L=32768, H=32, d=128, S=16, K=256, outliers=4,
     d=128, S=16, L=32768 (2048 pages), K=256; fp16 K/V N(0,1) with 4 seeded
     channels per KV head scaled x8 in both K and V; fp16 query N(0,1).
     Smaller L / H give the same recipe at test sizes."""
-    keys = _normal(seed, _KEYS, 0, (L, H, d))
-    values = _normal(seed, _VALUES, 0, (L, H, d))
     orng = _rng(seed, _OUTLIER)
+    col = np.ones((H, d), np.float32)
     for h in range(H):
-        ch = orng.choice(d, size=min(outliers, d), replace=False)
-        keys[:, h, ch] *= outlier_scale
-        values[:, h, ch] *= outlier_scale
+        col[h, orng.choice(d, size=min(outliers, d), replace=False)] = outlier_scale
+    keys = _tokens(seed, _KEYS, 0, L, H, d, "f16", col_scale=col)
+    values = _tokens(seed, _VALUES, 0, L, H, d, "f16", col_scale=col)
     q = _normal(seed, _QUERY, 0, (1, 1, H, d))
     P = ceil_div(L, S)
     if identity_table:
@@ -191,8 +224,8 @@ def config2(seed=2, L=32768, H=32, d=128, S=16, K=256, outliers=4,
     else:
         phys, pool = _pool_permutation(seed, P, 8)
     return DecodeCase("config2-llama2-7b-layer", 1, H, H, d, S, K, "f16",
-                      "f16", np.array([L], np.int32), [cast(keys, "f16")],
-                      [cast(values, "f16")], cast(q, "f16"), [phys], pool,
+                      "f16", np.array([L], np.int32), [keys],
+                      [values], cast(q, "f16"), [phys], pool,
                       notes="4 outlier channels per KV head x8 in K and V")
 
 
@@ -207,8 +240,8 @@ def config3(seed=3, B=8, L_min=8192, L_max=65536, H_q=32, H_kv=8, d=128,
     keys, values = [], []
     for r in range(B):
         T = int(lens[r]) + steps
-        keys.append(cast(_normal(seed, _KEYS, r, (T, H_kv, d)), "bf16"))
-        values.append(cast(_normal(seed, _VALUES, r, (T, H_kv, d)), "bf16"))
+        keys.append(_tokens(seed, _KEYS, r, T, H_kv, d, "bf16"))
+        values.append(_tokens(seed, _VALUES, r, T, H_kv, d, "bf16"))
     q = cast(_normal(seed, _QUERY, 0, (1 + steps, B, H_q, d)), "bf16")
     counts = [ceil_div(int(L) + steps, S) for L in lens]
     flat, pool = _pool_permutation(seed, sum(counts), 16)
@@ -228,10 +261,8 @@ def config5(seed=5, B=16, L=131072, H_q=32, H_kv=8, d=128, S=32, K=None,
         K = max(1, int(round(0.01 * P)))
     keys, values = [], []
     for r in range(B):
-        t = _rng(seed, _KEYS, r).standard_t(nu, size=(L, H_kv, d))
-        t = np.clip(t, -65504.0, 65504.0)
-        keys.append(cast(t, "f16"))
-        values.append(cast(_normal(seed, _VALUES, r, (L, H_kv, d)), "f16"))
+        keys.append(_tokens(seed, _KEYS, r, L, H_kv, d, "f16", dist="t", nu=nu))
+        values.append(_tokens(seed, _VALUES, r, L, H_kv, d, "f16"))
     q = cast(_normal(seed, _QUERY, 0, (1, B, H_q, d)), "f16")
     flat, pool = _pool_permutation(seed, B * P, 32)
     return DecodeCase("config5-stress", B, H_q, H_kv, d, S, K, "f16", "f16",
@@ -301,8 +332,8 @@ def config4(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
     filled to kq, so neighbours share ~70% of their pages.  K/V N(0,1)
     quantised to fp8 e4m3 with a per-KV-head scale amax/448; q bf16 N(0,1).
     Entries of each set are stored in seeded random order."""
-    keys = _normal(seed, _KEYS, 0, (L, H_kv, d))
-    values = _normal(seed, _VALUES, 0, (L, H_kv, d))
+    keys = _tokens(seed, _KEYS, 0, L, H_kv, d, "f32")
+    values = _tokens(seed, _VALUES, 0, L, H_kv, d, "f32")
     k_scale = (np.abs(keys).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
     v_scale = (np.abs(values).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
     k_codes = cast(keys / k_scale[None, :, None], "e4m3")
