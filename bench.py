@@ -1,0 +1,209 @@
+#!/usr/bin/env python
+"""Benchmark of the decode-layer hot path on one MI355X.
+
+Workload: the Llama-2-7B-shaped decode layer (batch 1, 32 query heads = 32
+KV heads, d=128, S=16, 32768-token context = 2048 pages, top-K = 256 pages,
+fp16 K/V with 4 outlier channels per head x8, fp16 query), built from the
+seeded generators.  One step is one decode-layer call of the library:
+append of the current token's K/V row and tail summary, page bounds of all
+2048 pages, top-K per KV head, sparse attention over the 256 selected pages
+with the split merge.  32 separate layer caches (as in a 32-layer model,
+~17 GB) are visited in turn so that no call finds its bytes in the 256 MB
+Infinity Cache; the 32 calls are captured once in a HIP graph and replayed.
+
+The value is the achieved rate on the bytes the method must move per call
+(summary scan + selected K/V + q/o + the append's row and summary record),
+divided by the measured time per call.
+
+    python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("µs per decode-layer call + achieved HBM GB/s, 32K ctx, K=256 pages, "
+          "32×128 heads")
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, timed on the host on the same call with the
+    summaries prebuilt (the GPU keeps them current): bounds of every page,
+    group scores, top-K and attention per head.  BLAS is held to one thread."""
+    import threadpoolctl
+
+    import oracle
+    from oracle import quest
+    from query_aware_sparse_amd import traffic
+
+    L = int(case.seq_lens[0])
+    keys, values = oracle.decoded_kv(case, 0)
+    m, M = quest.page_summaries(keys, L, case.S)
+    q = oracle.decode(case.q[0][0], case.q_dtype)
+    calls = 0
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            U = quest.kv_head_scores(quest.head_bounds(q, m, M), case.H_kv)
+            for h in range(case.H_kv):
+                sel = quest.top_k_pages(U[h], case.K)
+                for i in range(h * case.g, (h + 1) * case.g):
+                    A = quest.support(sel, L, L - 1, case.S)
+                    quest.attend(q[i], keys[:, h], values[:, h], A, case.sm_scale)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    per_call = el / calls
+    nbytes = traffic.decode_layer_bytes(
+        B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
+        pages_scanned=len(m), page_heads_selected=case.H_kv * case.K)["total"]
+    return {"value": round(nbytes / per_call / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{calls} full decode-layer calls of the same workload (layer 0, "
+                       f"summaries prebuilt), {el:.1f} s, float64 numpy, 1 thread; "
+                       f"{per_call * 1e3:.1f} ms per call"),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640, help="timed decode-layer calls")
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=32, help="layer caches visited in turn")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this build measures the "
+              "single-GPU path only (one GPU per box); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import query_aware_sparse_amd as qas
+    from query_aware_sparse_amd import traffic
+    from query_aware_sparse_amd.staging import PagedCache, prefill, to_device
+    from workloads import llama2_7b_layer, layer_queries
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    NL = args.layers
+    case = llama2_7b_layer()
+    L = int(case.seq_lens[0])
+    log(f"[bench] workload {case.name}: L={L} P={L // case.S} K={case.K} "
+        f"H={case.H_q}x{case.d} layers={NL}")
+
+    # layer 0 filled through the library's append; other layers are copies
+    base = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+    db = prefill(base, case)
+    layers = [base]
+    for _ in range(1, NL):
+        pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype,
+                        poison=False)
+        pc.k_pool.copy_(base.k_pool)
+        pc.v_pool.copy_(base.v_pool)
+        pc.summary.copy_(base.summary)
+        layers.append(pc)
+    qs = to_device(layer_queries(case, NL), case.q_dtype)          # [NL][1][H][d]
+    k_new = to_device(case.keys[0][L - 1:L], case.kv_dtype)      # current token
+    v_new = to_device(case.values[0][L - 1:L], case.kv_dtype)
+    out = torch.empty((NL, 1, case.H_q, case.d), dtype=torch.float16, device=dev)
+    lse = torch.empty((NL, 1, case.H_q), dtype=torch.float32, device=dev)
+    ws_bytes = qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, base.cache, db.batch,
+                                       case.H_q, case.K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def call(i):
+        qas.qas_decode_layer(layers[i].cache, db.batch, qs[i], case.K, case.sm_scale,
+                             out[i], lse[i], ws, k_new=k_new, v_new=v_new)
+
+    # eager warm-up, then capture one pass over the layers into a graph
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for w in range(max(NL, args.warmup)):
+            call(w % NL)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(NL):
+            call(i)
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup // NL)):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager_out):
+        raise RuntimeError("graph replay differs from the eager calls")
+
+    reps = max(1, math.ceil(args.steps / NL))
+    steps = reps * NL
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    replay_stream = torch.cuda.current_stream()   # graph.replay() launches here
+    for e0, e1 in evs:
+        e0.record(replay_stream)
+        graph.replay()
+        e1.record(replay_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL
+
+    nbytes = traffic.decode_layer_bytes(
+        B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
+        pages_scanned=L // case.S, page_heads_selected=case.H_kv * case.K,
+        append_tokens=1)
+    total = nbytes["total"]
+    value = total / (ms_per_step * 1e-3) / 1e9
+    achieved = total / (call_us * 1e-6) / 1e9
+    log(f"[bench] {steps} calls: {ms_per_step * 1e3:.2f} us/call (wall), "
+        f"{call_us:.2f} us/call (events), {value:.1f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama2-7b-shaped decode layer, 32K context",
+                   "batch": 1, "q_heads": case.H_q, "kv_heads": case.H_kv,
+                   "head_dim": case.d, "page_size": case.S, "context": L,
+                   "pages": L // case.S, "top_k_pages": case.K, "kv_dtype": "f16",
+                   "layer_caches": NL, "append_current_token": True,
+                   "hip_graph": True, "us_per_call": round(ms_per_step * 1e3, 3),
+                   "bytes_per_call": total, "bytes_parts": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "decode-layer call (score with fused append, top-k, attention with merge)",
+                     "us_per_launch": round(call_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

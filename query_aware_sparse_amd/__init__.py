@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqas.so")
+# QAS_LIB_PATH selects another build of the same library (same ABI)
+LIB_PATH = os.environ.get("QAS_LIB_PATH") or os.path.join(_HERE, "libqas.so")
 
 QAS_OK = 0
 QAS_F32, QAS_F16, QAS_BF16, QAS_FP8_E4M3 = 0, 1, 2, 3

@@ -7,13 +7,19 @@
 // sum per row).
 //
 // Grid (split, KV head, request).  A workgroup first turns its slice of the
-// selected list into distinct valid physical pages in LDS, then its four
-// waves stream "token groups" (TPI token rows of one page = one 16-byte load
-// per lane for K and one for V).  Each lane keeps a private online-softmax
-// state (max, sum, accumulator of its 16-byte dim chunk) per query head of
-// the group over the token rows it sees; lanes of one token row share the
-// logit after a DPP reduction.  States are merged across lanes, waves, and
-// finally splits.
+// selected list into distinct valid physical pages in LDS (lists from the
+// top-K stage are already canonical and carry their physical pages, so only
+// padding is dropped), then its four waves stream "token groups" (TPI token
+// rows of one page = one 16-byte load per lane for K and one for V), all of
+// a wave's groups in flight at once where registers allow.  Each lane keeps
+// a private online-softmax state (max, sum, accumulator of its 16-byte dim
+// chunk) per query head of the group over the token rows it sees; lanes of
+// one token row share the logit after a DPP reduction.  States are merged
+// across lanes, then waves; the split's state goes to the workspace, and a
+// small second kernel merges the splits of every (request, query head) by
+// log-sum-exp.  (Merging in the last-arriving split instead needs an
+// agent-scope fence per workgroup, which on this multi-XCD part writes back
+// and invalidates the XCD's L2 each time; the kernel boundary does that once.)
 #include "qas_device.h"
 #include "qas_internal.h"
 
@@ -23,7 +29,8 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDecUnroll = 8;          // token groups in flight per wave
+// token groups in flight per wave (bounded by registers)
+template <int G> constexpr int dec_unroll() { return G <= 2 ? 16 : 8; }
 constexpr int kDecMaxList = 1024;      // selected entries per split
 constexpr int kDecMaxRow = 4096;       // entries of a row when deduplicating
 constexpr float kLog2e = 1.4426950408889634f;
@@ -104,19 +111,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
   }
+  const int32_t* prow = a.sel_phys ? a.sel_phys + ((size_t)r * H + h) * a.sel_stride : nullptr;
   int npg = 0;
   for (int eb = e0; eb < e1; eb += kDecThreads) {
     const int e = eb + tid;
-    int id = -1;
+    int id = -1, phys = 0;
     bool keep = false;
     if (e < e1) {
       id = a.dedupe ? s_row[e] : row[e];
+      if (prow) phys = prow[e];
       keep = a.dedupe ? s_keep[e - e0] != 0 : (id >= 0 && id < n_pages);
     }
     int total;
     const int pos = npg + block_excl_count(keep, s_cnt, &total);
     if (keep) {
-      s_phys[pos] = a.page_indices[pbeg + id];
+      s_phys[pos] = prow ? phys : a.page_indices[pbeg + id];
       s_ntok[pos] = min(S, L - id * S);
     }
     npg += total;
@@ -147,11 +156,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
 
-  for (int u0 = wave; u0 < units; u0 += kDecWaves * kDecUnroll) {
-    uint4 kr[kDecUnroll], vr[kDecUnroll];
-    bool ok[kDecUnroll];
+  constexpr int UNR = dec_unroll<G>();
+  for (int u0 = wave; u0 < units; u0 += kDecWaves * UNR) {
+    uint4 kr[UNR], vr[UNR];
+    bool ok[UNR];
 #pragma unroll
-    for (int b = 0; b < kDecUnroll; ++b) {
+    for (int b = 0; b < UNR; ++b) {
       const int u = u0 + b * kDecWaves;
       kr[b] = make_uint4(0, 0, 0, 0);
       vr[b] = make_uint4(0, 0, 0, 0);
@@ -169,10 +179,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      float z[kDecUnroll];
+      float z[UNR];
       float zmax = m_run[gg];
 #pragma unroll
-      for (int b = 0; b < kDecUnroll; ++b) {
+      for (int b = 0; b < UNR; ++b) {
         float kf[EPL];
         unpack16<DT>(kr[b], kf);
         float dot = 0.f;
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[gg][e] *= alpha;
 #pragma unroll
-      for (int b = 0; b < kDecUnroll; ++b) {
+      for (int b = 0; b < UNR; ++b) {
         if (!ok[b]) continue;
         const float p = fast_exp2(z[b] - zmax);
         float vf[EPL];
@@ -243,30 +253,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     }
     part[2 + dim] = o;
   }
+
 }
 
-// Log-sum-exp merge of the split states of one (request, query head).
+// Log-sum-exp merge of the split states of one (request, query head): one
+// workgroup per row, one thread per output dim; the split states are loaded
+// MB at a time (independent loads in flight) and merged online.
 template <int DT, int D>
-__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
-  const int row = blockIdx.x;  // r * H_q + i
-  const float* part = a.partials + (size_t)row * a.n_split * (D + 2);
-  for (int dim = threadIdx.x; dim < D; dim += blockDim.x) {
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, part[s * (D + 2)]);
-    float o = 0.f, lsum = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.n_split; ++s) {
-        const float ms = part[s * (D + 2)];
-        const float w = fast_exp2(ms - M);
-        lsum += part[s * (D + 2) + 1] * w;
-        o += part[s * (D + 2) + 2 + dim] * w;
-      }
-      o = o / lsum;
+__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+  constexpr int MB = 16;
+  const int rowq = blockIdx.x;                 // r * H_q + i
+  const int dim = threadIdx.x;
+  const float* part = a.partials + (size_t)rowq * a.n_split * (D + 2);
+  float M = -INFINITY, lsum = 0.f, o = 0.f;
+  for (int sb = 0; sb < a.n_split; sb += MB) {
+    float ms[MB], ls[MB], os[MB];
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const int sp = sb + k;
+      const bool in = sp < a.n_split;
+      ms[k] = in ? part[sp * (D + 2)] : -INFINITY;
+      ls[k] = in ? part[sp * (D + 2) + 1] : 0.f;
+      os[k] = in ? part[sp * (D + 2) + 2 + dim] : 0.f;
     }
-    store_rn<DT>(a.out, (size_t)row * D + dim, o);
-    if (dim == 0 && a.lse)
-      a.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(lsum)) * 0.6931471805599453f;
+#pragma unroll
+    for (int k = 0; k < MB; ++k) merge_state<1>(M, lsum, &o, ms[k], ls[k], &os[k]);
   }
+  o = M == -INFINITY ? 0.f : o / lsum;
+  store_rn<DT>(a.out, (size_t)rowq * D + dim, o);
+  if (dim == 0 && a.lse)
+    a.lse[rowq] = M == -INFINITY ? -INFINITY : (M + log2f(lsum)) * 0.6931471805599453f;
 }
 
 template <int DT, int D, int G>
@@ -276,7 +292,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<DT, D, G>), grid, dim3(kDecThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(a.B * a.H_q), dim3(128), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(a.B * a.H_q), dim3(D), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/qas.h"
+#include "qas.h"
 #include "qas_internal.h"
 
 namespace {
@@ -73,6 +73,9 @@ qas_status check_heads(const qas_cache* c, int num_q_heads, int* g) {
   return QAS_OK;
 }
 
+// Workspace layout:
+//   sparse decode: [split partials]
+//   decode layer:  [scores][sel][sel_phys][split partials]
 struct DecodePlan {
   int n_split;
   size_t partial_bytes;
@@ -98,6 +101,10 @@ qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q,
                           int g, float* scores) {
   qas::ScoreArgs a;
   a.summary = c->summary;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
   a.q = q;
   a.seq_lens = b->seq_lens;
   a.page_indptr = b->page_indptr;
@@ -111,8 +118,7 @@ qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q,
   a.max_pages = b->max_pages;
   a.kv_dtype = c->kv_dtype;
   a.g = g;
-  a.recs_per_block = qas::score_recs_per_block(c->kv_dtype, c->head_dim,
-                                               (long)b->total_pages * c->num_kv_heads);
+  a.pages_per_iter = qas::score_pages_per_iter(c->kv_dtype, c->head_dim, c->num_kv_heads);
   return a;
 }
 
@@ -128,6 +134,7 @@ qas::DecodeArgs decode_args(const qas_cache* c, const qas_batch* b, const void* 
   a.page_indptr = b->page_indptr;
   a.page_indices = b->page_indices;
   a.sel = sel;
+  a.sel_phys = nullptr;
   a.out = out;
   a.lse = lse;
   a.partials = partials;
@@ -197,10 +204,11 @@ size_t qas_workspace_bytes(int32_t op, const qas_cache* cache, const qas_batch* 
   if (!cache || !batch || batch->batch < 1 || cache->num_kv_heads < 1 || num_q_heads < 1 ||
       k < 1)
     return 0;
-  if (op == QAS_OP_SPARSE_DECODE) return plan_decode(cache, batch, num_q_heads, k).partial_bytes;
+  const DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
+  if (op == QAS_OP_SPARSE_DECODE) return p.partial_bytes;
   if (op == QAS_OP_DECODE_LAYER)
-    return layer_scores_bytes(cache, batch) + layer_sel_bytes(cache, batch, k) +
-           plan_decode(cache, batch, num_q_heads, k).partial_bytes;
+    return layer_scores_bytes(cache, batch) + 2 * layer_sel_bytes(cache, batch, k) +
+           p.partial_bytes;
   return 0;
 }
 
@@ -234,6 +242,9 @@ qas_status qas_score_pages(const qas_cache* cache, const qas_batch* batch, const
   if (!q || !scores) return fail(QAS_ERR_NULL, "q / scores is NULL");
   if (q_dtype != cache->kv_dtype)
     return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
+  if (!qas::score_supported(cache->kv_dtype, cache->head_dim, g, cache->num_kv_heads))
+    return fail(QAS_ERR_UNSUPPORTED, "score: %d KV heads of d=%d", cache->num_kv_heads,
+                cache->head_dim);
   if (batch->max_pages == 0) return ok();
   qas::ScoreArgs a = score_args(cache, batch, q, num_q_heads, g, scores);
   hipError_t e = qas::launch_score(a, (hipStream_t)stream);
@@ -257,7 +268,9 @@ qas_status qas_topk_pages(const float* scores, const qas_batch* batch, int32_t n
   a.scores = scores;
   a.seq_lens = batch->seq_lens;
   a.page_indptr = batch->page_indptr;
+  a.page_indices = batch->page_indices;
   a.sel = sel;
+  a.sel_phys = nullptr;
   a.sel_count = sel_count;
   a.B = batch->batch;
   a.H_kv = num_kv_heads;
@@ -317,31 +330,34 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, k);
   if (!workspace || workspace_bytes < need)
     return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!qas::score_supported(cache->kv_dtype, cache->head_dim, g, cache->num_kv_heads))
+    return fail(QAS_ERR_UNSUPPORTED, "score: %d KV heads of d=%d", cache->num_kv_heads,
+                cache->head_dim);
   hipStream_t s = (hipStream_t)stream;
+  const DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
   char* ws = (char*)workspace;
   float* scores = (float*)ws;
   ws += layer_scores_bytes(cache, batch);
-  int32_t* sel = sel_out;
-  int32_t* sel_ws = (int32_t*)ws;
+  int32_t* sel = sel_out ? sel_out : (int32_t*)ws;
   ws += layer_sel_bytes(cache, batch, k);
-  if (!sel) sel = sel_ws;
-  DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
+  int32_t* sel_phys = (int32_t*)ws;
+  ws += layer_sel_bytes(cache, batch, k);
   float* partials = (float*)ws;
 
+  // 1. page bounds (with the current token's append folded in)
   hipError_t e;
-  if (k_new) {
-    qas::AppendArgs aa = append_args(cache, batch, nullptr, 1, k_new, v_new);
-    if ((e = qas::launch_append(aa, s)) != hipSuccess) return hip_fail(e, "append launch");
-  }
-  if (batch->max_pages > 0) {
-    qas::ScoreArgs sa = score_args(cache, batch, q, num_q_heads, g, scores);
-    if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
-  }
+  qas::ScoreArgs sa = score_args(cache, batch, q, num_q_heads, g, scores);
+  sa.k_new = k_new;
+  sa.v_new = v_new;
+  if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
+  // 2. top-k per (request, KV head), logical and physical page lists
   qas::TopkArgs ta;
   ta.scores = scores;
   ta.seq_lens = batch->seq_lens;
   ta.page_indptr = batch->page_indptr;
+  ta.page_indices = batch->page_indices;
   ta.sel = sel;
+  ta.sel_phys = qas::topk_phys_fits(batch->max_pages) ? sel_phys : nullptr;
   ta.sel_count = nullptr;
   ta.B = batch->batch;
   ta.H_kv = cache->num_kv_heads;
@@ -349,8 +365,10 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   ta.k = k;
   ta.max_pages = batch->max_pages;
   if ((e = qas::launch_topk(ta, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+  // 3. sparse attention with the split merge
   qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, sel, k, k, sm_scale, out, lse,
                                    partials, p.n_split, 0);
+  da.sel_phys = ta.sel_phys;
   if ((e = qas::launch_decode(da, s)) != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }

@@ -9,31 +9,39 @@
 namespace qas {
 
 struct ScoreArgs {
-  const void* summary;       // [pool][H_kv][2][d]
+  void* summary;             // [pool][H_kv][2][d]
   const void* q;             // [B][H_q][d]
   const int32_t* seq_lens;
   const int32_t* page_indptr;
   const int32_t* page_indices;
   float* scores;
+  // optional decode append of the token at seq_lens[r] - 1 (k_new != NULL)
+  const void* k_new;         // [B][H_kv][d]
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
   int B, H_kv, H_q, d, S, max_pages;
   int kv_dtype, g;
-  int recs_per_block;        // (page, KV head) records per workgroup
+  int pages_per_iter;        // pages one workgroup covers per lane step
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
-bool score_supported(int kv_dtype, int d, int g);
-int score_recs_per_block(int kv_dtype, int d, long total_recs);
+bool score_supported(int kv_dtype, int d, int g, int H_kv);
+int score_pages_per_iter(int kv_dtype, int d, int H_kv);
 
 struct TopkArgs {
   const float* scores;
   const int32_t* seq_lens;
   const int32_t* page_indptr;
+  const int32_t* page_indices;
   int32_t* sel;
+  int32_t* sel_phys;         // optional physical pages of `sel`
   int32_t* sel_count;
   int B, H_kv, S, k;
   int max_pages;             // longest row (sizes the LDS key array)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-constexpr int kTopkMaxPages = 15360;  // 60 KiB of LDS keys
+constexpr int kTopkMaxPages = 16000;  // keys + histogram within 64 KiB of LDS
+bool topk_phys_fits(int max_pages);    // physical lists also fit in LDS
 
 struct AppendArgs {
   void* k_pool;
@@ -59,6 +67,7 @@ struct DecodeArgs {
   const int32_t* page_indptr;
   const int32_t* page_indices;
   const int32_t* sel;
+  const int32_t* sel_phys;   // physical pages of sel (canonical lists), or NULL
   void* out;
   float* lse;
   float* partials;           // [B][H_q][n_split][2 + d]

@@ -1,11 +1,21 @@
 // Page-score kernel: the Quest page bound ("3.1.1 · Quest", §1.1 eq. (2)-(3))
-// with the group-max aggregate for grouped-query heads (§2.1).
+// with the group-max aggregate for grouped-query heads (§2.1), optionally
+// preceded by the decode append of the current token (§1.2 eq. (8)).
 //
-// The summaries of one request are streamed as (page, KV head) records of
-// 2*d elements ([min | max]).  A record is read by RL = d*bytes/16 lanes,
-// each lane holding 16 bytes of min and the matching 16 bytes of max, so a
-// wave reads whole 512-byte records with 16-byte loads.  Each thread keeps
-// U records in flight.  Queries live in LDS as fp32.
+// Lane layout: a page's record for one KV head is 2*d elements ([min | max])
+// read by RL = d*bytes/16 lanes, each holding 16 bytes of min and the
+// matching 16 bytes of max.  A workgroup has H_kv * RL * PPI lanes, so every
+// lane keeps one KV head and one 16-byte dim chunk for the whole kernel
+// (its query slice lives in registers) and walks PPI-strided pages of the
+// workgroup's page range, U pages in flight.  Dependent global loads are
+// three levels deep: request bounds and queries, then the page table, then
+// the summaries.
+//
+// Fused append: the lanes that own the request's tail page first copy the
+// current token's K/V row into the pool and fold the key into the page's
+// min/max (starting from +-inf when the token opens the page), then score
+// the updated record.  No other workgroup reads that record, and the
+// attention stage runs in a later kernel, so no synchronisation is needed.
 #include "qas_device.h"
 #include "qas_internal.h"
 
@@ -13,89 +23,137 @@ namespace qas {
 
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 4;
+constexpr int kScoreUnroll = 4;       // pages in flight per lane
+
+// elementwise min / max of two 16-byte chunks of stored values (exact)
+template <int DT, bool IS_MAX>
+__device__ __forceinline__ uint4 minmax16(const uint4& a, const uint4& b) {
+  constexpr int EPL = epl<DT>();
+  float fa[EPL], fb[EPL];
+  unpack16<DT>(a, fa);
+  unpack16<DT>(b, fb);
+  typedef typename Store<DT>::T ST;
+  ST out[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    out[e] = Store<DT>::from(IS_MAX ? fmaxf(fa[e], fb[e]) : fminf(fa[e], fb[e]));
+  return *reinterpret_cast<const uint4*>(out);
+}
 
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(1024) void score_kernel(ScoreArgs a) {
   constexpr int EPL = epl<DT>();
   constexpr int RL = D / EPL;                 // lanes per record half
-  constexpr int RPB = kScoreThreads / RL;     // records per block iteration
   constexpr int BYTES = DType<DT>::bytes;
-  extern __shared__ float q_lds[];            // [H_q][D] fp32
 
   const int r = blockIdx.y;
   const int H = a.H_kv;
+  const int tid = threadIdx.x;
+  const int lanes_pp = H * RL;                // lanes per page
+  const int ps = tid / lanes_pp;              // page slot
+  const int h = (tid / RL) % H;
+  const int c = tid % RL;
+  const int PPI = a.pages_per_iter;
+  const int j0 = blockIdx.x * PPI * kScoreUnroll;
+
+  // level 1: request bounds, query slices, the appended token
   const int pbeg = a.page_indptr[r];
   const int P_r = a.page_indptr[r + 1] - pbeg;
-  const int total = P_r * H;
-  const int rec0 = blockIdx.x * a.recs_per_block;
-  if (rec0 >= total) return;
-  const int rec1 = min(rec0 + a.recs_per_block, total);
   const int L = a.seq_lens[r];
-  const int n_used = min((L + a.S - 1) / a.S, P_r);
+  float qf[G][EPL];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const uint4 qr = load16(reinterpret_cast<const char*>(a.q) +
+                            (((size_t)r * a.H_q + h * G + gg) * D) * BYTES + c * 16);
+    unpack16<DT>(qr, qf[gg]);
+  }
+  uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+  const bool appending = a.k_new != nullptr && L > 0;
+  if (appending) {
+    const size_t o = (((size_t)r * H + h) * D) * BYTES + c * 16;
+    knew = load16(reinterpret_cast<const char*>(a.k_new) + o);
+    vnew = load16(reinterpret_cast<const char*>(a.v_new) + o);
+  }
+  if (j0 >= P_r) return;
+  const int n_used = L > 0 ? min((L + a.S - 1) / a.S, P_r) : 0;
+  const int tail = n_used - 1;
 
-  const int tid = threadIdx.x;
-  const int HQ = a.H_q;
-  for (int i = tid; i < HQ * D; i += kScoreThreads)
-    q_lds[i] = load_scalar<DT>(a.q, (size_t)r * HQ * D + i);
-  __syncthreads();
-
-  const int slot = tid / RL;
-  const int c = tid % RL;
-  const int* pt = a.page_indices + pbeg;
-  float* srow = a.scores + (size_t)pbeg * H;
+  // level 2: page table
+  int j[kScoreUnroll];
+  int pp[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    j[u] = j0 + ps + u * PPI;
+    pp[u] = j[u] < n_used ? a.page_indices[pbeg + j[u]] : 0;
+  }
+  // level 3: summaries
   const char* sum_base = reinterpret_cast<const char*>(a.summary);
+  uint4 mn[kScoreUnroll], mx[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    mn[u] = make_uint4(0, 0, 0, 0);
+    mx[u] = make_uint4(0, 0, 0, 0);
+    if (j[u] < n_used) {
+      const char* p = sum_base + (((size_t)pp[u] * H + h) * 2 * D) * BYTES + c * 16;
+      const bool fresh = appending && j[u] == tail && ((L - 1) % a.S) == 0;
+      if (!fresh) {
+        mn[u] = load16(p);
+        mx[u] = load16(p + D * BYTES);
+      }
+    }
+  }
+  if (appending) {
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      if (j[u] != tail) continue;
+      const int off = (L - 1) % a.S;
+      if (off == 0) {          // the token opens the page: -inf/+inf start
+        mn[u] = knew;
+        mx[u] = knew;
+      } else {
+        mn[u] = minmax16<DT, false>(mn[u], knew);
+        mx[u] = minmax16<DT, true>(mx[u], knew);
+      }
+      char* p = reinterpret_cast<char*>(a.summary) + (((size_t)pp[u] * H + h) * 2 * D) * BYTES +
+                c * 16;
+      *reinterpret_cast<uint4*>(p) = mn[u];
+      *reinterpret_cast<uint4*>(p + D * BYTES) = mx[u];
+      const size_t row = ((((size_t)pp[u] * H + h) * a.S + off) * D) * BYTES + c * 16;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.k_pool) + row) = knew;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.v_pool) + row) = vnew;
+    }
+  }
 
-  for (int base = rec0; base < rec1; base += RPB * kScoreUnroll) {
-    uint4 mn[kScoreUnroll], mx[kScoreUnroll];
-    int rec[kScoreUnroll];
+  float* srow = a.scores + (size_t)pbeg * H + (size_t)h * P_r;
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      rec[u] = base + u * RPB + slot;
-      mn[u] = make_uint4(0, 0, 0, 0);
-      mx[u] = make_uint4(0, 0, 0, 0);
-      if (rec[u] < rec1) {
-        const int j = rec[u] / H, h = rec[u] - (rec[u] / H) * H;
-        if (j < n_used) {
-          const size_t pp = (size_t)pt[j];
-          const char* p = sum_base + ((pp * H + h) * 2 * D) * BYTES + c * 16;
-          mn[u] = load16(p);
-          mx[u] = load16(p + D * BYTES);
-        }
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    float m[EPL], M[EPL];
+    unpack16<DT>(mn[u], m);
+    unpack16<DT>(mx[u], M);
+    float best = -INFINITY;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float qe = qf[gg][e];
+        s += qe >= 0.f ? qe * M[e] : qe * m[e];   // eq. (2)
       }
+      s = group_sum<RL>(s);                       // eq. (3)
+      best = fmaxf(best, s);                      // group max
     }
-#pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const bool live = rec[u] < rec1;
-      const int j = rec[u] / H, h = rec[u] - (rec[u] / H) * H;
-      float m[EPL], M[EPL];
-      unpack16<DT>(mn[u], m);
-      unpack16<DT>(mx[u], M);
-      float best = -INFINITY;
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const float* qv = q_lds + ((live ? h : 0) * G + gg) * D + c * EPL;
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float qe = qv[e];
-          s += qe >= 0.f ? qe * M[e] : qe * m[e];   // eq. (2)
-        }
-        s = group_sum<RL>(s);                       // eq. (3)
-        best = fmaxf(best, s);                      // group max
-      }
-      if (live && c == 0) srow[(size_t)h * P_r + j] = j < n_used ? best : -INFINITY;
-    }
+    if (c == 0 && j[u] < P_r) srow[j[u]] = j[u] < n_used ? best : -INFINITY;
   }
 }
 
 template <int DT, int D, int G>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
-  const int rpb = a.recs_per_block;
-  dim3 grid((a.max_pages * a.H_kv + rpb - 1) / rpb, a.B);
-  size_t lds = (size_t)a.H_q * D * sizeof(float);
-  hipLaunchKernelGGL((score_kernel<DT, D, G>), grid, dim3(kScoreThreads), lds, s, a);
+  constexpr int RL = D / epl<DT>();
+  const int lanes_pp = a.H_kv * RL;
+  const int threads = lanes_pp * a.pages_per_iter;
+  const int ppb = a.pages_per_iter * kScoreUnroll;
+  dim3 grid((a.max_pages + ppb - 1) / ppb, a.B);
+  hipLaunchKernelGGL((score_kernel<DT, D, G>), grid, dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -122,18 +180,19 @@ hipError_t by_d(const ScoreArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool score_supported(int kv_dtype, int d, int g) {
-  return (kv_dtype == kF32 || kv_dtype == kF16 || kv_dtype == kBF16) &&
-         (d == 16 || d == 64 || d == 128) && (g == 1 || g == 2 || g == 4 || g == 8);
+bool score_supported(int kv_dtype, int d, int g, int H_kv) {
+  if (!(kv_dtype == kF32 || kv_dtype == kF16 || kv_dtype == kBF16)) return false;
+  if (!(d == 16 || d == 64 || d == 128)) return false;
+  if (!(g == 1 || g == 2 || g == 4 || g == 8)) return false;
+  const int rl = d * (kv_dtype == kF32 ? 4 : 2) / 16;
+  return H_kv * rl <= 1024;
 }
 
-int score_recs_per_block(int kv_dtype, int d, long total_recs) {
-  const int e = kv_dtype == kF32 ? 4 : 8;
-  const int rpb = kScoreThreads / (d / e) * kScoreUnroll;
-  long want = (total_recs + 1023) / 1024;
-  long n = (want + rpb - 1) / rpb;
-  if (n < 1) n = 1;
-  return (int)(n * rpb);
+int score_pages_per_iter(int kv_dtype, int d, int H_kv) {
+  const int rl = d * (kv_dtype == kF32 ? 4 : 2) / 16;
+  const int lanes_pp = H_kv * rl;
+  int ppi = 512 / lanes_pp;
+  return ppi < 1 ? 1 : ppi;
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {

@@ -11,7 +11,7 @@ import oracle
 from oracle import quest
 from tests.gpu_util import (ATTN_TOL, assert_attn_close, assert_scores_close,
                             check_selection, out_to_numpy, say, score_denominator)
-from workloads import (config1, config2, config3, config5, corrupt_lists,
+from workloads import (tiny_single_head, llama2_7b_layer, batched_gqa_append, stress_long_context, corrupt_lists,
                        figure2_case, worked_example_case)
 
 pytestmark = pytest.mark.gpu
@@ -40,11 +40,11 @@ SCORE_CASES = {
     "worked-example": lambda: worked_example_case(),
     "worked-example-b": lambda: worked_example_case(second_set=True),
     "figure2": lambda: figure2_case(),
-    "config1": lambda: config1(),
-    "config2-small-shuffled": lambda: config2(L=3001, H=4, identity_table=False),
-    "config3-small-gqa": lambda: config3(B=3, L_min=300, L_max=2000, steps=0),
-    "config5-small": lambda: config5(B=2, L=4096, H_q=8, H_kv=2),
-    "d64-bf16-g8": lambda: config3(B=2, L_min=100, L_max=700, H_q=16, H_kv=2, d=64,
+    "tiny_single_head": lambda: tiny_single_head(),
+    "llama2_7b_layer-small-shuffled": lambda: llama2_7b_layer(L=3001, H=4, identity_table=False),
+    "batched_gqa_append-small-gqa": lambda: batched_gqa_append(B=3, L_min=300, L_max=2000, steps=0),
+    "stress_long_context-small": lambda: stress_long_context(B=2, L=4096, H_q=8, H_kv=2),
+    "d64-bf16-g8": lambda: batched_gqa_append(B=2, L_min=100, L_max=700, H_q=16, H_kv=2, d=64,
                                    S=32, steps=0),
 }
 
@@ -123,7 +123,7 @@ def test_append_decode_steps_and_boundaries(qas, L):
     """Prefill L tokens, then decode-append 20 single tokens (crossing page
     boundaries); summaries stay exactly the oracle's after every step."""
     from query_aware_sparse_amd.staging import DeviceBatch, to_device
-    case = config3(B=2, L_min=L, L_max=L, H_q=4, H_kv=2, d=128, S=16, steps=20)
+    case = batched_gqa_append(B=2, L_min=L, L_max=L, H_q=4, H_kv=2, d=128, S=16, steps=20)
     pc, _ = _stage(qas, case)
     for s in range(case.steps):
         lengths = case.lengths(s)
@@ -158,7 +158,7 @@ def test_recycled_page_summary_equals_fresh(qas):
     owner, reused by a new request, ends with the same summary as a fresh
     page (the Quest page, §3, page recycling)."""
     from query_aware_sparse_amd.staging import DeviceBatch, PagedCache, to_device
-    case = config2(L=40, H=2, d=128, identity_table=False)
+    case = llama2_7b_layer(L=40, H=2, d=128, identity_table=False)
     pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
     pc.summary.fill_(1000.0)                     # stale values of a former owner
     pc.summary[:, :, 0].fill_(-1000.0)
@@ -191,10 +191,10 @@ def _sparse_decode(qas, case, pc, db, lists, step=-1):
 
 
 SPARSE_CASES = {
-    "config1": lambda: config1(),
-    "config2-small": lambda: config2(L=5000, H=4, K=40),
-    "config3-small": lambda: config3(B=3, L_min=900, L_max=3000, steps=0, K=37),
-    "config5-small": lambda: config5(B=4, L=6000, H_q=8, H_kv=2, K=12),
+    "tiny_single_head": lambda: tiny_single_head(),
+    "llama2_7b_layer-small": lambda: llama2_7b_layer(L=5000, H=4, K=40),
+    "batched_gqa_append-small": lambda: batched_gqa_append(B=3, L_min=900, L_max=3000, steps=0, K=37),
+    "stress_long_context-small": lambda: stress_long_context(B=4, L=6000, H_q=8, H_kv=2, K=12),
 }
 
 
@@ -232,7 +232,7 @@ def test_sparse_decode_on_corrupted_lists(qas, name):
 
 def test_dense_fallback_all_pages(qas):
     """K = all pages reproduces dense paged attention (the Quest page, §1.2)."""
-    case = config2(L=2000, H=2, K=10000)
+    case = llama2_7b_layer(L=2000, H=2, K=10000)
     pc, db = _stage(qas, case)
     q = _q(case)
     out = torch.empty_like(q)
@@ -257,7 +257,7 @@ def test_empty_and_zero_length_requests(qas):
     """A zero-length request in a ragged batch gets no pages, no selection and
     a zero output; its neighbours are unaffected."""
     from query_aware_sparse_amd.staging import DeviceBatch, PagedCache, prefill
-    case = config3(B=3, L_min=100, L_max=400, steps=0, K=8)
+    case = batched_gqa_append(B=3, L_min=100, L_max=400, steps=0, K=8)
     case.seq_lens[1] = 0
     pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
     db = prefill(pc, case)
@@ -277,3 +277,24 @@ def test_empty_and_zero_length_requests(qas):
     ref = oracle.run_decode(case, requests=[0, 2])
     for r, res in zip((0, 2), ref):
         assert_attn_close(got[r], res["out"], "bf16", f"r={r}")
+
+
+def test_long_rows_without_physical_lists(qas):
+    """Rows too long for top-K to also keep their page table in LDS (more than
+    8064 pages): attention then translates pages through the page table."""
+    case = tiny_single_head(L=33000, S=4, K=300)            # 8250 pages, fp32, d=16
+    pc, db = _stage(qas, case)
+    q = _q(case)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 1), device="cuda")
+    sel = torch.empty((1, 1, case.K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
+                                             case.H_q, case.K), dtype=torch.uint8,
+                     device="cuda")
+    qas.qas_decode_layer(pc.cache, db.batch, q, case.K, case.sm_scale, out, lse, ws,
+                         sel_out=sel)
+    torch.cuda.synchronize()
+    ref = oracle.run_decode(case)[0]
+    from tests.gpu_util import check_selection
+    if check_selection(sel.cpu().numpy()[0, 0], ref["U"][0], case.K):
+        assert_attn_close(out_to_numpy(out)[0], ref["out"], "f32", "long row")

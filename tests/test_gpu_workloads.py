@@ -10,7 +10,7 @@ import torch
 import oracle
 from tests.gpu_util import (assert_attn_close, assert_scores_close, check_selection,
                             out_to_numpy, say, score_denominator)
-from workloads import (config1, config2, config3, config5, corrupt_lists, figure2_case,
+from workloads import (tiny_single_head, llama2_7b_layer, batched_gqa_append, stress_long_context, corrupt_lists, figure2_case,
                        worked_example_case)
 
 pytestmark = pytest.mark.gpu
@@ -94,7 +94,7 @@ def compare(case, got_out, got_lse, got_sel, ref, requests, got_scores=None, db=
 
 
 @pytest.mark.parametrize("make", [worked_example_case, lambda: worked_example_case(True),
-                                  config1], ids=["worked", "worked-b", "config1"])
+                                  tiny_single_head], ids=["worked", "worked-b", "tiny_single_head"])
 def test_tiny_cases(qas, make):
     case = make()
     say(f"[e2e] {case.name}")
@@ -120,10 +120,10 @@ def test_figure2_two_steps(qas):
     assert_attn_close(out1[0], ref[0]["out"], "f32", "figure2 step t+1")
 
 
-def test_config2_llama_layer_full(qas):
+def test_llama2_7b_layer_full(qas):
     """Llama-2-7B-shaped decode layer, full size (32K context, 2048 pages,
     K=256, 32x128 heads, fp16): every score, set and output."""
-    case = config2()
+    case = llama2_7b_layer()
     say(f"[e2e] {case.name} L={case.seq_lens[0]}")
     lay = Layer(qas, case)
     out, lse, sel, db = lay.call()
@@ -136,10 +136,10 @@ def test_config2_llama_layer_full(qas):
         assert np.array_equal(l2, lse)
 
 
-def test_config2_attention_on_oracle_sets(qas):
-    """The attention stage at full config-2 size on the oracle's own sets, so
+def test_llama2_7b_layer_attention_on_oracle_sets(qas):
+    """The attention stage of the full Llama-shaped layer on the oracle's own sets, so
     every head is compared even where a near tie lets the sets differ."""
-    case = config2()
+    case = llama2_7b_layer()
     lay = Layer(qas, case)
     ref = oracle.run_decode(case)
     lists = np.array([[ref[0]["sel"][h] for h in range(case.H_kv)]], dtype=np.int32)
@@ -154,15 +154,15 @@ def test_config2_attention_on_oracle_sets(qas):
     qas.qas_sparse_decode(lay.pc.cache, lay.db.batch, q, sel, case.K, case.sm_scale, out,
                           lse, ws)
     torch.cuda.synchronize()
-    assert_attn_close(out_to_numpy(out)[0], ref[0]["out"], "f16", "config2 on oracle sets")
+    assert_attn_close(out_to_numpy(out)[0], ref[0]["out"], "f16", "llama2_7b_layer on oracle sets")
 
 
-def test_config3_batched_gqa_with_append(qas):
+def test_batched_gqa_with_append(qas):
     """8 requests of 8K-64K tokens, 32/8 heads, bf16, K=128: 16 decode steps,
     each appending one token per request (one page boundary crossed per
     request).  The oracle checks the first call and a sample of steps; the
     summaries after the last append are checked in full."""
-    case = config3()
+    case = batched_gqa_append()
     say(f"[e2e] {case.name} lengths={case.seq_lens.tolist()}")
     lay = Layer(qas, case)
     decoded = {r: oracle.decoded_kv(case, r) for r in range(case.B)}
@@ -182,12 +182,12 @@ def test_config3_batched_gqa_with_append(qas):
         assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
 
 
-def test_config5_stress(qas):
+def test_stress_long_context(qas):
     """16 requests at 131072 tokens, 32/8 heads, S=32, K=41, Student-t keys,
     fp16: decode-layer call checked on a seeded sample of requests; then
     attention on corrupted lists (duplicates, invalid IDs, fully invalid
     rows) built from the oracle's own top-K of the sampled requests."""
-    case = config5()
+    case = stress_long_context()
     say(f"[e2e] {case.name} K={case.K}")
     lay = Layer(qas, case)
     out, lse, sel, db = lay.call()
@@ -217,7 +217,7 @@ def test_config5_stress(qas):
     got = out_to_numpy(o)
     ref2 = oracle.run_decode(case, page_ids=bad, requests=reqs, decoded=decoded)
     for r, res in zip(reqs, ref2):
-        assert_attn_close(got[r], res["out"], "f16", f"config5 corrupted r={r}")
+        assert_attn_close(got[r], res["out"], "f16", f"stress_long_context corrupted r={r}")
     empty_rows = np.argwhere(cat == 4)
     assert len(empty_rows) > 0
     for r, h in empty_rows:

@@ -15,7 +15,7 @@ import torch
 
 from oracle import quest, run_decode
 from tests.conftest import load_golden
-from workloads import config1, config2, config3, figure2_case, worked_example_case
+from workloads import tiny_single_head, llama2_7b_layer, batched_gqa_append, figure2_case, worked_example_case
 
 
 def _rng(seed):
@@ -338,7 +338,7 @@ def test_sparse_output_error_bound_eq7():
 def test_chunk_attention_per_query_matches_decode_definition():
     """A chunk query with c = L-1 and the request's own page list is exactly
     the decode result; executing as a union does not change the result."""
-    case = config1()
+    case = tiny_single_head()
     keys = case.keys[0].astype(np.float64)
     values = case.values[0].astype(np.float64)
     q = case.q[0, 0].astype(np.float64)
@@ -349,12 +349,12 @@ def test_chunk_attention_per_query_matches_decode_definition():
 
 
 def test_workload_cases_are_well_formed():
-    c1 = config1()
+    c1 = tiny_single_head()
     assert c1.keys[0].shape == (64, 1, 16) and c1.K == 4
     assert sorted(c1.pages[0].tolist()) == sorted(set(c1.pages[0].tolist()))
-    c2 = config2(L=256, H=2)
+    c2 = llama2_7b_layer(L=256, H=2)
     assert c2.keys[0].dtype == np.float16 and c2.keys[0].shape == (256, 2, 128)
-    c3 = config3(B=2, L_min=40, L_max=70, steps=3)
+    c3 = batched_gqa_append(B=2, L_min=40, L_max=70, steps=3)
     assert all(k.shape[0] == L + 3 for k, L in zip(c3.keys, c3.seq_lens))
     flat = np.concatenate(c3.pages)
     assert len(set(flat.tolist())) == len(flat) and flat.max() < c3.num_pool_pages

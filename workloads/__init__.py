@@ -14,10 +14,10 @@ RNG: numpy ``default_rng(SeedSequence([seed, stream, index...]))`` drawing
 float32 (or float64 for Student-t), then cast with round-to-nearest-even:
 numpy for fp16, torch CPU casts for bf16 and float8_e4m3fn.
 """
-from .cases import (DecodeCase, ChunkCase, config1, config2, config3,
-                    config4, config5, corrupt_lists, worked_example_case,
-                    figure2_case, STEP_STREAM)
+from .cases import (DecodeCase, ChunkCase, tiny_single_head, llama2_7b_layer, batched_gqa_append,
+                    multiquery_chunk, stress_long_context, corrupt_lists, worked_example_case,
+                    figure2_case, layer_queries, STEP_STREAM)
 
-__all__ = ["DecodeCase", "ChunkCase", "config1", "config2", "config3",
-           "config4", "config5", "corrupt_lists", "worked_example_case",
-           "figure2_case", "STEP_STREAM"]
+__all__ = ["DecodeCase", "ChunkCase", "tiny_single_head", "llama2_7b_layer", "batched_gqa_append",
+           "multiquery_chunk", "stress_long_context", "corrupt_lists", "worked_example_case",
+           "figure2_case", "layer_queries", "STEP_STREAM"]

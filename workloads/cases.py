@@ -189,9 +189,9 @@ def _split_pages(flat, counts):
     return out
 
 
-# ----------------------------------------------------------------- configs --
+# --------------------------------------------------------------- workloads --
 
-def config1(seed=1, L=64, S=4, d=16, K=4):
+def tiny_single_head(seed=1, L=64, S=4, d=16, K=4):
     """Tiny single instance: 1 request, 1 KV head, 1 query head, d=16, S=4,
     L=64 (16 pages), K=4, fp32 N(0,1); physical pages are a seeded
     permutation inside a slightly larger pool."""
@@ -200,12 +200,12 @@ def config1(seed=1, L=64, S=4, d=16, K=4):
     q = _normal(seed, _QUERY, 0, (1, 1, 1, d))
     P = ceil_div(L, S)
     phys, pool = _pool_permutation(seed, P, 4)
-    return DecodeCase("config1-tiny", 1, 1, 1, d, S, K, "f32", "f32",
+    return DecodeCase("tiny-single-head-d16", 1, 1, 1, d, S, K, "f32", "f32",
                       np.array([L], np.int32), [keys], [values], q, [phys],
                       pool)
 
 
-def config2(seed=2, L=32768, H=32, d=128, S=16, K=256, outliers=4,
+def llama2_7b_layer(seed=2, L=32768, H=32, d=128, S=16, K=256, outliers=4,
             outlier_scale=8.0, identity_table=True):
     """Llama-2-7B-shaped decode layer: B=1, 32 query heads = 32 KV heads,
     d=128, S=16, L=32768 (2048 pages), K=256; fp16 K/V N(0,1) with 4 seeded
@@ -223,13 +223,13 @@ def config2(seed=2, L=32768, H=32, d=128, S=16, K=256, outliers=4,
         phys, pool = np.arange(P, dtype=np.int32), P
     else:
         phys, pool = _pool_permutation(seed, P, 8)
-    return DecodeCase("config2-llama2-7b-layer", 1, H, H, d, S, K, "f16",
+    return DecodeCase("llama2-7b-layer-32k", 1, H, H, d, S, K, "f16",
                       "f16", np.array([L], np.int32), [keys],
                       [values], cast(q, "f16"), [phys], pool,
                       notes="4 outlier channels per KV head x8 in K and V")
 
 
-def config3(seed=3, B=8, L_min=8192, L_max=65536, H_q=32, H_kv=8, d=128,
+def batched_gqa_append(seed=3, B=8, L_min=8192, L_max=65536, H_q=32, H_kv=8, d=128,
             S=16, K=128, steps=16):
     """Batched GQA decode with append: B requests, L_r ~ U{L_min..L_max},
     32 query / 8 KV heads, d=128, S=16, K=128, bf16 K/V/q N(0,1).  Each of
@@ -245,12 +245,12 @@ def config3(seed=3, B=8, L_min=8192, L_max=65536, H_q=32, H_kv=8, d=128,
     q = cast(_normal(seed, _QUERY, 0, (1 + steps, B, H_q, d)), "bf16")
     counts = [ceil_div(int(L) + steps, S) for L in lens]
     flat, pool = _pool_permutation(seed, sum(counts), 16)
-    return DecodeCase("config3-batched-gqa-append", B, H_q, H_kv, d, S, K,
+    return DecodeCase("batched-gqa-append", B, H_q, H_kv, d, S, K,
                       "bf16", "bf16", lens, keys, values, q,
                       _split_pages(flat, counts), pool, steps=steps)
 
 
-def config5(seed=5, B=16, L=131072, H_q=32, H_kv=8, d=128, S=32, K=None,
+def stress_long_context(seed=5, B=16, L=131072, H_q=32, H_kv=8, d=128, S=32, K=None,
             nu=3.0):
     """Stress: B requests at L tokens, 32 query / 8 KV heads, d=128, S=32,
     K = 1% of the pages rounded to nearest (41 for 4096 pages); keys are
@@ -265,7 +265,7 @@ def config5(seed=5, B=16, L=131072, H_q=32, H_kv=8, d=128, S=32, K=None,
         values.append(_tokens(seed, _VALUES, r, L, H_kv, d, "f16"))
     q = cast(_normal(seed, _QUERY, 0, (1, B, H_q, d)), "f16")
     flat, pool = _pool_permutation(seed, B * P, 32)
-    return DecodeCase("config5-stress", B, H_q, H_kv, d, S, K, "f16", "f16",
+    return DecodeCase("stress-16x128k", B, H_q, H_kv, d, S, K, "f16", "f16",
                       np.full(B, L, np.int32), keys, values, q,
                       _split_pages(flat, [P] * B), pool,
                       notes="Student-t(3) keys; lists corrupted after top-K")
@@ -322,7 +322,7 @@ def corrupt_lists(lists, num_pages, seed=5, n_slots=8):
     return lists.astype(np.int32), cat.reshape(B, H)
 
 
-def config4(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
+def multiquery_chunk(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
             keep=45, group=8):
     """Multi-query sparse chunk: one request of L tokens, S=64, N query
     positions c_i = L - N + i (L_i = L), each with its own kq-page set per KV
@@ -370,9 +370,20 @@ def config4(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
             prev = [int(p) for p in cur]
     P = ceil_div(L, S)
     phys, pool = _pool_permutation(seed, P, 8)
-    return ChunkCase("config4-multiquery-chunk", H_q, H_kv, d, S, L, N, kq,
+    return ChunkCase("multiquery-chunk-64k", H_q, H_kv, d, S, L, N, kq,
                      group, "e4m3", "bf16", k_codes, v_codes, k_scale,
                      v_scale, q, q_pos, q_len, sets, phys, pool)
+
+
+def layer_queries(case, n_layers, seed=2):
+    """Queries for n_layers copies of a single-call DecodeCase (one per layer
+    of a model): layer 0 keeps case.q[0], layer i > 0 draws N(0,1) from its
+    own stream.  Returns raw [n_layers][B][H_q][d] in case.q_dtype."""
+    out = [case.q[0]]
+    for i in range(1, n_layers):
+        out.append(cast(_normal(seed, _QUERY, 1000 + i, (case.B, case.H_q, case.d)),
+                        case.q_dtype))
+    return np.stack(out)
 
 
 # ------------------------------------------------------ pages' fixed cases --
