@@ -189,6 +189,58 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * Multi-query chunk ([PageWeaver] eq. (1)-(2) per query; query unions and
+ * membership masks, annotations SS2BST9I / AWLR3K97 / 5ALRMYYY).
+ *
+ * Query n belongs to request r with q_indptr[r] <= n < q_indptr[r+1]; it has
+ * its own page set per KV head, sets[n][h][0..kq), and causal limit
+ * q_pos[n] = c_n, and attends over
+ *   A = { t : floor(t/S) in its set, t < seq_lens[r], t <= c_n }
+ * (invalid IDs ignored, duplicates once, empty support -> 0, lse -inf).
+ * Queries are executed in groups of `group` consecutive queries of one
+ * request; a group's query heads of one KV head form one 32-row tile
+ * (group * (H_q / H_kv) <= 32, group <= 8, group * kq <= 1024) that walks
+ * the union of the group's page sets with per-query membership masks.
+ * Groups are numbered request by request; qas_chunk_groups() bounds their
+ * number for sizing.
+ */
+int32_t qas_chunk_groups(int32_t num_queries, int32_t batch, int32_t group);
+
+/*
+ * qas_union_pages - union preparation alone: for every group g and KV head
+ * h, the ascending union of the group's valid page IDs, its size, and one
+ * membership byte per union page (bit i: query i of the group holds the
+ * page).
+ *   union_pages  device [groups][H_kv][group * kq] int32, -1 padded
+ *   union_count  device [groups][H_kv] int32
+ *   membership   device [groups][H_kv][group * kq] uint8
+ * groups = qas_chunk_groups(num_queries, B, group); missing groups get 0.
+ */
+qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr,
+                           int32_t num_queries, const int32_t* sets,
+                           int32_t num_kv_heads, int32_t kq, int32_t group,
+                           int32_t page_size, int32_t* union_pages,
+                           int32_t* union_count, uint8_t* membership,
+                           void* stream);
+
+/*
+ * qas_chunk_attention - attention of every query of the chunk over its own
+ * support, executed over group unions with MFMA tiles.  The cache must be
+ * FP8 E4M3 with k_scale/v_scale (k = k_scale[h] * code); q is bf16
+ * [N][H_q][128]; out is bf16 [N][H_q][128], lse float [N][H_q] (may be
+ * NULL).  Page size 32 or 64.  QK^T runs with the query row quantised to
+ * e4m3 (per-row scale) and PV with probabilities scaled by 256 and
+ * quantised to e4m3; running max/sum and accumulation are fp32.  No summary
+ * is read and no workspace is needed.
+ */
+qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
+                               const int32_t* q_indptr, int32_t num_queries,
+                               const int32_t* q_pos, const void* q, int32_t q_dtype,
+                               int32_t num_q_heads, const int32_t* sets, int32_t kq,
+                               int32_t group, float sm_scale, void* out, float* lse,
+                               void* stream);
+
 enum { QAS_OP_SPARSE_DECODE = 1, QAS_OP_DECODE_LAYER = 2 };
 
 /*

@@ -57,26 +57,41 @@ _SIGNATURES = {
     "qas_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
                               _P, _P, _P, ctypes.c_size_t, _P]),
     "qas_workspace_bytes": (ctypes.c_size_t, [_I, _P, _P, _I, _I]),
+    "qas_chunk_groups": (_I, [_I, _I, _I]),
+    "qas_union_pages": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "qas_chunk_attention": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _I, _I, ctypes.c_float,
+                                 _P, _P, _P]),
     "qas_status_string": (ctypes.c_char_p, [_I]),
     "qas_last_error": (ctypes.c_char_p, []),
     "qas_version": (ctypes.c_char_p, []),
 }
 
 
+_lib = None
+
+
 def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m query_aware_sparse_amd.build` "
-            "(there is no non-HIP fallback)")
-    lib = ctypes.CDLL(LIB_PATH)
-    for name, (res, args) in _SIGNATURES.items():
-        fn = getattr(lib, name)
-        fn.restype = res
-        fn.argtypes = args
-    return lib
+    """Load libqas.so on first use (so the build step can import this package
+    before the library exists); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m query_aware_sparse_amd.build` "
+                "(there is no non-HIP fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
 
 
-lib = _load()
+def __getattr__(name):
+    if name == "lib":
+        return _load()
+    raise AttributeError(name)
 
 
 def _ptr(t):
@@ -91,7 +106,7 @@ def _stream(stream):
 
 def _check(status):
     if status != QAS_OK:
-        raise QasError(status, lib.qas_last_error().decode())
+        raise QasError(status, _load().qas_last_error().decode())
 
 
 def dtype_code(t):
@@ -120,31 +135,31 @@ def make_batch(seq_lens, page_indptr, page_indices, total_pages, max_pages):
 
 
 def qas_append(cache, batch, new_indptr, total_new, max_new, k_new, v_new, stream=None):
-    _check(lib.qas_append(ctypes.byref(cache), ctypes.byref(batch), _ptr(new_indptr),
+    _check(_load().qas_append(ctypes.byref(cache), ctypes.byref(batch), _ptr(new_indptr),
                           int(total_new), int(max_new), _ptr(k_new), _ptr(v_new),
                           _stream(stream)))
 
 
 def qas_score_pages(cache, batch, q, scores, stream=None):
-    _check(lib.qas_score_pages(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+    _check(_load().qas_score_pages(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
                                dtype_code(q), q.shape[1], _ptr(scores), _stream(stream)))
 
 
 def qas_topk_pages(scores, batch, num_kv_heads, page_size, k, sel, sel_count=None,
                    stream=None):
-    _check(lib.qas_topk_pages(_ptr(scores), ctypes.byref(batch), int(num_kv_heads),
+    _check(_load().qas_topk_pages(_ptr(scores), ctypes.byref(batch), int(num_kv_heads),
                               int(page_size), int(k), _ptr(sel), _ptr(sel_count),
                               _stream(stream)))
 
 
 def qas_workspace_bytes(op, cache, batch, num_q_heads, k):
-    return int(lib.qas_workspace_bytes(int(op), ctypes.byref(cache), ctypes.byref(batch),
+    return int(_load().qas_workspace_bytes(int(op), ctypes.byref(cache), ctypes.byref(batch),
                                        int(num_q_heads), int(k)))
 
 
 def qas_sparse_decode(cache, batch, q, sel, sel_len, sm_scale, out, lse, workspace,
                       stream=None):
-    _check(lib.qas_sparse_decode(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+    _check(_load().qas_sparse_decode(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
                                  dtype_code(q), q.shape[1], _ptr(sel), sel.shape[-1],
                                  int(sel_len), float(sm_scale), _ptr(out), _ptr(lse),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -153,7 +168,7 @@ def qas_sparse_decode(cache, batch, q, sel, sel_len, sm_scale, out, lse, workspa
 
 def qas_decode_layer(cache, batch, q, k, sm_scale, out, lse, workspace, k_new=None,
                      v_new=None, sel_out=None, stream=None):
-    _check(lib.qas_decode_layer(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+    _check(_load().qas_decode_layer(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
                                 dtype_code(q), q.shape[1], int(k), float(sm_scale),
                                 _ptr(k_new), _ptr(v_new), _ptr(sel_out), _ptr(out),
                                 _ptr(lse), _ptr(workspace),
@@ -161,10 +176,34 @@ def qas_decode_layer(cache, batch, q, k, sm_scale, out, lse, workspace, k_new=No
                                 _stream(stream)))
 
 
+def qas_chunk_groups(num_queries, batch, group):
+    return int(_load().qas_chunk_groups(int(num_queries), int(batch), int(group)))
+
+
+def qas_union_pages(batch, q_indptr, sets, group, page_size, union_pages, union_count,
+                    membership, stream=None):
+    """sets: int32 [N][H_kv][kq]; outputs sized by qas_chunk_groups()."""
+    N, H_kv, kq = sets.shape
+    _check(_load().qas_union_pages(ctypes.byref(batch), _ptr(q_indptr), N, _ptr(sets), H_kv, kq,
+                               int(group), int(page_size), _ptr(union_pages), _ptr(union_count),
+                               _ptr(membership), _stream(stream)))
+
+
+def qas_chunk_attention(cache, batch, q_indptr, q_pos, q, sets, group, sm_scale, out, lse=None,
+                        stream=None):
+    """q: bf16 [N][H_q][d]; sets: int32 [N][H_kv][kq]; out like q."""
+    N, H_q, _ = q.shape
+    _check(_load().qas_chunk_attention(ctypes.byref(cache), ctypes.byref(batch), _ptr(q_indptr), N,
+                                   _ptr(q_pos), _ptr(q), dtype_code(q), H_q, _ptr(sets),
+                                   sets.shape[-1], int(group), float(sm_scale), _ptr(out),
+                                   _ptr(lse), _stream(stream)))
+
+
 def version():
-    return lib.qas_version().decode()
+    return _load().qas_version().decode()
 
 
 __all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_sparse_decode",
-           "qas_decode_layer", "qas_workspace_bytes", "make_cache", "make_batch",
+           "qas_decode_layer", "qas_workspace_bytes", "qas_chunk_groups", "qas_union_pages",
+           "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

@@ -28,7 +28,7 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-SOURCES = ["qas_api.cpp", "append.hip", "score.hip", "topk.hip", "decode.hip"]
+SOURCES = ["qas_api.cpp", "append.hip", "score.hip", "topk.hip", "decode.hip", "union.hip"]
 
 
 def _compile(src, verbose):

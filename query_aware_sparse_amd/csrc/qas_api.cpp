@@ -373,4 +373,105 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   return ok();
 }
 
+int32_t qas_chunk_groups(int32_t num_queries, int32_t batch, int32_t group) {
+  if (num_queries < 0 || batch < 1 || group < 1) return 0;
+  return (num_queries + group - 1) / group + batch;
+}
+
+static qas_status check_chunk(const qas_batch* batch, const int32_t* q_indptr, int32_t num_queries,
+                              const int32_t* sets, int32_t num_kv_heads, int32_t kq,
+                              int32_t group, int32_t page_size) {
+  qas_status st = check_batch(batch);
+  if (st) return st;
+  if (!q_indptr || !sets) return fail(QAS_ERR_NULL, "q_indptr / sets is NULL");
+  if (num_queries < 1) return fail(QAS_ERR_SHAPE, "num_queries %d < 1", num_queries);
+  if (num_kv_heads < 1 || kq < 1 || group < 1 || group > 8 || group * kq > 1024)
+    return fail(QAS_ERR_SHAPE, "num_kv_heads %d / kq %d / group %d out of range", num_kv_heads,
+                kq, group);
+  if (page_size != 32 && page_size != 64)
+    return fail(QAS_ERR_UNSUPPORTED, "chunk attention: page_size %d not in {32, 64}", page_size);
+  if (batch->max_pages > qas::union_max_pages())
+    return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed %d", batch->max_pages,
+                qas::union_max_pages());
+  return QAS_OK;
+}
+
+static qas::UnionArgs union_args(const qas_batch* batch, const int32_t* q_indptr,
+                                 int32_t num_queries, const int32_t* sets, int32_t H_kv, int32_t kq,
+                                 int32_t group, int32_t S) {
+  qas::UnionArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.seq_lens = batch->seq_lens;
+  a.page_indptr = batch->page_indptr;
+  a.page_indices = batch->page_indices;
+  a.q_indptr = q_indptr;
+  a.sets = sets;
+  a.B = batch->batch;
+  a.H_kv = H_kv;
+  a.kq = kq;
+  a.group = group;
+  a.S = S;
+  a.max_groups = qas_chunk_groups(num_queries, batch->batch, group);
+  return a;
+}
+
+qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr, int32_t num_queries,
+                           const int32_t* sets, int32_t num_kv_heads, int32_t kq, int32_t group,
+                           int32_t page_size, int32_t* union_pages, int32_t* union_count,
+                           uint8_t* membership, void* stream) {
+  qas_status st = check_chunk(batch, q_indptr, num_queries, sets, num_kv_heads, kq, group,
+                              page_size);
+  if (st) return st;
+  if (!union_pages || !union_count || !membership)
+    return fail(QAS_ERR_NULL, "union outputs are NULL");
+  qas::UnionArgs a = union_args(batch, q_indptr, num_queries, sets, num_kv_heads, kq, group,
+                                page_size);
+  a.union_out = union_pages;
+  a.count_out = union_count;
+  a.member_out = membership;
+  hipError_t e = qas::launch_union_prep(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "union prep launch");
+  return ok();
+}
+
+qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
+                               const int32_t* q_indptr, int32_t num_queries, const int32_t* q_pos,
+                               const void* q, int32_t q_dtype, int32_t num_q_heads,
+                               const int32_t* sets, int32_t kq, int32_t group, float sm_scale,
+                               void* out, float* lse, void* stream) {
+  if (!cache) return fail(QAS_ERR_NULL, "cache is NULL");
+  qas_status st = check_chunk(batch, q_indptr, num_queries, sets, cache->num_kv_heads, kq, group,
+                              cache->page_size);
+  if (st) return st;
+  if (!cache->k_pool || !cache->v_pool || !cache->k_scale || !cache->v_scale)
+    return fail(QAS_ERR_NULL, "k_pool / v_pool / k_scale / v_scale is NULL");
+  if (!q || !out || !q_pos) return fail(QAS_ERR_NULL, "q / out / q_pos is NULL");
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(QAS_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                cache->num_kv_heads);
+  const int g = num_q_heads / cache->num_kv_heads;
+  if (!qas::union_supported(cache->kv_dtype, q_dtype, cache->head_dim, cache->page_size, g, group,
+                            kq))
+    return fail(QAS_ERR_UNSUPPORTED,
+                "chunk attention needs fp8 K/V, bf16 q, d=128, S in {32,64}, group*g <= 32 "
+                "(kv %d, q %d, d %d, S %d, g %d, group %d)",
+                cache->kv_dtype, q_dtype, cache->head_dim, cache->page_size, g, group);
+  qas::UnionArgs a = union_args(batch, q_indptr, num_queries, sets, cache->num_kv_heads, kq, group,
+                                cache->page_size);
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.q_pos = q_pos;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.H_q = num_q_heads;
+  a.g = g;
+  a.sm_scale = sm_scale;
+  hipError_t e = qas::launch_union_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "union attention launch");
+  return ok();
+}
+
 }  // extern "C"

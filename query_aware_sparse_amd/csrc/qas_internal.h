@@ -80,4 +80,29 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 bool decode_supported(int kv_dtype, int d, int g);
 int decode_num_splits(int rows, int sel_len);
 
+struct UnionArgs {
+  const void* k_pool;        // fp8 [pool][H_kv][S][d]
+  const void* v_pool;
+  const float* k_scale;      // [H_kv]
+  const float* v_scale;
+  const int32_t* seq_lens;
+  const int32_t* page_indptr;
+  const int32_t* page_indices;
+  const int32_t* q_indptr;   // [B+1] queries of each request
+  const int32_t* q_pos;      // [N] causal limit c_i
+  const void* q;             // bf16 [N][H_q][d]
+  const int32_t* sets;       // [N][H_kv][kq]
+  void* out;                 // bf16 [N][H_q][d]
+  float* lse;                // [N][H_q] or NULL
+  int32_t* union_out;        // union prep only: [groups][H_kv][group * kq]
+  int32_t* count_out;        //                  [groups][H_kv]
+  unsigned char* member_out; //                  [groups][H_kv][group * kq]
+  int B, H_kv, H_q, g, S, kq, group, max_groups;
+  float sm_scale;
+};
+hipError_t launch_union_attn(const UnionArgs& a, hipStream_t s);
+hipError_t launch_union_prep(const UnionArgs& a, hipStream_t s);
+bool union_supported(int kv_dtype, int q_dtype, int d, int S, int g, int group, int kq);
+int union_max_pages();
+
 }  // namespace qas

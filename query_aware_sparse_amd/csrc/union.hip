@@ -1,0 +1,440 @@
+// Multi-query chunk attention over query unions (the PageWeaver notes:
+// support semantics of eq. (1)-(2), annotation 2BIFS6UT; query union and
+// membership masks, SS2BST9I; union preparation, AWLR3K97; per-group tiles
+// that keep each query's own softmax, 5ALRMYYY; FP8 QK / FP8 PV with fp32
+// running statistics, SS2UKVF2).
+//
+// A group is `group` consecutive queries of one request; with g query heads
+// per KV head its rows form one 32-row MFMA tile (rows = query * g + head).
+// One workgroup per (group, KV head), mapped so that all groups of one KV
+// head land on the same XCD (their page unions overlap, so neighbours hit
+// in that XCD's L2):
+//   1. union preparation: each query's valid page IDs set bits in a per-query
+//      bitmap in LDS; OR-ing them gives the union, emitted in ascending page
+//      order with an 8-bit membership mask per page and its physical page;
+//   2. each wave streams its share of the union pages.  S^T = K Q^T with
+//      the fp8 K tile as A straight from HBM/L2 and Q quantised per row to
+//      e4m3 as B (v_mfma 32x32x64 f8f6f4); each lane then owns one row's
+//      logits, so the mask (membership, t <= c_i, t < L) and the online
+//      softmax are lane-local; P is scaled by 256 and quantised to e4m3 and
+//      feeds O^T += V^T P^T from registers, V^T being gathered from the
+//      page staged in LDS (rows padded to 136 bytes: conflict-free byte
+//      reads);
+//   3. the four waves' states are merged in LDS and written at the queries'
+//      own output rows.
+#include "qas_device.h"
+#include "qas_internal.h"
+
+namespace qas {
+
+namespace {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+constexpr int kUThreads = 256;
+constexpr int kUWaves = kUThreads / kWave;
+constexpr int kURows = 32;                  // MFMA tile rows
+constexpr int kUMaxGroup = 8;               // queries per group (membership byte)
+constexpr int kUMaxWords = 512;             // bitmap words: pages < 16384
+constexpr int kUMaxUnion = 1024;            // union pages per group
+constexpr int kUD = 128;                    // head dim
+constexpr int kUVStride = 136;              // LDS row stride of a staged V page
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct UnionShared {
+  uint32_t bm[kUMaxGroup][kUMaxWords];
+  int ulist[kUMaxUnion];
+  int uphys[kUMaxUnion];
+  unsigned char umask[kUMaxUnion];
+  int cpos[kUMaxGroup];
+  int wave_tot[kUWaves];
+  int count;
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Exclusive prefix sum over the workgroup (thread order), one barrier after
+// the per-wave totals are published; *total gets the sum.
+__device__ __forceinline__ int block_excl(int v, int* scratch, int* total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kUWaves; ++w) {
+    before += w < wave ? scratch[w] : 0;
+    all += scratch[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+struct GroupInfo {
+  int r, q0, nq;   // request, first query, queries in the group (0: none)
+};
+
+// Group gi of the launch: requests contribute ceil(n_r / group) groups each,
+// in request order.
+__device__ GroupInfo find_group(const int32_t* q_indptr, int B, int group, int gi) {
+  GroupInfo gr{0, 0, 0};
+  int base = 0;
+  for (int r = 0; r < B; ++r) {
+    const int a = q_indptr[r], n = q_indptr[r + 1] - a;
+    const int ng = (n + group - 1) / group;
+    if (gi < base + ng) {
+      const int local = gi - base;
+      gr.r = r;
+      gr.q0 = a + local * group;
+      gr.nq = min(group, n - local * group);
+      return gr;
+    }
+    base += ng;
+  }
+  return gr;
+}
+
+// Union of the group's page sets in ascending order with membership bits
+// and physical pages (the PageWeaver notes, SS2BST9I / AWLR3K97).  Returns
+// the union size; the lists are in `sh`.
+__device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo& gr, int h,
+                           int n_pages, int pbeg) {
+  const int tid = threadIdx.x;
+  const int words = (n_pages + 31) / 32;
+  for (int i = tid; i < kUMaxGroup * words; i += kUThreads) sh.bm[i / words][i % words] = 0;
+  // causal limits (the union preparation alone has none)
+  if (tid < kUMaxGroup) sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[gr.q0 + tid] : -1;
+  __syncthreads();
+  const int entries = gr.nq * a.kq;
+  for (int e = tid; e < entries; e += kUThreads) {
+    const int i = e / a.kq;
+    const int id = a.sets[((size_t)(gr.q0 + i) * a.H_kv + h) * a.kq + (e - i * a.kq)];
+    if (id >= 0 && id < n_pages) atomicOr(&sh.bm[i][id >> 5], 1u << (id & 31));
+  }
+  __syncthreads();
+  // each thread owns a contiguous run of bitmap words
+  const int per = (words + kUThreads - 1) / kUThreads;
+  const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t u = 0;
+    for (int i = 0; i < gr.nq; ++i) u |= sh.bm[i][w];
+    mine += __popc(u);
+  }
+  int total;
+  int pos = block_excl(mine, sh.wave_tot, &total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t u = 0;
+    for (int i = 0; i < gr.nq; ++i) u |= sh.bm[i][w];
+    while (u) {
+      const int b = __builtin_ctz(u);
+      u &= u - 1;
+      const int id = w * 32 + b;
+      unsigned char m = 0;
+      for (int i = 0; i < gr.nq; ++i) m |= ((sh.bm[i][w] >> b) & 1u) << i;
+      sh.ulist[pos] = id;
+      sh.umask[pos] = m;
+      ++pos;
+    }
+  }
+  __syncthreads();
+  // physical pages of the union: independent loads, all in flight together
+  for (int u = tid; u < total; u += kUThreads) sh.uphys[u] = a.page_indices[pbeg + sh.ulist[u]];
+  if (tid == 0) sh.count = total;
+  __syncthreads();
+  return total;
+}
+
+// order this wave's LDS accesses (a staged page is written and read by the
+// same wave only)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float lane_rowsum(float v) { return v + __shfl_xor(v, 32, kWave); }
+__device__ __forceinline__ float lane_rowmax(float v) { return fmaxf(v, __shfl_xor(v, 32, kWave)); }
+
+// e4m3 byte of x (|x| <= 448 after the clamp; the conversion does not saturate)
+__device__ __forceinline__ uint32_t to_e4m3(float x) {
+  x = fminf(fmaxf(x, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xffu;
+}
+
+template <int G, int NT>
+__global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
+  constexpr int S = 32 * NT;                  // page size
+  __shared__ UnionShared sh;
+  __shared__ __align__(16) unsigned char vstage[kUWaves][64 * kUVStride];
+
+  const int H = a.H_kv;
+  const int h = blockIdx.x % H;
+  const int gi = blockIdx.x / H;
+  const GroupInfo gr = find_group(a.q_indptr, a.B, a.group, gi);
+  if (gr.nq == 0) return;                     // uniform: no such group
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int L = a.seq_lens[gr.r];
+  const int pbeg = a.page_indptr[gr.r];
+  const int P_r = a.page_indptr[gr.r + 1] - pbeg;
+  const int n_pages = L > 0 ? min(min((L + S - 1) / S, P_r), kUMaxWords * 32) : 0;
+
+  const int U = build_union(sh, a, gr, h, n_pages, pbeg);
+
+  // ---- per-lane row: row = query * G + head (S^T / O^T column = lane % 32)
+  const int row = lane % 32, hf = lane / 32;
+  const int qi = row / G, hq = row % G;
+  const bool row_ok = qi < gr.nq;
+  const int cq = row_ok ? sh.cpos[qi] : -1;
+  // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row
+  float qf[64];
+  {
+    const size_t qbase = ((size_t)(gr.q0 + (row_ok ? qi : 0)) * a.H_q + h * G + hq) * kUD;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        qf[ks * 32 + e] = row_ok ? load_scalar<kBF16>(a.q, qbase + 64 * ks + 32 * hf + e) : 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(qf[e]));
+  amax = lane_rowmax(amax);
+  const float qs = amax > 0.f ? amax / 448.f : 1.f;
+  v8i_t qop[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    uint32_t w[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v |= to_e4m3(qf[ks * 32 + 4 * b + k] / qs) << (8 * k);
+      w[b] = v;
+    }
+    qop[ks] = *reinterpret_cast<v8i_t*>(w);
+  }
+  // logit scale (log2 units) of this row
+  const float zscale = qs * a.k_scale[h] * a.sm_scale * kLog2e;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  v16f_t acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  unsigned char* vs = vstage[wave];
+
+  for (int u = wave; u < U; u += kUWaves) {
+    const int id = sh.ulist[u];
+    const unsigned char mk = sh.umask[u];
+    const size_t tile = ((size_t)sh.uphys[u] * H + h) * S * kUD;   // bytes (fp8)
+    // K operand: token 32*tau + lane%32, dims 64*ks + 32*hf + [0, 32)
+    v8i_t kop[NT][2];
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* p = kbase + tile + (size_t)(32 * tau + row) * kUD + 64 * ks + 32 * hf;
+        const uint4 x0 = load16(p), x1 = load16(p + 16);
+        const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        kop[tau][ks] = *reinterpret_cast<const v8i_t*>(w);
+      }
+    // V page -> LDS, rows of kUVStride bytes (8-byte stores)
+    wave_lds_sync();                          // previous page's reads are done
+    uint4 vv[S * kUD / 16 / kWave];
+#pragma unroll
+    for (int c = 0; c < S * kUD / 16 / kWave; ++c)
+      vv[c] = load16(vbase + tile + (size_t)(c * kWave + lane) * 16);
+#pragma unroll
+    for (int c = 0; c < S * kUD / 16 / kWave; ++c) {
+      const int chunk = c * kWave + lane;
+      const int t = chunk / (kUD / 16), off = (chunk % (kUD / 16)) * 16;
+      uint2* dst = reinterpret_cast<uint2*>(vs + t * kUVStride + off);
+      dst[0] = make_uint2(vv[c].x, vv[c].y);
+      dst[1] = make_uint2(vv[c].z, vv[c].w);
+    }
+    wave_lds_sync();                          // staged page visible to the wave
+    // S^T = K Q^T: lane holds row `row`, tokens 32 tau + 8 (e/4) + 4 hf + e%4
+    v16f_t st[NT];
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[tau][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        st[tau] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[tau][ks], qop[ks], st[tau],
+                                                                  0, 0, 0, 0, 0, 0);
+    }
+    // mask + online softmax, lane-local per row
+    const bool member = row_ok && ((mk >> qi) & 1);
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = id * S + 32 * tau + 8 * (e / 4) + 4 * hf + (e % 4);
+        const bool ok = member && t <= cq && t < L;
+        st[tau][e] = ok ? st[tau][e] * zscale : -INFINITY;
+        zmax = fmaxf(zmax, st[tau][e]);
+      }
+    zmax = lane_rowmax(zmax);
+    const float m_new = fmaxf(m_run, zmax);
+    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T operand: 32 e4m3 bytes
+    const bool live = m_new != -INFINITY;       // same for both lanes of a row
+    float lsum = 0.f;
+    if (live) {
+#pragma unroll
+      for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(st[tau][e] - m_new);       // 0 for masked
+          const uint32_t b = to_e4m3(p * 256.f);
+          lsum += __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+          const int k = 16 * tau + e;
+          pw[k / 4] |= b << (8 * (k % 4));
+        }
+    }
+    lsum = lane_rowsum(lsum);
+    if (live) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run = l_run * alpha + lsum * (1.f / 256.f);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+      m_run = m_new;
+    }
+    const v8i_t pop = *reinterpret_cast<const v8i_t*>(pw);
+    // O^T += V^T P^T: A lane (dim 32 dt + lane%32, hf) gathers the same 32
+    // tokens, in the same order, as the lane's P bytes
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      uint32_t vw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const int dim = 32 * dt + row;
+#pragma unroll
+      for (int k = 0; k < 16 * NT; ++k) {
+        const int tau = k / 16, e = k % 16;
+        const int t = 32 * tau + 8 * (e / 4) + 4 * hf + (e % 4);
+        vw[k / 4] |= (uint32_t)vs[t * kUVStride + dim] << (8 * (k % 4));
+      }
+      const v8i_t vop = *reinterpret_cast<const v8i_t*>(vw);
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[dt], 0, 0, 0, 0, 0,
+                                                                0);
+    }
+  }
+
+  // ---- merge the waves: 2,3 -> 0,1 then 1 -> 0 (V staging area reused) -----
+  float* red = reinterpret_cast<float*>(&vstage[0][0]);   // [2][32 rows][130]
+  constexpr int RS = kUD + 2;
+  __syncthreads();
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const int lo_w = step == 0 ? 2 : 1;       // waves >= lo_w publish
+    if (wave >= lo_w && wave < 2 * lo_w) {
+      float* dst = red + (size_t)(wave - lo_w) * kURows * RS + row * RS;
+      if (hf == 0) {
+        dst[0] = m_run;
+        dst[1] = l_run;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dst[2 + 32 * dt + 8 * (e / 4) + 4 * hf + (e % 4)] = acc[dt][e];
+    }
+    __syncthreads();
+    if (wave < lo_w) {
+      const float* src = red + (size_t)wave * kURows * RS + row * RS;
+      const float m2 = src[0], l2 = src[1];
+      const float mm = fmaxf(m_run, m2);
+      if (mm != -INFINITY) {
+        const float a1 = fast_exp2(m_run - mm), a2 = fast_exp2(m2 - mm);
+        l_run = l_run * a1 + l2 * a2;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[dt][e] = acc[dt][e] * a1 + src[2 + 32 * dt + 8 * (e / 4) + 4 * hf + (e % 4)] * a2;
+        m_run = mm;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- outputs at the queries' own rows ----------------------------------------
+  if (wave == 0 && row_ok) {
+    const size_t orow = (size_t)(gr.q0 + qi) * a.H_q + h * G + hq;
+    const float oscale = l_run > 0.f ? a.v_scale[h] / (256.f * l_run) : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        store_rn<kBF16>(a.out, orow * kUD + 32 * dt + 8 * (e / 4) + 4 * hf + (e % 4),
+                        acc[dt][e] * oscale);
+    if (hf == 0 && a.lse)
+      a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+// Standalone union preparation: lists, counts and membership per (group, head).
+__global__ __launch_bounds__(kUThreads) void union_prep_kernel(UnionArgs a) {
+  __shared__ UnionShared sh;
+  const int H = a.H_kv;
+  const int h = blockIdx.x % H;
+  const int gi = blockIdx.x / H;
+  const GroupInfo gr = find_group(a.q_indptr, a.B, a.group, gi);
+  const int cap = a.group * a.kq;
+  int32_t* ul = a.union_out + ((size_t)gi * H + h) * cap;
+  unsigned char* um = a.member_out + ((size_t)gi * H + h) * cap;
+  int U = 0;
+  if (gr.nq > 0) {
+    const int L = a.seq_lens[gr.r];
+    const int pbeg = a.page_indptr[gr.r];
+    const int P_r = a.page_indptr[gr.r + 1] - pbeg;
+    const int n_pages = L > 0 ? min(min((L + a.S - 1) / a.S, P_r), kUMaxWords * 32) : 0;
+    U = build_union(sh, a, gr, h, n_pages, pbeg);
+  }
+  for (int i = threadIdx.x; i < cap; i += kUThreads) {
+    ul[i] = i < U ? sh.ulist[i] : -1;
+    um[i] = i < U ? sh.umask[i] : 0;
+  }
+  if (threadIdx.x == 0) a.count_out[(size_t)gi * H + h] = U;
+}
+
+}  // namespace
+
+bool union_supported(int kv_dtype, int q_dtype, int d, int S, int g, int group, int kq) {
+  return kv_dtype == kE4M3 && q_dtype == kBF16 && d == kUD && (S == 32 || S == 64) &&
+         (g == 1 || g == 2 || g == 4 || g == 8) && group >= 1 && group * g <= kURows &&
+         group <= kUMaxGroup && group * kq <= kUMaxUnion && kq >= 1;
+}
+
+int union_max_pages() { return kUMaxWords * 32; }
+
+hipError_t launch_union_attn(const UnionArgs& a, hipStream_t s) {
+  dim3 grid(a.max_groups * a.H_kv);
+#define QAS_UNION_CASE(GG, NT)                                                        \
+  if (a.g == GG && a.S == 32 * NT) {                                                  \
+    hipLaunchKernelGGL((union_attn_kernel<GG, NT>), grid, dim3(kUThreads), 0, s, a); \
+    return hipGetLastError();                                                         \
+  }
+  QAS_UNION_CASE(1, 1) QAS_UNION_CASE(1, 2) QAS_UNION_CASE(2, 1) QAS_UNION_CASE(2, 2)
+  QAS_UNION_CASE(4, 1) QAS_UNION_CASE(4, 2) QAS_UNION_CASE(8, 1) QAS_UNION_CASE(8, 2)
+#undef QAS_UNION_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_union_prep(const UnionArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(union_prep_kernel, dim3(a.max_groups * a.H_kv), dim3(kUThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace qas

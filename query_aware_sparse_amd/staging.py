@@ -97,3 +97,44 @@ def prefill(pc, case, lengths=None, device="cuda"):
         del k, v
     torch.cuda.synchronize()
     return full
+
+
+class ChunkBatch:
+    """Device state of one or more multi-query chunks (one per request) sharing
+    an fp8 pool: pages of request r are placed after those of r - 1.  K/V
+    tokens go to their pages by plain copies (this path reads no summaries)."""
+
+    def __init__(self, cases, device="cuda"):
+        c0 = cases[0]
+        H, S, d = c0.H_kv, c0.S, c0.d
+        pool = sum(c.num_pool_pages for c in cases)
+        shape = (pool, H, S, d)
+        self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)   # e4m3 NaN
+        self.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
+        lengths, pages, off = [], [], 0
+        for c in cases:
+            P = ceil_div(c.L, S)
+            phys = torch.from_numpy(np.asarray(c.pages[:P], np.int64) + off).to(device)
+            for pool_t, raw in ((self.k_pool, c.keys), (self.v_pool, c.values)):
+                t = np.zeros((P * S, H, d), np.uint8)
+                t[:c.L] = raw[:c.L]
+                tt = torch.from_numpy(t).to(device).view(P, S, H, d).permute(0, 2, 1, 3)
+                pool_t[phys] = tt.contiguous()
+            lengths.append(c.L)
+            pages.append(np.asarray(c.pages[:P], np.int32) + off)
+            off += c.num_pool_pages
+        self.k_scale = torch.from_numpy(np.asarray(c0.k_scale, np.float32)).to(device)
+        self.v_scale = torch.from_numpy(np.asarray(c0.v_scale, np.float32)).to(device)
+        self.cache = make_cache(self.k_pool.view(torch.float8_e4m3fn),
+                                self.v_pool.view(torch.float8_e4m3fn), None,
+                                self.k_scale, self.v_scale)
+        self.db = DeviceBatch(lengths, pages, S, device)
+        q_indptr = np.zeros(len(cases) + 1, np.int32)
+        q_indptr[1:] = np.cumsum([c.N for c in cases])
+        self.q_indptr = torch.from_numpy(q_indptr).to(device)
+        self.q = to_device(np.concatenate([c.q for c in cases]), "bf16", device)
+        self.q_pos = torch.from_numpy(np.concatenate([c.q_pos for c in cases])).to(device)
+        self.sets = torch.from_numpy(np.ascontiguousarray(
+            np.concatenate([c.sets for c in cases]), np.int32)).to(device)
+        self.N = int(q_indptr[-1])
+        self.group = c0.group

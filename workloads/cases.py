@@ -323,7 +323,7 @@ def corrupt_lists(lists, num_pages, seed=5, n_slots=8):
 
 
 def multiquery_chunk(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
-            keep=45, group=8):
+            keep=45, group=8, scales=None):
     """Multi-query sparse chunk: one request of L tokens, S=64, N query
     positions c_i = L - N + i (L_i = L), each with its own kq-page set per KV
     head that always holds the query's own page floor(c_i/S).  S_0 = own page
@@ -331,11 +331,16 @@ def multiquery_chunk(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
     of S_{i-1} (own page excluded) + fresh pages <= own page not in S_{i-1},
     filled to kq, so neighbours share ~70% of their pages.  K/V N(0,1)
     quantised to fp8 e4m3 with a per-KV-head scale amax/448; q bf16 N(0,1).
-    Entries of each set are stored in seeded random order."""
+    Entries of each set are stored in seeded random order.  `scales`
+    ((k_scale, v_scale)) quantises with given per-head scales instead (so
+    several requests can share one fp8 cache)."""
     keys = _tokens(seed, _KEYS, 0, L, H_kv, d, "f32")
     values = _tokens(seed, _VALUES, 0, L, H_kv, d, "f32")
-    k_scale = (np.abs(keys).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
-    v_scale = (np.abs(values).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
+    if scales is None:
+        k_scale = (np.abs(keys).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
+        v_scale = (np.abs(values).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
+    else:
+        k_scale, v_scale = (np.asarray(x, np.float32) for x in scales)
     k_codes = cast(keys / k_scale[None, :, None], "e4m3")
     v_codes = cast(values / v_scale[None, :, None], "e4m3")
     del keys, values
