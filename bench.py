@@ -16,6 +16,11 @@ The value is the achieved rate on the bytes the method must move per call
 divided by the measured time per call.
 
     python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline]
+
+`--workload chunk` measures the multi-query chunk path instead (64K
+context, S=64, 512 queries with 64-page sets, 32/8 heads, fp8 K/V, groups
+of 8 queries over page unions on fp8 MFMA): one line with µs per chunk call
+and executed / useful MFMA TFLOP/s against the fp8 dense peak.
 """
 import argparse
 import json
@@ -33,6 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = ("µs per decode-layer call + achieved HBM GB/s, 32K ctx, K=256 pages, "
           "32×128 heads")
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+CHUNK_METRIC = "µs per multi-query chunk call + fp8 MFMA TFLOP/s, 64K ctx, 512 queries, union-8"
 
 
 def log(*a):
@@ -79,6 +86,121 @@ def cpu_baseline(case, seconds):
             "cpu": platform.processor() or platform.machine()}
 
 
+def chunk_accounting(case):
+    """Executed MFMA flops (every union page of every (group, KV head) tile:
+    QK and PV of 32 rows x S tokens x d), useful flops (each query head over
+    its own support), and K/V bytes (union-logical and distinct)."""
+    import numpy as np
+    P = -(-case.L // case.S)
+    N, H, _ = case.sets.shape
+    rows = 32
+    executed = useful = 0
+    union_pages = 0
+    distinct = set()
+    for h in range(H):
+        for g0 in range(0, N, case.group):
+            union = set()
+            for n in range(g0, min(N, g0 + case.group)):
+                s = {int(p) for p in case.sets[n, h] if 0 <= p < P}
+                union |= s
+                toks = sum(min(case.S, min(case.L, int(case.q_pos[n]) + 1) - p * case.S)
+                           for p in s if p * case.S <= case.q_pos[n])
+                useful += case.g * toks * case.d * 2 * 2
+            union_pages += len(union)
+            distinct |= {(h, p) for p in union}
+    executed = union_pages * rows * case.S * case.d * 2 * 2
+    page_bytes = 2 * case.S * case.d            # fp8 K + V of one page of one head
+    return {"executed_flops": executed, "useful_flops": useful,
+            "union_kv_bytes": union_pages * page_bytes,
+            "distinct_kv_bytes": len(distinct) * page_bytes,
+            "mean_union_pages": union_pages / (H * (-(-N // case.group)))}
+
+
+def bench_chunk(args):
+    import torch
+
+    import query_aware_sparse_amd as qas
+    from query_aware_sparse_amd.staging import ChunkBatch
+    from workloads import multiquery_chunk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    NL = max(1, args.layers)
+    case = multiquery_chunk()
+    log(f"[bench] workload {case.name}: L={case.L} S={case.S} N={case.N} "
+        f"kq={case.kq} heads={case.H_q}/{case.H_kv} copies={NL}")
+    acct = chunk_accounting(case)
+    base = ChunkBatch([case])
+    copies = [base]
+    for _ in range(1, NL):
+        c = ChunkBatch.__new__(ChunkBatch)
+        c.__dict__.update(base.__dict__)
+        c.k_pool = base.k_pool.clone()
+        c.v_pool = base.v_pool.clone()
+        c.cache = qas.make_cache(c.k_pool.view(torch.float8_e4m3fn),
+                                 c.v_pool.view(torch.float8_e4m3fn), None, base.k_scale,
+                                 base.v_scale)
+        copies.append(c)
+    out = torch.empty((NL, case.N, case.H_q, case.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((NL, case.N, case.H_q), device="cuda")
+    scale = 1.0 / math.sqrt(case.d)
+
+    def call(i):
+        c = copies[i]
+        qas.qas_chunk_attention(c.cache, c.db.batch, c.q_indptr, c.q_pos, c.q, c.sets,
+                                c.group, scale, out[i], lse[i])
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for w in range(max(NL, args.warmup)):
+            call(w % NL)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(NL):
+            call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(args.steps / NL))
+    steps = reps * NL
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    rs = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(rs)
+        graph.replay()
+        e1.record(rs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / steps
+    call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL
+    exe = acct["executed_flops"] / (call_us * 1e-6) / 1e12
+    use = acct["useful_flops"] / (call_us * 1e-6) / 1e12
+    log(f"[bench] {steps} chunk calls: {ms * 1e3:.2f} us/call, executed {exe:.1f} TFLOP/s, "
+        f"useful {use:.1f} TFLOP/s, mean union {acct['mean_union_pages']:.1f} pages")
+    result = {
+        "metric": CHUNK_METRIC, "value": round(call_us, 3), "unit": "us/call", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 (fp8 MFMA), bf16 q/out, fp32 softmax", "data": "synthetic",
+        "config": {"workload": "multi-query chunk, 64K context", "context": case.L,
+                   "page_size": case.S, "queries": case.N, "pages_per_set": case.kq,
+                   "q_heads": case.H_q, "kv_heads": case.H_kv, "head_dim": case.d,
+                   "group": case.group, "cache_copies": NL, "hip_graph": True, **acct},
+        "roofline": {"bound": "mfma", "achieved": round(exe, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(exe / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "union_attn_kernel",
+                     "us_per_launch": round(call_us, 3),
+                     "useful_tflops": round(use, 2)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -88,11 +210,16 @@ def main():
     ap.add_argument("--layers", type=int, default=32, help="layer caches visited in turn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", choices=("decode", "chunk"), default="decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures the "
               "single-GPU path only (one GPU per box); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "chunk":
+        if args.layers == 32:
+            args.layers = 4
+        return bench_chunk(args)
 
     import torch
 

@@ -143,7 +143,7 @@ qas_status qas_score_pages(const qas_cache* cache, const qas_batch* batch,
  *   scores     device float, layout of qas_score_pages
  *   sel        device [B][H_kv][k] int32
  *   sel_count  device [B][H_kv] int32, may be NULL
- *   Rows longer than 16000 pages return QAS_ERR_UNSUPPORTED.
+ *   Rows longer than 16384 pages return QAS_ERR_UNSUPPORTED.
  */
 qas_status qas_topk_pages(const float* scores, const qas_batch* batch,
                           int32_t num_kv_heads, int32_t page_size, int32_t k,

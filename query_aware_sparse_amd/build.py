@@ -28,7 +28,8 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-SOURCES = ["qas_api.cpp", "append.hip", "score.hip", "topk.hip", "decode.hip", "union.hip"]
+SOURCES = ["qas_api.cpp", "append.hip", "score.hip", "topk.hip", "decode.hip", "decode_f32.hip",
+           "decode_f16.hip", "decode_bf16.hip", "union.hip"]
 
 
 def _compile(src, verbose):

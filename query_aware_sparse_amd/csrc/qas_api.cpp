@@ -74,11 +74,13 @@ qas_status check_heads(const qas_cache* c, int num_q_heads, int* g) {
 }
 
 // Workspace layout:
-//   sparse decode: [split partials]
-//   decode layer:  [scores][sel][sel_phys][split partials]
+//   sparse decode: [split partials][tickets]
+//   decode layer:  [scores][split partials][tickets], plus [sel][sel_phys]
+//                  for rows too long for the in-kernel top-K
 struct DecodePlan {
   int n_split;
   size_t partial_bytes;
+  size_t ticket_bytes;
 };
 
 DecodePlan plan_decode(const qas_cache* c, const qas_batch* b, int num_q_heads, int sel_len) {
@@ -86,14 +88,24 @@ DecodePlan plan_decode(const qas_cache* c, const qas_batch* b, int num_q_heads, 
   p.n_split = qas::decode_num_splits(b->batch * c->num_kv_heads, sel_len);
   p.partial_bytes = align256((size_t)b->batch * num_q_heads * p.n_split *
                              (c->head_dim + 2) * sizeof(float));
+  p.ticket_bytes = align256((size_t)b->batch * c->num_kv_heads * sizeof(unsigned int));
   return p;
 }
 
+// Scores of the decode layer: [B][H_kv][max_pages] when the attention kernel
+// selects in-kernel (fixed row stride), else the packed qas_score_pages layout.
+bool layer_fused_topk(const qas_batch* b);
 size_t layer_scores_bytes(const qas_cache* c, const qas_batch* b) {
-  return align256((size_t)b->total_pages * c->num_kv_heads * sizeof(float));
+  const size_t n = layer_fused_topk(b) ? (size_t)b->batch * b->max_pages : (size_t)b->total_pages;
+  return align256(n * c->num_kv_heads * sizeof(float));
+}
+
+bool layer_fused_topk(const qas_batch* b) {
+  return b->max_pages <= qas::decode_fused_topk_max_pages();
 }
 
 size_t layer_sel_bytes(const qas_cache* c, const qas_batch* b, int k) {
+  if (layer_fused_topk(b)) return 0;
   return align256((size_t)b->batch * c->num_kv_heads * k * sizeof(int32_t));
 }
 
@@ -119,6 +131,8 @@ qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q,
   a.kv_dtype = c->kv_dtype;
   a.g = g;
   a.pages_per_iter = qas::score_pages_per_iter(c->kv_dtype, c->head_dim, c->num_kv_heads);
+  a.tickets = nullptr;
+  a.row_stride = 0;
   return a;
 }
 
@@ -150,6 +164,11 @@ qas::DecodeArgs decode_args(const qas_cache* c, const qas_batch* b, const void* 
   a.n_split = n_split;
   a.dedupe = dedupe;
   a.sm_scale = sm_scale;
+  a.tickets = nullptr;
+  a.scores = nullptr;
+  a.sel_out = nullptr;
+  a.max_pages = b->max_pages;
+  a.clear_tickets = 0;
   return a;
 }
 
@@ -176,10 +195,6 @@ qas::AppendArgs append_args(const qas_cache* c, const qas_batch* b, const int32_
 
 }  // namespace
 
-namespace qas {
-int decode_max_dedupe_row();
-}
-
 extern "C" {
 
 const char* qas_version(void) { return "qas 0.1.0 (gfx950)"; }
@@ -205,10 +220,10 @@ size_t qas_workspace_bytes(int32_t op, const qas_cache* cache, const qas_batch* 
       k < 1)
     return 0;
   const DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
-  if (op == QAS_OP_SPARSE_DECODE) return p.partial_bytes;
+  if (op == QAS_OP_SPARSE_DECODE) return p.partial_bytes + p.ticket_bytes;
   if (op == QAS_OP_DECODE_LAYER)
-    return layer_scores_bytes(cache, batch) + 2 * layer_sel_bytes(cache, batch, k) +
-           p.partial_bytes;
+    return layer_scores_bytes(cache, batch) + p.partial_bytes + p.ticket_bytes +
+           2 * layer_sel_bytes(cache, batch, k);
   return 0;
 }
 
@@ -299,11 +314,13 @@ qas_status qas_sparse_decode(const qas_cache* cache, const qas_batch* batch, con
   if (sel_len > qas::decode_max_dedupe_row())
     return fail(QAS_ERR_UNSUPPORTED, "sel_len %d > %d", sel_len, qas::decode_max_dedupe_row());
   DecodePlan p = plan_decode(cache, batch, num_q_heads, sel_len);
-  if (!workspace || workspace_bytes < p.partial_bytes)
-    return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes,
-                p.partial_bytes);
+  const size_t need = p.partial_bytes + p.ticket_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   qas::DecodeArgs a = decode_args(cache, batch, q, num_q_heads, g, sel, sel_stride, sel_len,
                                   sm_scale, out, lse, (float*)workspace, p.n_split, 1);
+  a.tickets = (unsigned int*)((char*)workspace + p.partial_bytes);
+  a.clear_tickets = 1;
   hipError_t e = qas::launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -338,37 +355,50 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   char* ws = (char*)workspace;
   float* scores = (float*)ws;
   ws += layer_scores_bytes(cache, batch);
-  int32_t* sel = sel_out ? sel_out : (int32_t*)ws;
-  ws += layer_sel_bytes(cache, batch, k);
-  int32_t* sel_phys = (int32_t*)ws;
-  ws += layer_sel_bytes(cache, batch, k);
   float* partials = (float*)ws;
+  ws += p.partial_bytes;
+  unsigned int* tickets = (unsigned int*)ws;
+  ws += p.ticket_bytes;
 
-  // 1. page bounds (with the current token's append folded in)
+  // 1. page bounds (with the current token's append folded in); clears the
+  //    attention kernel's tickets
   hipError_t e;
   qas::ScoreArgs sa = score_args(cache, batch, q, num_q_heads, g, scores);
   sa.k_new = k_new;
   sa.v_new = v_new;
+  sa.tickets = tickets;
+  sa.row_stride = layer_fused_topk(batch) ? batch->max_pages : 0;
   if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
-  // 2. top-k per (request, KV head), logical and physical page lists
-  qas::TopkArgs ta;
-  ta.scores = scores;
-  ta.seq_lens = batch->seq_lens;
-  ta.page_indptr = batch->page_indptr;
-  ta.page_indices = batch->page_indices;
-  ta.sel = sel;
-  ta.sel_phys = qas::topk_phys_fits(batch->max_pages) ? sel_phys : nullptr;
-  ta.sel_count = nullptr;
-  ta.B = batch->batch;
-  ta.H_kv = cache->num_kv_heads;
-  ta.S = cache->page_size;
-  ta.k = k;
-  ta.max_pages = batch->max_pages;
-  if ((e = qas::launch_topk(ta, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+  qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, nullptr, k, k, sm_scale, out,
+                                   lse, partials, p.n_split, 0);
+  da.tickets = tickets;
+  if (layer_fused_topk(batch)) {
+    // 2. top-k per (request, KV head) inside the attention kernel
+    da.scores = scores;
+    da.sel_out = sel_out;
+  } else {
+    // 2. top-k per (request, KV head) in a kernel of its own (long rows)
+    int32_t* sel = sel_out ? sel_out : (int32_t*)ws;
+    ws += layer_sel_bytes(cache, batch, k);
+    int32_t* sel_phys = (int32_t*)ws;
+    qas::TopkArgs ta;
+    ta.scores = scores;
+    ta.seq_lens = batch->seq_lens;
+    ta.page_indptr = batch->page_indptr;
+    ta.page_indices = batch->page_indices;
+    ta.sel = sel;
+    ta.sel_phys = sel_phys;
+    ta.sel_count = nullptr;
+    ta.B = batch->batch;
+    ta.H_kv = cache->num_kv_heads;
+    ta.S = cache->page_size;
+    ta.k = k;
+    ta.max_pages = batch->max_pages;
+    if ((e = qas::launch_topk(ta, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+    da.sel = sel;
+    da.sel_phys = sel_phys;
+  }
   // 3. sparse attention with the split merge
-  qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, sel, k, k, sm_scale, out, lse,
-                                   partials, p.n_split, 0);
-  da.sel_phys = ta.sel_phys;
   if ((e = qas::launch_decode(da, s)) != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }

@@ -14,7 +14,8 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   const int32_t* page_indptr;
   const int32_t* page_indices;
-  float* scores;
+  float* scores;             // row_stride 0: [pbeg*H_kv + h*P_r + j], else [(r*H_kv + h)*row_stride + j]
+  int row_stride;
   // optional decode append of the token at seq_lens[r] - 1 (k_new != NULL)
   const void* k_new;         // [B][H_kv][d]
   const void* v_new;
@@ -23,6 +24,7 @@ struct ScoreArgs {
   int B, H_kv, H_q, d, S, max_pages;
   int kv_dtype, g;
   int pages_per_iter;        // pages one workgroup covers per lane step
+  unsigned int* tickets;     // optional [B][H_kv] counters zeroed for the attention kernel
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 bool score_supported(int kv_dtype, int d, int g, int H_kv);
@@ -37,11 +39,10 @@ struct TopkArgs {
   int32_t* sel_phys;         // optional physical pages of `sel`
   int32_t* sel_count;
   int B, H_kv, S, k;
-  int max_pages;             // longest row (sizes the LDS key array)
+  int max_pages;             // longest row (sizes the per-thread register run)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-constexpr int kTopkMaxPages = 16000;  // keys + histogram within 64 KiB of LDS
-bool topk_phys_fits(int max_pages);    // physical lists also fit in LDS
+constexpr int kTopkMaxPages = 16384;  // 256 threads x 64 scores held in registers
 
 struct AppendArgs {
   void* k_pool;
@@ -71,14 +72,23 @@ struct DecodeArgs {
   void* out;
   float* lse;
   float* partials;           // [B][H_q][n_split][2 + d]
+  unsigned int* tickets;     // [B][H_kv] split arrival counters, zero on entry
+  // in-kernel top-K (scores != NULL): select sel_len pages per (request, KV
+  // head) from scores laid out [B][H_kv][max_pages]; sel / sel_phys unused
+  const float* scores;
+  int32_t* sel_out;          // optional [B][H_kv][sel_len] copy of the selection
+  int max_pages;
   int B, H_kv, H_q, d, S, kv_dtype, g;
   int sel_stride, sel_len, n_split;
   int dedupe;                // 0: lists known unique and valid-or-negative
+  int clear_tickets;         // zero the tickets in a kernel of their own first
   float sm_scale;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 bool decode_supported(int kv_dtype, int d, int g);
 int decode_num_splits(int rows, int sel_len);
+int decode_max_dedupe_row();
+int decode_fused_topk_max_pages();   // longest row the in-kernel top-K takes
 
 struct UnionArgs {
   const void* k_pool;        // fp8 [pool][H_kv][S][d]

@@ -16,6 +16,8 @@
 // min/max (starting from +-inf when the token opens the page), then score
 // the updated record.  No other workgroup reads that record, and the
 // attention stage runs in a later kernel, so no synchronisation is needed.
+// The first workgroup of each request also zeroes the attention kernel's
+// split counters of that request.
 #include "qas_device.h"
 #include "qas_internal.h"
 
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(1024) void score_kernel(ScoreArgs a) {
     knew = load16(reinterpret_cast<const char*>(a.k_new) + o);
     vnew = load16(reinterpret_cast<const char*>(a.v_new) + o);
   }
+  if (a.tickets && blockIdx.x == 0)
+    for (int i = tid; i < H; i += blockDim.x) a.tickets[(size_t)r * H + i] = 0u;
   if (j0 >= P_r) return;
   const int n_used = L > 0 ? min((L + a.S - 1) / a.S, P_r) : 0;
   const int tail = n_used - 1;
@@ -124,7 +128,9 @@ __global__ __launch_bounds__(1024) void score_kernel(ScoreArgs a) {
     }
   }
 
-  float* srow = a.scores + (size_t)pbeg * H + (size_t)h * P_r;
+  float* srow = a.row_stride ? a.scores + ((size_t)r * H + h) * a.row_stride
+                             : a.scores + (size_t)pbeg * H + (size_t)h * P_r;
+  const int lim = a.row_stride ? min(P_r, a.row_stride) : P_r;   // stay inside the row
 #pragma unroll
   for (int u = 0; u < kScoreUnroll; ++u) {
     float m[EPL], M[EPL];
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(1024) void score_kernel(ScoreArgs a) {
       s = group_sum<RL>(s);                       // eq. (3)
       best = fmaxf(best, s);                      // group max
     }
-    if (c == 0 && j[u] < P_r) srow[j[u]] = j[u] < n_used ? best : -INFINITY;
+    if (c == 0 && j[u] < lim) srow[j[u]] = j[u] < n_used ? best : -INFINITY;
   }
 }
 

@@ -1,0 +1,378 @@
+// Workgroup-level top-K page selection for one (request, KV head) row: the
+// Quest page's second stage ("3.1.1 · Quest", §1 and Fig. 1), ordered by
+// (score descending, page index ascending) so ties go to the lower index.
+// Used by the standalone top-K kernel and inside the attention kernel of the
+// decode layer.
+//
+// A workgroup of kTkThreads threads holds the row in registers: thread t
+// keeps the run of scores j in [t*PT, t*PT + PT) and their physical pages.
+// Every per-element step is branch-free (invalid elements go to a dummy
+// histogram bin or LDS slot), and block-uniform values are moved to scalar
+// registers, so one select costs a few thousand cycles.  Selection narrows a closed score interval [lo, hi] that holds the
+// K-th largest score:
+//   * histogram the candidates into kTkBins bins through a monotone map
+//     (lo in bin 0, hi in the top bin);
+//   * one wave walks the bins from the top to the one holding the K-th
+//     score; scores in higher bins are taken and that bin's scores are the
+//     candidates (if still too many, [lo, hi] shrinks to their exact
+//     min/max and the step repeats; the bin misses lo or hi, so each repeat
+//     drops at least one distinct value);
+//   * rank the candidates exactly by (score desc, index asc).  The last one
+//     taken is the threshold (T_s, T_j): page j is selected iff s_j > T_s,
+//     or s_j == T_s and j <= T_j.
+// An index-ordered compaction (one workgroup scan over the runs) gives every
+// selected page its position in the ascending output list.  -0.0 and +0.0
+// are equal scores; NaN ranks below every number.
+#pragma once
+
+#include <float.h>
+
+#include "qas_device.h"
+
+namespace qas {
+
+constexpr int kTkThreads = 256;
+constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kTkBins = 1024;
+constexpr int kTkCand = 512;         // candidates ranked from LDS
+constexpr float kTkMinRange = 1e-30f;
+
+struct TopkShared {
+  __align__(16) int hist[kTkBins + 4];   // + a dummy bin for skipped elements
+  int cidx[kTkCand + kTkThreads];        // + one dummy slot per thread
+  float cval[kTkCand + kTkThreads];
+  int scan[2][kTkWaves];
+  float mm[2 * kTkWaves];
+  int nslot, tj;
+  float ts;
+};
+
+namespace tk {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_shift(int v) {
+  // lanes without a source (or outside ROW_MASK) read 0
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr 1/2/4/8 scan each row of
+// 16 lanes, row_bcast 15/31 carry row totals into the following rows.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_shift<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_shift<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_shift<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_shift<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_shift<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_shift<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Exclusive prefix sum over the workgroup in thread order; one barrier.
+// `scratch` (kTkWaves ints) must not be rewritten before another barrier.
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+  const int incl = wave_incl_scan(v);
+  if (lane_id() == kWave - 1) scratch[wave_id()] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const int c = scratch[w];
+    before += w < wave_id() ? c : 0;
+    all += c;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_f<0xB1>(v));
+  v = fminf(v, dpp_f<0x4E>(v));
+  v = fminf(v, dpp_f<0x141>(v));
+  v = fminf(v, dpp_f<0x140>(v));
+  v = fminf(v, __shfl_xor(v, 16, kWave));
+  return fminf(v, __shfl_xor(v, 32, kWave));
+}
+
+// (min, max) over the workgroup; one barrier.
+__device__ __forceinline__ void block_minmax(float& lo, float& hi, float* scratch) {
+  lo = wave_min(lo);
+  hi = group_max<kWave>(hi);
+  if (lane_id() == 0) {
+    scratch[2 * wave_id()] = lo;
+    scratch[2 * wave_id() + 1] = hi;
+  }
+  __syncthreads();
+  lo = scratch[0];
+  hi = scratch[1];
+#pragma unroll
+  for (int w = 1; w < kTkWaves; ++w) {
+    lo = fminf(lo, scratch[2 * w]);
+    hi = fmaxf(hi, scratch[2 * w + 1]);
+  }
+}
+
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Monotone map of a score in [lo, hi] to one of kTkBins bins, with lo in bin
+// 0 and hi in a higher bin whenever lo < hi.  Normal ranges bin the float
+// value linearly; ranges too narrow (or too wide) for a finite fp32 scale
+// bin the order-preserving integer key, shifted so that the key range
+// spans fewer than kTkBins bins.  lo and hi must be block-uniform.
+struct Binner {
+  float lo, inv;
+  uint32_t klo;
+  int kshift;
+  bool by_key;
+  __device__ __forceinline__ void init(float l, float h) {
+    const float range = h - l;
+    by_key = uniform_i(!(range >= kTkMinRange && range <= FLT_MAX) ? 1 : 0) != 0;
+    lo = l;
+    inv = uniform_f(by_key ? 0.f : (float)kTkBins / range);
+    klo = order_key(l);
+    const uint32_t span = order_key(h) - klo;
+    int sh = 0;
+    while ((span >> sh) >= (uint32_t)kTkBins) ++sh;
+    kshift = uniform_i(sh);
+  }
+  // the two maps; callers branch once on the uniform by_key
+  __device__ __forceinline__ int by_value(float s) const {
+    const float t = fminf(fmaxf((s - lo) * inv, 0.f), (float)(kTkBins - 1));
+    return (int)t;
+  }
+  __device__ __forceinline__ int by_order_key(float s) const {
+    return (int)((order_key(s) - klo) >> kshift);
+  }
+};
+
+}  // namespace tk
+
+// One row held by the workgroup: PT scores per thread.
+template <int PT>
+struct TopkRow {
+  float v[PT];
+  int pv[PT];
+  int j0, n;
+  float Ts;
+  int Tj;
+
+  // Scores srow[j] for j < cap (the row's allocated extent; entries at or
+  // beyond the row length are loaded but never used).
+  __device__ __forceinline__ void load_scores(const float* srow, int cap) {
+    j0 = threadIdx.x * PT;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      const int j = j0 + k;
+      v[k] = j < cap ? srow[j] : 0.f;
+    }
+  }
+
+  // Row length n_ and, if pt != NULL, the physical pages pt[0, n_).
+  __device__ __forceinline__ void load_pages(const int32_t* pt, int n_) {
+    n = n_;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      const int j = j0 + k;
+      pv[k] = (j < n && pt) ? pt[j] : 0;
+    }
+  }
+
+  __device__ __forceinline__ void load(const float* srow, const int32_t* pt, int n_) {
+    load_scores(srow, n_);
+    load_pages(pt, n_);
+  }
+
+  __device__ __forceinline__ bool valid(int k) const { return j0 + k < n; }
+
+  __device__ __forceinline__ bool selected(int k) const {
+    return valid(k) & ((v[k] > Ts) | ((v[k] == Ts) & (j0 + k <= Tj)));
+  }
+
+  // Find (Ts, Tj) for the top `take` (<= n) entries; every thread of the
+  // workgroup must call this.
+  __device__ void select(int take, TopkShared& sh) {
+    using namespace tk;
+    const int tid = threadIdx.x;
+    float lo = FLT_MAX, hi = -FLT_MAX;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      // -0 ranks as +0 and NaN below every number
+      float x = v[k];
+      x = x == 0.f ? 0.f : x;
+      x = x != x ? -INFINITY : x;
+      v[k] = x;
+      const bool ok = valid(k);
+      lo = fminf(lo, ok ? x : FLT_MAX);
+      hi = fmaxf(hi, ok ? x : -FLT_MAX);
+    }
+    Ts = -INFINITY;
+    Tj = n;                                    // take == n: everything
+    if (take >= n) return;
+
+    for (int b = tid; b < kTkBins + 4; b += kTkThreads) sh.hist[b] = 0;
+    if (tid == 0) sh.nslot = 0;
+    block_minmax(lo, hi, sh.mm);
+    lo = uniform_f(lo);
+    hi = uniform_f(hi);
+    int kk = take;                             // still to take among candidates
+    int ncand = n;
+    Binner bin;
+    int cbin = -1;                             // bin of the candidates (last round)
+    int bk[PT];                                // element bins of the last round
+    int round = 0;
+    while (ncand > kTkCand && lo < hi) {
+      bin.init(lo, hi);
+      if (round > 0) {
+        for (int b = tid; b < kTkBins + 4; b += kTkThreads) sh.hist[b] = 0;
+        __syncthreads();
+      }
+      // skipped elements go to the dummy bin; out-of-range values may map
+      // anywhere, the select discards them
+      if (bin.by_key) {
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+          const int b = bin.by_order_key(v[k]);
+          bk[k] = (valid(k) & (v[k] >= lo) & (v[k] <= hi)) ? b : kTkBins;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+          const int b = bin.by_value(v[k]);
+          bk[k] = (valid(k) & (v[k] >= lo) & (v[k] <= hi)) ? b : kTkBins;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PT; ++k) atomicAdd(&sh.hist[bk[k]], 1);
+      __syncthreads();
+      {
+        // every wave walks the histogram itself, so no barrier publishes the
+        // result; lane l owns bins NB-1-16l ... NB-16-16l (lane order walks
+        // downward)
+        constexpr int PER = kTkBins / kWave;
+        const int lane = lane_id();
+        int c[PER], local = 0;
+        const int4* hv = reinterpret_cast<const int4*>(sh.hist + kTkBins - PER * (lane + 1));
+#pragma unroll
+        for (int q4 = 0; q4 < PER / 4; ++q4) {
+          const int4 x = hv[q4];
+          // bins ascend in memory; c[] walks them descending
+          c[PER - 1 - 4 * q4] = x.x;
+          c[PER - 2 - 4 * q4] = x.y;
+          c[PER - 3 - 4 * q4] = x.z;
+          c[PER - 4 - 4 * q4] = x.w;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) local += c[k];
+        const int incl = wave_incl_scan(local);
+        const int excl = incl - local;
+        int b_here = 0, above_here = 0, cnt_here = 0, run = excl;
+        bool found = false;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const bool hit = !found && run + c[k] >= kk;
+          b_here = hit ? kTkBins - 1 - (lane * PER + k) : b_here;
+          above_here = hit ? run : above_here;
+          cnt_here = hit ? c[k] : cnt_here;
+          found = found || hit;
+          run += c[k];
+        }
+        const uint64_t here = __ballot(excl < kk && incl >= kk);
+        const int src = uniform_i(__ffsll((unsigned long long)here) - 1);
+        cbin = __builtin_amdgcn_readlane(b_here, src);
+        kk -= __builtin_amdgcn_readlane(above_here, src);
+        ncand = __builtin_amdgcn_readlane(cnt_here, src);
+      }
+      ++round;
+      if (ncand <= kTkCand) break;
+      // too many left: shrink [lo, hi] to the crossing bin's exact extremes
+      // (it misses lo or hi, so every round drops at least one value)
+      float nlo = FLT_MAX, nhi = -FLT_MAX;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) {
+        const bool in = bk[k] == cbin;
+        nlo = fminf(nlo, in ? v[k] : FLT_MAX);
+        nhi = fmaxf(nhi, in ? v[k] : -FLT_MAX);
+      }
+      block_minmax(nlo, nhi, sh.mm);
+      lo = uniform_f(nlo);
+      hi = uniform_f(nhi);
+      cbin = -1;
+    }
+    // candidates: the crossing bin of the last round, else all of [lo, hi]
+    auto is_cand = [&](int k) {
+      return cbin >= 0 ? bk[k] == cbin : (valid(k) & (v[k] >= lo) & (v[k] <= hi));
+    };
+
+    if (lo == hi) {
+      // every candidate ties: the kk-th lowest index holding the value
+      int mine = 0;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) mine += (valid(k) & (v[k] == lo)) ? 1 : 0;
+      int total;
+      int seen = block_excl_scan(mine, sh.scan[0], &total);
+#pragma unroll
+      for (int k = 0; k < PT; ++k) {
+        const bool eq = valid(k) & (v[k] == lo);
+        seen += eq ? 1 : 0;
+        if (eq && seen == kk) sh.tj = j0 + k;
+      }
+      __syncthreads();
+      Ts = lo;
+      Tj = uniform_i(sh.tj);
+    } else {
+      // at most kTkCand (= ncand) candidates: gather them in any order (one
+      // LDS atomic per wave), rank each exactly by (score desc, index asc)
+      int mine = 0;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) mine += is_cand(k) ? 1 : 0;
+      const int incl = wave_incl_scan(mine);
+      int base = 0;
+      if (lane_id() == kWave - 1) base = atomicAdd(&sh.nslot, incl);
+      int at = __builtin_amdgcn_readlane(base, kWave - 1) + incl - mine;
+      const int dummy = kTkCand + tid;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) {
+        const bool c = is_cand(k);
+        const int slot = c ? at : dummy;
+        sh.cidx[slot] = j0 + k;
+        sh.cval[slot] = v[k];
+        at += c ? 1 : 0;
+      }
+      __syncthreads();
+      const int total = ncand;
+      for (int i = tid; i < total; i += kTkThreads) {
+        const float si = sh.cval[i];
+        const int ji = sh.cidx[i];
+        int rank = 0;
+        for (int t = 0; t < total; ++t) {
+          const float st = sh.cval[t];
+          rank += ((st > si) | ((st == si) & (sh.cidx[t] < ji))) ? 1 : 0;
+        }
+        if (rank == kk - 1) {
+          sh.ts = si;
+          sh.tj = ji;
+        }
+      }
+      __syncthreads();
+      Ts = uniform_f(sh.ts);
+      Tj = uniform_i(sh.tj);
+    }
+  }
+
+  // Output position of this thread's first selected page (selected pages
+  // are numbered in ascending page order); every thread must call this.
+  __device__ __forceinline__ int first_position(TopkShared& sh) const {
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) mine += selected(k) ? 1 : 0;
+    int total;
+    return tk::block_excl_scan(mine, sh.scan[1], &total);
+  }
+};
+
+}  // namespace qas

@@ -81,26 +81,56 @@ def _topk_rows(rng, B, H, maxP):
     return lens
 
 
+def _topk_scores(kind, total, rng):
+    """Seeded score rows that exercise every branch of a histogram select."""
+    if kind == "ints":
+        return rng.integers(-20, 20, size=total).astype(np.float32)       # heavy ties
+    if kind == "normal":
+        return rng.standard_normal(total).astype(np.float32)
+    if kind == "zeros":                                                    # -0 == +0
+        return np.where(rng.random(total) < 0.5, np.float32(0.0), np.float32(-0.0))
+    if kind == "cluster":
+        # most values within a few ulps of 1000, the rest spread wide: the
+        # crossing bin is narrowed several times
+        ulp = np.spacing(np.float32(1000))
+        c = np.float32(1000) + rng.integers(0, 40, size=total).astype(np.float32) * ulp
+        wide = (rng.standard_normal(total) * 5000).astype(np.float32)
+        return np.where(rng.random(total) < 0.85, c, wide).astype(np.float32)
+    if kind == "huge":
+        # a range beyond fp32 (and -inf entries): binning by order keys
+        x = (rng.standard_normal(total) * 1e38).astype(np.float32)
+        pick = rng.random(total)
+        x[pick < 0.05] = -np.inf
+        x[(pick >= 0.05) & (pick < 0.1)] = np.float32(3.4e38)
+        x[(pick >= 0.1) & (pick < 0.15)] = np.float32(-3.4e38)
+        return x
+    if kind == "subnormal":
+        # a range far below any fp32 scale: binning by order keys
+        return (rng.integers(0, 3000, size=total) * np.float32(1e-45)).astype(np.float32)
+    raise ValueError(kind)
+
+
+TOPK_KINDS = ["ints", "normal", "zeros", "cluster", "huge", "subnormal"]
+TOPK_ROWS = {"short": [1, 300, 2048, 1000, 77], "long": [4097, 16384, 9000]}
+
+
+@pytest.mark.parametrize("rows", list(TOPK_ROWS))
 @pytest.mark.parametrize("K", [1, 4, 64, 256, 4096])
-def test_topk_exact_on_identical_scores(qas, K):
-    """The oracle's top-K on the very fp32 scores the kernel reads: exact."""
+def test_topk_exact_on_identical_scores(qas, K, rows):
+    """The oracle's top-K on the very fp32 scores the kernel reads: exact,
+    up to the longest row the kernel takes (16384 pages)."""
     from query_aware_sparse_amd.staging import DeviceBatch
-    rng = np.random.default_rng(100 + K)
-    B, H, S = 5, 3, 16
-    P = [1, 300, 2048, 4097, 1000]
+    rng = np.random.default_rng(100 + K + 7 * len(rows))
+    H, S = 3, 16
+    P = TOPK_ROWS[rows]
+    B = len(P)
     lens = [p * S - int(rng.integers(0, S)) for p in P]
     pages = [np.arange(p, dtype=np.int32) for p in P]
     db = DeviceBatch(lens, pages, S)
     total = db.total_pages * H
-    kinds = ["ints", "normal", "zeros"]
-    for kind in kinds:
-        if kind == "ints":
-            s = rng.integers(-20, 20, size=total).astype(np.float32)   # heavy ties
-        elif kind == "normal":
-            s = rng.standard_normal(total).astype(np.float32)
-        else:
-            s = np.where(rng.random(total) < 0.5, np.float32(0.0), np.float32(-0.0))
-        say(f"[topk] K={K} kind={kind}")
+    for kind in TOPK_KINDS:
+        s = _topk_scores(kind, total, rng)
+        say(f"[topk] K={K} rows={rows} kind={kind}")
         scores = torch.from_numpy(s).cuda()
         sel = torch.full((B, H, K), 12345, dtype=torch.int32, device="cuda")
         cnt = torch.zeros((B, H), dtype=torch.int32, device="cuda")
@@ -279,10 +309,9 @@ def test_empty_and_zero_length_requests(qas):
         assert_attn_close(got[r], res["out"], "bf16", f"r={r}")
 
 
-def test_long_rows_without_physical_lists(qas):
-    """Rows too long for top-K to also keep their page table in LDS (more than
-    8064 pages): attention then translates pages through the page table."""
-    case = tiny_single_head(L=33000, S=4, K=300)            # 8250 pages, fp32, d=16
+def test_longest_row(qas):
+    """A row of 16384 pages, the longest the decode layer takes."""
+    case = tiny_single_head(L=65536, S=4, K=300)            # 16384 pages, fp32, d=16
     pc, db = _stage(qas, case)
     q = _q(case)
     out = torch.empty_like(q)
