@@ -41,6 +41,57 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 CHUNK_METRIC = "µs per multi-query chunk call + fp8 MFMA TFLOP/s, 64K ctx, 512 queries, union-8"
 
+# HBM traffic of one decode-layer call from two rocprofv3 --pmc passes of this
+# bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the timed
+# dispatches), scaled by what the same counters read for a plain 1 GiB copy
+# (`bench.py --copy-calibration`): FETCH_SIZE read 524303 KiB and WRITE_SIZE
+# 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write x1.0.  Valid only
+# for the kernel sources they were taken on (sha256 of csrc/).
+PMC_TRAFFIC = {
+    "csrc_sha256": "5ebf4dbe3403c1f5dfa9875672d7444b088c95aa69b007f55939e34dea917d67",
+    "fetch_kib": {"score_kernel": 16560.9, "decode_kernel": 34176.1},
+    "write_kib": {"score_kernel": 544.1, "decode_kernel": 337.3},
+    "fetch_factor": 2.0,
+    "write_factor": 1.0,
+}
+
+
+def csrc_sha256():
+    import hashlib
+    d = os.path.join(ROOT, "query_aware_sparse_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_traffic_bytes():
+    """HBM bytes per decode-layer call from the recorded counters, or None if
+    the kernels changed since they were taken."""
+    t = PMC_TRAFFIC
+    if t["csrc_sha256"] is None or t["csrc_sha256"] != csrc_sha256():
+        return None
+    kib = (sum(t["fetch_kib"].values()) * t["fetch_factor"] +
+           sum(t["write_kib"].values()) * t["write_factor"])
+    return int(round(kib * 1024))
+
+
+def copy_calibration():
+    """A plain device copy of known size (1 GiB, four times) to scale the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -211,11 +262,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--workload", choices=("decode", "chunk"), default="decode")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures the "
               "single-GPU path only (one GPU per box); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        return copy_calibration()
     if args.workload == "chunk":
         if args.layers == 32:
             args.layers = 4
@@ -253,9 +308,8 @@ def main():
     v_new = to_device(case.values[0][L - 1:L], case.kv_dtype)
     out = torch.empty((NL, 1, case.H_q, case.d), dtype=torch.float16, device=dev)
     lse = torch.empty((NL, 1, case.H_q), dtype=torch.float32, device=dev)
-    ws_bytes = qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, base.cache, db.batch,
-                                       case.H_q, case.K)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, base.cache, db.batch, case.H_q, case.K,
+                            device=dev)
     torch.cuda.synchronize()
 
     def call(i):
@@ -322,7 +376,7 @@ def main():
                    "bytes_per_call": total, "bytes_parts": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": pmc_traffic_bytes(),
                      "kernel": "decode-layer call (score with fused append, top-k, attention with merge)",
                      "us_per_launch": round(call_us, 3)},
     }

@@ -157,6 +157,12 @@ def qas_workspace_bytes(op, cache, batch, num_q_heads, k):
                                        int(num_q_heads), int(k)))
 
 
+def make_workspace(op, cache, batch, num_q_heads, k, device="cuda"):
+    """A zero-filled device workspace of qas_workspace_bytes() for `op`."""
+    n = qas_workspace_bytes(op, cache, batch, num_q_heads, k)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+
 def qas_sparse_decode(cache, batch, q, sel, sel_len, sm_scale, out, lse, workspace,
                       stream=None):
     _check(_load().qas_sparse_decode(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
@@ -204,6 +210,6 @@ def version():
 
 
 __all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_sparse_decode",
-           "qas_decode_layer", "qas_workspace_bytes", "qas_chunk_groups", "qas_union_pages",
+           "qas_decode_layer", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

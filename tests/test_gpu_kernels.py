@@ -162,9 +162,7 @@ def test_append_decode_steps_and_boundaries(qas, L):
         v_new = np.stack([case.values[r][lengths[r] - 1] for r in range(case.B)])
         kn, vn = to_device(k_new, "bf16"), to_device(v_new, "bf16")
         out = torch.empty((case.B, case.H_q, case.d), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
-                                                 case.H_q, case.K), dtype=torch.uint8,
-                         device="cuda")
+        ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch, case.H_q, case.K)
         qas.qas_decode_layer(pc.cache, db.batch, _q(case, s), case.K, case.sm_scale, out,
                              None, ws, k_new=kn, v_new=vn)
     torch.cuda.synchronize()
@@ -213,8 +211,7 @@ def _sparse_decode(qas, case, pc, db, lists, step=-1):
     q = _q(case, step)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((B, case.H_q), float("nan"), device="cuda")
-    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_SPARSE_DECODE, pc.cache, db.batch,
-                                             case.H_q, kk), dtype=torch.uint8, device="cuda")
+    ws = qas.make_workspace(qas.QAS_OP_SPARSE_DECODE, pc.cache, db.batch, case.H_q, kk)
     qas.qas_sparse_decode(pc.cache, db.batch, q, sel, kk, case.sm_scale, out, lse, ws)
     torch.cuda.synchronize()
     return out_to_numpy(out), lse.cpu().numpy().astype(np.float64)
@@ -267,9 +264,7 @@ def test_dense_fallback_all_pages(qas):
     q = _q(case)
     out = torch.empty_like(q)
     lse = torch.empty((1, case.H_q), device="cuda")
-    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
-                                             case.H_q, case.K), dtype=torch.uint8,
-                     device="cuda")
+    ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch, case.H_q, case.K)
     sel = torch.empty((1, case.H_kv, case.K), dtype=torch.int32, device="cuda")
     qas.qas_decode_layer(pc.cache, db.batch, q, case.K, case.sm_scale, out, lse, ws,
                          sel_out=sel)
@@ -295,9 +290,7 @@ def test_empty_and_zero_length_requests(qas):
     out = torch.full_like(q, float("nan"))
     lse = torch.empty((case.B, case.H_q), device="cuda")
     sel = torch.empty((case.B, case.H_kv, case.K), dtype=torch.int32, device="cuda")
-    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
-                                             case.H_q, case.K), dtype=torch.uint8,
-                     device="cuda")
+    ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch, case.H_q, case.K)
     qas.qas_decode_layer(pc.cache, db.batch, q, case.K, case.sm_scale, out, lse, ws,
                          sel_out=sel)
     torch.cuda.synchronize()
@@ -317,9 +310,7 @@ def test_longest_row(qas):
     out = torch.empty_like(q)
     lse = torch.empty((1, 1), device="cuda")
     sel = torch.empty((1, 1, case.K), dtype=torch.int32, device="cuda")
-    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch,
-                                             case.H_q, case.K), dtype=torch.uint8,
-                     device="cuda")
+    ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, pc.cache, db.batch, case.H_q, case.K)
     qas.qas_decode_layer(pc.cache, db.batch, q, case.K, case.sm_scale, out, lse, ws,
                          sel_out=sel)
     torch.cuda.synchronize()

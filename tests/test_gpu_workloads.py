@@ -47,9 +47,7 @@ class Layer:
         out = torch.full_like(q, float("nan"))
         lse = torch.full((case.B, case.H_q), float("nan"), device="cuda")
         sel = torch.full((case.B, case.H_kv, case.K), -9, dtype=torch.int32, device="cuda")
-        ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_DECODE_LAYER, self.pc.cache,
-                                                 db.batch, case.H_q, case.K),
-                         dtype=torch.uint8, device="cuda")
+        ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, self.pc.cache, db.batch, case.H_q, case.K)
         qas.qas_decode_layer(self.pc.cache, db.batch, q, case.K, case.sm_scale, out, lse,
                              ws, k_new=kn, v_new=vn, sel_out=sel)
         torch.cuda.synchronize()
@@ -148,9 +146,7 @@ def test_llama2_7b_layer_attention_on_oracle_sets(qas):
     q = to_device(case.q[0], case.q_dtype)
     out = torch.empty_like(q)
     lse = torch.empty((1, case.H_q), device="cuda")
-    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_SPARSE_DECODE, lay.pc.cache,
-                                             lay.db.batch, case.H_q, case.K),
-                     dtype=torch.uint8, device="cuda")
+    ws = qas.make_workspace(qas.QAS_OP_SPARSE_DECODE, lay.pc.cache, lay.db.batch, case.H_q, case.K)
     qas.qas_sparse_decode(lay.pc.cache, lay.db.batch, q, sel, case.K, case.sm_scale, out,
                           lse, ws)
     torch.cuda.synchronize()
@@ -207,9 +203,7 @@ def test_stress_long_context(qas):
     q = to_device(case.q[0], case.q_dtype)
     o = torch.full_like(q, float("nan"))
     ls = torch.empty((case.B, case.H_q), device="cuda")
-    ws = torch.empty(qas.qas_workspace_bytes(qas.QAS_OP_SPARSE_DECODE, lay.pc.cache,
-                                             lay.db.batch, case.H_q, case.K),
-                     dtype=torch.uint8, device="cuda")
+    ws = qas.make_workspace(qas.QAS_OP_SPARSE_DECODE, lay.pc.cache, lay.db.batch, case.H_q, case.K)
     qas.qas_sparse_decode(lay.pc.cache, lay.db.batch, q,
                           torch.from_numpy(bad.astype(np.int32)).cuda(), case.K,
                           case.sm_scale, o, ls, ws)
