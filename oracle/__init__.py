@@ -40,10 +40,12 @@ def decoded_kv(case, r):
     return _decoded_kv(case, r)
 
 
-def run_decode(case, step=-1, page_ids=None, requests=None, decoded=None):
+def run_decode(case, step=-1, page_ids=None, requests=None, decoded=None, sink_tokens=0,
+               local_tokens=0):
     """Oracle of one decode call of a DecodeCase: the call before the first
     append (step=-1) or the call after step ``step``'s append.  ``page_ids``
-    ([B][H_kv][*]) replaces the top-K lists.  ``decoded`` optionally maps a
+    ([B][H_kv][*]) replaces the top-K lists; ``sink_tokens`` / ``local_tokens``
+    add the fixed sink and local pages to them.  ``decoded`` optionally maps a
     request to decoded_kv(case, r).  Returns one result dict per request (see
     quest.decode_request)."""
     lengths = case.lengths(step)
@@ -58,7 +60,8 @@ def run_decode(case, step=-1, page_ids=None, requests=None, decoded=None):
             keys, values = _decoded_kv(case, r, L)
         res = quest.decode_request(q_all[r], keys, values, L, case.S, case.K,
                                    scale=case.sm_scale,
-                                   page_ids=None if page_ids is None else page_ids[r])
+                                   page_ids=None if page_ids is None else page_ids[r],
+                                   sink_tokens=sink_tokens, local_tokens=local_tokens)
         res["L"] = L
         out.append(res)
     return out

@@ -124,6 +124,39 @@ def top_k_pages(scores, K):
     return sorted(order[:min(int(K), P)])
 
 
+# ------------------------------------------- fixed local / sink pages ----
+
+def fixed_pages(L, S, sink_tokens, local_tokens):
+    """[Quest] §2.2 and §3.2 (local window and sink kept besides Quest): the
+    sink pages are those holding the first ``sink_tokens`` tokens, the local
+    pages those holding the last ``local_tokens`` tokens, t in
+    [L - local_tokens, L).  Only pages holding a valid token count.  Returns
+    (sink set, local set)."""
+    P = num_pages(L, S)
+    sink = set()
+    if sink_tokens > 0:
+        sink = set(range(min(P, -(-int(sink_tokens) // S))))
+    local = set()
+    if local_tokens > 0:
+        first = max(0, L - int(local_tokens)) // S
+        local = set(range(first, P))
+    return sink, local
+
+
+def mixed_pages(scores, K, L, S, sink_tokens, local_tokens):
+    """[Quest] §3.2: C = C_local | C_sink | C_quest, where C_quest is the
+    usual top-K over all the request's pages; the three may overlap and a
+    page counts once.  Returned in ascending page order."""
+    sink, local = fixed_pages(L, S, sink_tokens, local_tokens)
+    return sorted(set(top_k_pages(scores, K)) | sink | local)
+
+
+def quest_budget_pages(total_tokens, local_tokens, sink_tokens, S):
+    """[Quest] §2.2 worked budget: after the local window and the sinks, the
+    remaining token slots pay for whole Quest pages."""
+    return (int(total_tokens) - int(local_tokens) - int(sink_tokens)) // int(S)
+
+
 # ------------------------------------------------------------ attention ----
 
 def support(page_ids, L, c, S):
@@ -156,10 +189,12 @@ def attend(q, keys, values, tokens, scale):
     return o, zmax + math.log(w.sum())
 
 
-def decode_request(q, keys, values, L, S, K, scale=None, page_ids=None):
+def decode_request(q, keys, values, L, S, K, scale=None, page_ids=None, sink_tokens=0,
+                   local_tokens=0):
     """One decode step of one request, all heads: summaries (eq. (1)), head
-    bounds (eq. (2)-(3)), KV-head scores (group max), top-K, then exact
-    attention over each query head's support with c = L - 1.
+    bounds (eq. (2)-(3)), KV-head scores (group max), top-K (joined with the
+    fixed sink and local pages when those are asked for, [Quest] §3.2), then
+    exact attention over each query head's support with c = L - 1.
 
     q: [H_q][d]; keys, values: [>= L][H_kv][d] float64.  If ``page_ids``
     ([H_kv][*]) is given it replaces the top-K lists (attention over given
@@ -172,7 +207,10 @@ def decode_request(q, keys, values, L, S, K, scale=None, page_ids=None):
     m, M = page_summaries(keys, L, S)
     U_heads = head_bounds(q, m, M)
     U = kv_head_scores(U_heads, H_kv)
-    sel = [top_k_pages(U[h], K) for h in range(H_kv)]
+    if sink_tokens or local_tokens:
+        sel = [mixed_pages(U[h], K, L, S, sink_tokens, local_tokens) for h in range(H_kv)]
+    else:
+        sel = [top_k_pages(U[h], K) for h in range(H_kv)]
     lists = sel if page_ids is None else page_ids
     out = np.zeros((H_q, d))
     lse = np.zeros(H_q)

@@ -240,6 +240,55 @@ def test_topk_all_equal_and_all_pages():
     assert quest.top_k_pages(np.arange(5.0), 9) == [0, 1, 2, 3, 4]
 
 
+# ------------------------------------------------- fixed local / sink pages ----
+
+def test_local_sink_budget_worked_example():
+    """[Quest] §2.2: 2048 tokens, 512 recent + 4 sinks kept, 1532 slots left,
+    which pay for 95 whole pages at S = 16."""
+    g = load_golden("quest_local_sink_budget.json")
+    assert g["total_tokens"] - g["local_tokens"] - g["sink_tokens"] == g["remaining_tokens"]
+    assert quest.quest_budget_pages(g["total_tokens"], g["local_tokens"], g["sink_tokens"],
+                                    g["page_size"]) == g["quest_whole_pages"]
+
+
+def test_fixed_pages_by_token_positions():
+    # L = 100, S = 16: pages 0..6, the last holding tokens 96..99
+    assert quest.fixed_pages(100, 16, 4, 0) == ({0}, set())
+    assert quest.fixed_pages(100, 16, 16, 0) == ({0}, set())
+    assert quest.fixed_pages(100, 16, 17, 0) == ({0, 1}, set())
+    # the last 20 tokens are 80..99: pages 5 and 6, not only the last page
+    assert quest.fixed_pages(100, 16, 0, 20) == (set(), {5, 6})
+    assert quest.fixed_pages(100, 16, 0, 4) == (set(), {6})
+    assert quest.fixed_pages(100, 16, 0, 5) == (set(), {5, 6})
+    # windows longer than the request keep every page; none past the length
+    assert quest.fixed_pages(100, 16, 1000, 1000) == (set(range(7)), set(range(7)))
+    assert quest.fixed_pages(0, 16, 4, 20) == (set(), set())
+
+
+def test_mixed_pages_union_bruteforce():
+    """[Quest] §3.2: C = C_local | C_sink | C_quest, overlaps once; without
+    fixed pages it is the plain top-K."""
+    rng = _rng(21)
+    for _ in range(200):
+        S = int(rng.choice([1, 4, 16]))
+        L = int(rng.integers(1, 300))
+        P = quest.num_pages(L, S)
+        s = rng.integers(-3, 4, size=P).astype(float)
+        K = int(rng.integers(1, P + 3))
+        sink, local = int(rng.integers(0, 40)), int(rng.integers(0, 80))
+        C = quest.mixed_pages(s, K, L, S, sink, local)
+        top = set(quest.top_k_pages(s, K))
+        fs, fl = quest.fixed_pages(L, S, sink, local)
+        assert C == sorted(set(C)) and all(0 <= j < P for j in C)
+        assert top <= set(C) and fs <= set(C) and fl <= set(C)
+        assert set(C) <= top | fs | fl
+        assert len(C) <= min(K, P) + len(fs) + len(fl)
+        # brute force over token positions for the fixed sets
+        assert fs == {t // S for t in range(min(sink, L))}
+        assert fl == {t // S for t in range(max(0, L - local), L)}
+        assert quest.mixed_pages(s, K, L, S, 0, 0) == quest.top_k_pages(s, K)
+
+
 # ------------------------------------------------------------- attention ----
 
 def _sdpa(q, k, v, scale):
