@@ -150,6 +150,32 @@ qas_status qas_topk_pages(const float* scores, const qas_batch* batch,
                           int32_t* sel, int32_t* sel_count, void* stream);
 
 /*
+ * qas_selection_capacity - entries a selected list can hold when the top-k
+ * is joined with fixed pages: k + ceil(sink_tokens / S) + (local_tokens > 0 ?
+ * ceil(local_tokens / S) + 1 : 0).  Returns 0 for invalid arguments.
+ */
+int32_t qas_selection_capacity(int32_t k, int32_t page_size, int32_t sink_tokens,
+                               int32_t local_tokens);
+
+/*
+ * qas_select_pages - the candidate set C = C_local | C_sink | C_quest of
+ * [Quest] §3.2 (local window and sinks kept besides the Quest pages, §2.2):
+ * C_quest is the top-k of qas_topk_pages over all of the row's pages, C_sink
+ * the pages holding tokens [0, sink_tokens), C_local the pages holding tokens
+ * [L_r - local_tokens, L_r); a page in several sets counts once.  Written in
+ * ascending page order, padded with -1 to sel_stride; sel_count (may be
+ * NULL) receives |C| per row.  sink_tokens = local_tokens = 0 is
+ * qas_topk_pages.
+ *   sel        device [B][H_kv][sel_stride] int32,
+ *              sel_stride >= qas_selection_capacity(k, S, sink, local)
+ */
+qas_status qas_select_pages(const float* scores, const qas_batch* batch,
+                            int32_t num_kv_heads, int32_t page_size, int32_t k,
+                            int32_t sink_tokens, int32_t local_tokens,
+                            int32_t* sel, int32_t sel_stride, int32_t* sel_count,
+                            void* stream);
+
+/*
  * qas_sparse_decode - exact softmax attention of each query head over its
  * support ([PageWeaver] eq. (1)-(2); [Quest] §2.1 paged sparse load):
  * A = { t : floor(t/S) in the KV head's selected list, t < L_r } (decode,
@@ -188,6 +214,24 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch,
                             int32_t* sel_out, void* out, float* lse,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * qas_decode_layer_mixed - qas_decode_layer whose lists are the candidate
+ * set of qas_select_pages (top-k joined with the sink pages of the first
+ * sink_tokens tokens and the local pages of the last local_tokens tokens,
+ * [Quest] §2.2, §3.2).  sel_out, if given, is [B][H_kv][cap] with cap =
+ * qas_selection_capacity(k, S, sink_tokens, local_tokens); the workspace
+ * must hold qas_workspace_bytes(QAS_OP_DECODE_LAYER, ..., cap).  With
+ * sink_tokens = local_tokens = 0 this is qas_decode_layer.
+ */
+qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch,
+                                  const void* q, int32_t q_dtype,
+                                  int32_t num_q_heads, int32_t k,
+                                  int32_t sink_tokens, int32_t local_tokens,
+                                  float sm_scale, const void* k_new,
+                                  const void* v_new, int32_t* sel_out, void* out,
+                                  float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Multi-query chunk ([PageWeaver] eq. (1)-(2) per query; query unions and

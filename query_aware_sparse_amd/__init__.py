@@ -52,10 +52,14 @@ _SIGNATURES = {
     "qas_append": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
     "qas_score_pages": (_I, [_P, _P, _P, _I, _I, _P, _P]),
     "qas_topk_pages": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "qas_selection_capacity": (_I, [_I, _I, _I, _I]),
+    "qas_select_pages": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P]),
     "qas_sparse_decode": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, ctypes.c_float,
                                _P, _P, _P, ctypes.c_size_t, _P]),
     "qas_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
                               _P, _P, _P, ctypes.c_size_t, _P]),
+    "qas_decode_layer_mixed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                                    _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "qas_workspace_bytes": (ctypes.c_size_t, [_I, _P, _P, _I, _I]),
     "qas_chunk_groups": (_I, [_I, _I, _I]),
     "qas_union_pages": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
@@ -152,6 +156,19 @@ def qas_topk_pages(scores, batch, num_kv_heads, page_size, k, sel, sel_count=Non
                               _stream(stream)))
 
 
+def qas_selection_capacity(k, page_size, sink_tokens, local_tokens):
+    return int(_load().qas_selection_capacity(int(k), int(page_size), int(sink_tokens),
+                                              int(local_tokens)))
+
+
+def qas_select_pages(scores, batch, num_kv_heads, page_size, k, sink_tokens, local_tokens, sel,
+                     sel_count=None, stream=None):
+    """sel: int32 [B][H_kv][stride], stride >= qas_selection_capacity(...)."""
+    _check(_load().qas_select_pages(_ptr(scores), ctypes.byref(batch), int(num_kv_heads),
+                                    int(page_size), int(k), int(sink_tokens), int(local_tokens),
+                                    _ptr(sel), sel.shape[-1], _ptr(sel_count), _stream(stream)))
+
+
 def qas_workspace_bytes(op, cache, batch, num_q_heads, k):
     return int(_load().qas_workspace_bytes(int(op), ctypes.byref(cache), ctypes.byref(batch),
                                        int(num_q_heads), int(k)))
@@ -182,6 +199,17 @@ def qas_decode_layer(cache, batch, q, k, sm_scale, out, lse, workspace, k_new=No
                                 _stream(stream)))
 
 
+def qas_decode_layer_mixed(cache, batch, q, k, sink_tokens, local_tokens, sm_scale, out, lse,
+                           workspace, k_new=None, v_new=None, sel_out=None, stream=None):
+    _check(_load().qas_decode_layer_mixed(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+                                          dtype_code(q), q.shape[1], int(k), int(sink_tokens),
+                                          int(local_tokens), float(sm_scale), _ptr(k_new),
+                                          _ptr(v_new), _ptr(sel_out), _ptr(out), _ptr(lse),
+                                          _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
+
+
 def qas_chunk_groups(num_queries, batch, group):
     return int(_load().qas_chunk_groups(int(num_queries), int(batch), int(group)))
 
@@ -209,7 +237,7 @@ def version():
     return _load().qas_version().decode()
 
 
-__all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_sparse_decode",
-           "qas_decode_layer", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_union_pages",
+__all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
+           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

@@ -130,10 +130,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     TopkRow<TPT> t;
     t.load_scores(a.scores + ((size_t)r * H + h) * a.max_pages, cap);
     const int n_tk = min(n_pages, cap);
-    const int take = min(a.sel_len, n_tk);
+    const int take = min(a.k, n_tk);
     t.load_pages(a.page_indices + pbeg, n_tk);
+    t.set_fixed(L, S, a.sink_tokens, a.local_tokens);
     t.select(take, tsh);
-    int pos = t.first_position(tsh);
+    int count;
+    int pos = t.first_position(tsh, &count);
     int32_t* so = a.sel_out ? a.sel_out + ((size_t)r * H + h) * a.sel_len : nullptr;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
@@ -148,8 +150,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
       }
     }
     if (so)
-      for (int e = max(e0, take) + tid; e < e1; e += kDecThreads) so[e] = -1;
-    npg = max(0, min(e1, take) - e0);
+      for (int e = max(e0, count) + tid; e < e1; e += kDecThreads) so[e] = -1;
+    npg = max(0, min(e1, count) - e0);
   } else {
     // ---- 1. distinct valid pages of entries [e0, e1), in entry order --------
     const int32_t* row = a.sel + ((size_t)r * H + h) * a.sel_stride;

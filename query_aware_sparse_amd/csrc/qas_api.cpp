@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "qas.h"
+#include <stdint.h>
 #include "qas_internal.h"
 
 namespace {
@@ -169,6 +170,9 @@ qas::DecodeArgs decode_args(const qas_cache* c, const qas_batch* b, const void* 
   a.sel_out = nullptr;
   a.max_pages = b->max_pages;
   a.clear_tickets = 0;
+  a.k = sel_len;
+  a.sink_tokens = 0;
+  a.local_tokens = 0;
   return a;
 }
 
@@ -267,15 +271,30 @@ qas_status qas_score_pages(const qas_cache* cache, const qas_batch* batch, const
   return ok();
 }
 
-qas_status qas_topk_pages(const float* scores, const qas_batch* batch, int32_t num_kv_heads,
-                          int32_t page_size, int32_t k, int32_t* sel, int32_t* sel_count,
-                          void* stream) {
+int32_t qas_selection_capacity(int32_t k, int32_t page_size, int32_t sink_tokens,
+                               int32_t local_tokens) {
+  if (k < 1 || page_size < 1 || sink_tokens < 0 || local_tokens < 0) return 0;
+  const int64_t cap = (int64_t)k + (sink_tokens + (int64_t)page_size - 1) / page_size +
+                      (local_tokens > 0 ? (local_tokens + (int64_t)page_size - 1) / page_size + 1
+                                        : 0);
+  return cap > INT32_MAX ? 0 : (int32_t)cap;
+}
+
+qas_status qas_select_pages(const float* scores, const qas_batch* batch, int32_t num_kv_heads,
+                            int32_t page_size, int32_t k, int32_t sink_tokens,
+                            int32_t local_tokens, int32_t* sel, int32_t sel_stride,
+                            int32_t* sel_count, void* stream) {
   qas_status st = check_batch(batch);
   if (st) return st;
   if (!scores || !sel) return fail(QAS_ERR_NULL, "scores / sel is NULL");
   if (num_kv_heads < 1) return fail(QAS_ERR_SHAPE, "num_kv_heads %d < 1", num_kv_heads);
   if (!pow2_in(page_size, 1, 256)) return fail(QAS_ERR_SHAPE, "page_size %d", page_size);
   if (k < 1) return fail(QAS_ERR_SHAPE, "k %d < 1", k);
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(QAS_ERR_SHAPE, "sink_tokens %d / local_tokens %d < 0", sink_tokens, local_tokens);
+  const int32_t cap = qas_selection_capacity(k, page_size, sink_tokens, local_tokens);
+  if (cap < 1 || sel_stride < cap)
+    return fail(QAS_ERR_SHAPE, "sel_stride %d < qas_selection_capacity %d", sel_stride, cap);
   if (batch->max_pages > qas::kTopkMaxPages)
     return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed %d", batch->max_pages,
                 qas::kTopkMaxPages);
@@ -292,9 +311,19 @@ qas_status qas_topk_pages(const float* scores, const qas_batch* batch, int32_t n
   a.S = page_size;
   a.k = k;
   a.max_pages = batch->max_pages;
+  a.sink_tokens = sink_tokens;
+  a.local_tokens = local_tokens;
+  a.sel_stride = sel_stride;
   hipError_t e = qas::launch_topk(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
+}
+
+qas_status qas_topk_pages(const float* scores, const qas_batch* batch, int32_t num_kv_heads,
+                          int32_t page_size, int32_t k, int32_t* sel, int32_t* sel_count,
+                          void* stream) {
+  return qas_select_pages(scores, batch, num_kv_heads, page_size, k, 0, 0, sel, k, sel_count,
+                          stream);
 }
 
 qas_status qas_sparse_decode(const qas_cache* cache, const qas_batch* batch, const void* q,
@@ -326,10 +355,12 @@ qas_status qas_sparse_decode(const qas_cache* cache, const qas_batch* batch, con
   return ok();
 }
 
-qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, const void* q,
-                            int32_t q_dtype, int32_t num_q_heads, int32_t k, float sm_scale,
-                            const void* k_new, const void* v_new, int32_t* sel_out, void* out,
-                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch,
+                                  const void* q, int32_t q_dtype, int32_t num_q_heads, int32_t k,
+                                  int32_t sink_tokens, int32_t local_tokens, float sm_scale,
+                                  const void* k_new, const void* v_new, int32_t* sel_out,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   qas_status st = check_cache(cache, true, true);
   if (st) return st;
   if ((st = check_batch(batch))) return st;
@@ -341,17 +372,21 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   if (q_dtype != cache->kv_dtype)
     return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
   if (k < 1) return fail(QAS_ERR_SHAPE, "k %d < 1", k);
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(QAS_ERR_SHAPE, "sink_tokens %d / local_tokens %d < 0", sink_tokens, local_tokens);
+  const int32_t cap = qas_selection_capacity(k, cache->page_size, sink_tokens, local_tokens);
+  if (cap < 1) return fail(QAS_ERR_SHAPE, "selection capacity overflows");
   if (batch->max_pages > qas::kTopkMaxPages)
     return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed %d", batch->max_pages,
                 qas::kTopkMaxPages);
-  const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, k);
+  const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, cap);
   if (!workspace || workspace_bytes < need)
     return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   if (!qas::score_supported(cache->kv_dtype, cache->head_dim, g, cache->num_kv_heads))
     return fail(QAS_ERR_UNSUPPORTED, "score: %d KV heads of d=%d", cache->num_kv_heads,
                 cache->head_dim);
   hipStream_t s = (hipStream_t)stream;
-  const DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
+  const DecodePlan p = plan_decode(cache, batch, num_q_heads, cap);
   char* ws = (char*)workspace;
   float* scores = (float*)ws;
   ws += layer_scores_bytes(cache, batch);
@@ -369,9 +404,13 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   sa.tickets = tickets;
   sa.row_stride = layer_fused_topk(batch) ? batch->max_pages : 0;
   if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
-  qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, nullptr, k, k, sm_scale, out,
-                                   lse, partials, p.n_split, 0);
+  // lists hold the top-k joined with the fixed pages: cap entries per row
+  qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, nullptr, cap, cap, sm_scale,
+                                   out, lse, partials, p.n_split, 0);
   da.tickets = tickets;
+  da.k = k;
+  da.sink_tokens = sink_tokens;
+  da.local_tokens = local_tokens;
   if (layer_fused_topk(batch)) {
     // 2. top-k per (request, KV head) inside the attention kernel
     da.scores = scores;
@@ -379,7 +418,7 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   } else {
     // 2. top-k per (request, KV head) in a kernel of its own (long rows)
     int32_t* sel = sel_out ? sel_out : (int32_t*)ws;
-    ws += layer_sel_bytes(cache, batch, k);
+    ws += layer_sel_bytes(cache, batch, cap);
     int32_t* sel_phys = (int32_t*)ws;
     qas::TopkArgs ta;
     ta.scores = scores;
@@ -394,6 +433,9 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
     ta.S = cache->page_size;
     ta.k = k;
     ta.max_pages = batch->max_pages;
+    ta.sink_tokens = sink_tokens;
+    ta.local_tokens = local_tokens;
+    ta.sel_stride = cap;
     if ((e = qas::launch_topk(ta, s)) != hipSuccess) return hip_fail(e, "top-k launch");
     da.sel = sel;
     da.sel_phys = sel_phys;
@@ -401,6 +443,14 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
   // 3. sparse attention with the split merge
   if ((e = qas::launch_decode(da, s)) != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, const void* q,
+                            int32_t q_dtype, int32_t num_q_heads, int32_t k, float sm_scale,
+                            const void* k_new, const void* v_new, int32_t* sel_out, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return qas_decode_layer_mixed(cache, batch, q, q_dtype, num_q_heads, k, 0, 0, sm_scale, k_new,
+                                v_new, sel_out, out, lse, workspace, workspace_bytes, stream);
 }
 
 int32_t qas_chunk_groups(int32_t num_queries, int32_t batch, int32_t group) {

@@ -37,9 +37,11 @@ struct TopkArgs {
   const int32_t* page_indices;
   int32_t* sel;
   int32_t* sel_phys;         // optional physical pages of `sel`
-  int32_t* sel_count;
+  int32_t* sel_count;        // pages written per row (top-K and fixed pages)
   int B, H_kv, S, k;
   int max_pages;             // longest row (sizes the per-thread register run)
+  int sink_tokens, local_tokens;   // fixed pages joined with the top-K (0: none)
+  int sel_stride;            // row stride of sel / sel_phys (>= the row's count)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 constexpr int kTopkMaxPages = 16384;  // 256 threads x 64 scores held in registers
@@ -78,6 +80,8 @@ struct DecodeArgs {
   const float* scores;
   int32_t* sel_out;          // optional [B][H_kv][sel_len] copy of the selection
   int max_pages;
+  int k;                     // in-kernel top-K: pages Quest selects per row
+  int sink_tokens, local_tokens;   // in-kernel top-K: fixed pages joined with it
   int B, H_kv, H_q, d, S, kv_dtype, g;
   int sel_stride, sel_len, n_split;
   int dedupe;                // 0: lists known unique and valid-or-negative

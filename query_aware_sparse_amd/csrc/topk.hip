@@ -1,6 +1,7 @@
 // Standalone top-K page selection per (request, KV head): the Quest page's
 // second stage ("3.1.1 · Quest", §1 and Fig. 1), ordered by (score
-// descending, page index ascending), written in ascending page order and
+// descending, page index ascending), joined with the fixed sink and
+// local-window pages when asked (§3.2), written in ascending page order and
 // padded with -1.  One workgroup per row runs the register-resident
 // histogram select of topk_block.h.
 #include "qas_device.h"
@@ -23,17 +24,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
   const int L = a.seq_lens[r];
   // never more scores than the registers hold
   const int n = L > 0 ? min(min((L + a.S - 1) / a.S, P_r), kTkThreads * PT) : 0;
-  const int K = a.k;
-  const int take = min(K, n);
-  int32_t* out = a.sel + (size_t)row * K;
-  int32_t* out_phys = a.sel_phys ? a.sel_phys + (size_t)row * K : nullptr;
-  if (a.sel_count && tid == 0) a.sel_count[row] = take;
+  const int take = min(a.k, n);
+  int32_t* out = a.sel + (size_t)row * a.sel_stride;
+  int32_t* out_phys = a.sel_phys ? a.sel_phys + (size_t)row * a.sel_stride : nullptr;
 
   TopkRow<PT> t;
   t.load(a.scores + (size_t)pbeg * H + (size_t)h * P_r,
          out_phys ? a.page_indices + pbeg : nullptr, n);
+  t.set_fixed(L, a.S, a.sink_tokens, a.local_tokens);
   t.select(take, sh);
-  int pos = t.first_position(sh);
+  int count;
+  int pos = t.first_position(sh, &count);
+  if (a.sel_count && tid == 0) a.sel_count[row] = count;
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
     if (t.selected(k)) {
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
       ++pos;
     }
   }
-  for (int j = take + tid; j < K; j += kTkThreads) {
+  for (int j = count + tid; j < a.sel_stride; j += kTkThreads) {
     out[j] = -1;
     if (out_phys) out_phys[j] = -1;
   }

@@ -21,7 +21,10 @@
 //     taken is the threshold (T_s, T_j): page j is selected iff s_j > T_s,
 //     or s_j == T_s and j <= T_j.
 // An index-ordered compaction (one workgroup scan over the runs) gives every
-// selected page its position in the ascending output list.  -0.0 and +0.0
+// selected page its position in the ascending output list.  Pages fixed in
+// advance (the sink pages j < fs_end and the local-window pages j >=
+// fl_begin, the Quest page's §3.2 candidate set C_local | C_sink | C_quest)
+// join the top-K in that list; a page in several sets appears once.  -0.0 and +0.0
 // are equal scores; NaN ranks below every number.
 #pragma once
 
@@ -160,6 +163,15 @@ struct TopkRow {
   int j0, n;
   float Ts;
   int Tj;
+  int fs_end = 0;                 // pages j < fs_end are kept (sinks)
+  int fl_begin = 0x7fffffff;      // pages j >= fl_begin are kept (local window)
+
+  // Fixed pages of a row of L tokens (n valid pages of S tokens): those
+  // holding the first sink_tokens tokens and the last local_tokens tokens.
+  __device__ __forceinline__ void set_fixed(int L, int S, int sink_tokens, int local_tokens) {
+    fs_end = sink_tokens > 0 ? min(n, (sink_tokens + S - 1) / S) : 0;
+    fl_begin = local_tokens > 0 ? max(0, L - local_tokens) / S : 0x7fffffff;
+  }
 
   // Scores srow[j] for j < cap (the row's allocated extent; entries at or
   // beyond the row length are loaded but never used).
@@ -190,7 +202,8 @@ struct TopkRow {
   __device__ __forceinline__ bool valid(int k) const { return j0 + k < n; }
 
   __device__ __forceinline__ bool selected(int k) const {
-    return valid(k) & ((v[k] > Ts) | ((v[k] == Ts) & (j0 + k <= Tj)));
+    const int j = j0 + k;
+    return valid(k) & ((v[k] > Ts) | ((v[k] == Ts) & (j <= Tj)) | (j < fs_end) | (j >= fl_begin));
   }
 
   // Find (Ts, Tj) for the top `take` (<= n) entries; every thread of the
@@ -365,13 +378,13 @@ struct TopkRow {
   }
 
   // Output position of this thread's first selected page (selected pages
-  // are numbered in ascending page order); every thread must call this.
-  __device__ __forceinline__ int first_position(TopkShared& sh) const {
+  // are numbered in ascending page order) and, in *count, the number of
+  // selected pages; every thread must call this.
+  __device__ __forceinline__ int first_position(TopkShared& sh, int* count) const {
     int mine = 0;
 #pragma unroll
     for (int k = 0; k < PT; ++k) mine += selected(k) ? 1 : 0;
-    int total;
-    return tk::block_excl_scan(mine, sh.scan[1], &total);
+    return tk::block_excl_scan(mine, sh.scan[1], count);
   }
 };
 

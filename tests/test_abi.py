@@ -98,3 +98,30 @@ def test_workspace_sizes_are_consistent(qas):
     assert 0 < sd < dl
     assert sd % 256 == 0 and dl % 256 == 0
     assert lib.qas_workspace_bytes(9, ctypes.byref(c), ctypes.byref(b), 32, 64) == 0
+
+
+def test_selection_capacity_and_select_validation(qas):
+    """List capacity for the top-k joined with fixed sink / local pages, and
+    argument checks of qas_select_pages / qas_decode_layer_mixed (no launch)."""
+    from ctypes import byref
+    lib = qas.lib
+    assert qas.qas_selection_capacity(256, 16, 0, 0) == 256
+    # 4 sink tokens -> 1 page; 512 local tokens -> up to 32 + 1 pages (unaligned window)
+    assert qas.qas_selection_capacity(95, 16, 4, 512) == 95 + 1 + 33
+    assert qas.qas_selection_capacity(10, 16, 17, 1) == 10 + 2 + 2
+    assert qas.qas_selection_capacity(0, 16, 0, 0) == 0
+    assert qas.qas_selection_capacity(4, 16, -1, 0) == 0
+    b = _batch(qas)
+    # stride below the capacity, negative window: shape errors before any launch
+    assert lib.qas_select_pages(8, byref(b), 8, 16, 4, 4, 32, 8, 4, None, None) == 2
+    assert b"sel_stride" in lib.qas_last_error()
+    assert lib.qas_select_pages(8, byref(b), 8, 16, 4, -1, 0, 8, 16, None, None) == 2
+    c = _cache(qas)
+    assert lib.qas_decode_layer_mixed(byref(c), byref(b), 8, 1, 32, 64, 0, -5, 0.1, None, None,
+                                      None, 8, None, 8, 1 << 30, None) == 2
+    # the mixed layer needs the workspace of its list capacity
+    cap = qas.qas_selection_capacity(64, 16, 4, 512)
+    need = lib.qas_workspace_bytes(2, byref(c), byref(b), 32, cap)
+    assert need > lib.qas_workspace_bytes(2, byref(c), byref(b), 32, 64)
+    assert lib.qas_decode_layer_mixed(byref(c), byref(b), 8, 1, 32, 64, 4, 512, 0.1, None, None,
+                                      None, 8, None, 8, need - 1, None) == 5
