@@ -237,6 +237,52 @@ def union_with_membership(page_sets):
     return union, member
 
 
+# ------------------------------------------------------------- regroup ---
+
+def regroup_window(page_sets, g):
+    """[PageWeaver] Algorithm 1 (windowed page-affinity grouping) on one
+    window, as the notes walk through it: the lowest unassigned query seeds a
+    group with U = its set; the next member is the unassigned query j with the
+    smallest (|S_j minus U|, j), after which U grows by S_j and the costs are
+    taken again; a group closes at g members or when the window is used up.
+    ``page_sets`` are the window's sets in query order; returns the window's
+    local indices in execution order (a permutation)."""
+    left = list(range(len(page_sets)))
+    order = []
+    while left:
+        seed = min(left)
+        left.remove(seed)
+        group = [seed]
+        U = set(page_sets[seed])
+        while len(group) < g and left:
+            j = min(left, key=lambda j: (len(set(page_sets[j]) - U), j))
+            left.remove(j)
+            group.append(j)
+            U |= set(page_sets[j])
+        order += group
+    return order
+
+
+def regroup(sets, n_pages, q_indptr, window, g, capacity):
+    """[PageWeaver] windowed regroup of one KV head's queries: windows of
+    ``window`` consecutive queries that stay inside their request; a query's
+    set is its deduplicated valid page IDs (0 <= p < n_pages[r]); a request
+    with more than ``capacity`` pages keeps the identity order.  Returns ids
+    [N]: ids[n] is the original query executed in slot n (a bijection inside
+    every request)."""
+    ids = []
+    for r in range(len(q_indptr) - 1):
+        a, b = int(q_indptr[r]), int(q_indptr[r + 1])
+        if n_pages[r] > capacity:
+            ids += list(range(a, b))
+            continue
+        for w0 in range(a, b, window):
+            w1 = min(b, w0 + window)
+            win = [{int(p) for p in sets[n] if 0 <= p < n_pages[r]} for n in range(w0, w1)]
+            ids += [w0 + i for i in regroup_window(win, g)]
+    return ids
+
+
 def chunk_attention(q, keys, values, sets, L, c, S, g, scale=None):
     """Multi-query chunk ([PageWeaver] eq. (1)-(2)): every query position n has
     its own page set per KV head, its own length L[n] and causal limit c[n].

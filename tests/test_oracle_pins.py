@@ -109,6 +109,60 @@ def test_union_and_membership_example():
 
 # ---------------------------------------------------- closed forms, bounds --
 
+def test_regroup_worked_example():
+    """[PageWeaver] Algorithm 1 step-by-step example (g = 3): seed 0, first
+    costs 2,1,2,2,2, pi = [0,2,3,1,4,5]; page visits of the two groups go
+    from 5 + 5 = 10 in the original order to 4 + 3 = 7."""
+    g = load_golden("pageweaver_regroup.json")
+    sets = [set(x) for x in g["sets"]]
+    # the printed first-round costs |S_j minus S_0| of candidates 1..5
+    assert [len(sets[j] - sets[0]) for j in range(1, 6)] == g["seed0_costs"]
+    pi = quest.regroup_window(sets, g["group"])
+    assert pi == g["pi"]
+
+    def visits(order):
+        G = g["group"]
+        return sum(len(quest.union_with_membership([sets[i] for i in order[k:k + G]])[0])
+                   for k in range(0, len(order), G))
+    assert visits(list(range(6))) == g["pages_original_order"]
+    assert visits(pi) == g["pages_regrouped"]
+    # windows within a request: one window holding all six gives the same
+    assert quest.regroup([list(x) for x in g["sets"]], [11], [0, 6], 8, 3, 512) == pi
+
+
+def test_regroup_uses_marginal_increase_not_overlap():
+    """With sets of different sizes the notes keep the marginal increase
+    |S_j minus U| (not the largest overlap): S_1 shares 2 pages with S_0 but
+    adds 4, S_2 shares none and adds 1."""
+    sets = [{1, 2, 3, 4}, {1, 2, 5, 6, 7, 8}, {9}]
+    assert quest.regroup_window(sets, 2) == [0, 2, 1]
+
+
+def test_regroup_is_a_windowed_bijection():
+    rng = _rng(33)
+    for _ in range(40):
+        B = int(rng.integers(1, 4))
+        counts = rng.integers(0, 40, size=B)
+        q_indptr = np.concatenate([[0], np.cumsum(counts)])
+        n_pages = rng.integers(1, 30, size=B)
+        N = int(q_indptr[-1])
+        sets = [list(rng.integers(-2, 35, size=5)) for _ in range(N)]
+        W = int(rng.choice([8, 16, 64]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        cap = int(rng.choice([8, 512]))
+        ids = quest.regroup(sets, n_pages, q_indptr, W, g, cap)
+        assert sorted(ids) == list(range(N))
+        for r in range(B):
+            a, b = int(q_indptr[r]), int(q_indptr[r + 1])
+            assert sorted(ids[a:b]) == list(range(a, b))        # stays in its request
+            for w0 in range(a, b, W):                            # and in its window
+                assert sorted(ids[w0:min(b, w0 + W)]) == list(range(w0, min(b, w0 + W)))
+            if n_pages[r] > cap or g == 1:
+                assert ids[a:b] == list(range(a, b))             # identity
+    # equal sets: every cost ties, the lowest ID wins, so the order is kept
+    assert quest.regroup_window([{1, 2}] * 9, 4) == list(range(9))
+
+
 def test_bound_closed_form():
     """A box's support function is q.(M+m)/2 + |q|.(M-m)/2."""
     rng = _rng(1)
