@@ -137,10 +137,11 @@ def cpu_baseline(case, seconds):
             "cpu": platform.processor() or platform.machine()}
 
 
-def chunk_accounting(case):
+def chunk_accounting(case, ids=None):
     """Executed MFMA flops (every union page of every (group, KV head) tile:
     QK and PV of 32 rows x S tokens x d), useful flops (each query head over
-    its own support), and K/V bytes (union-logical and distinct)."""
+    its own support), and K/V bytes (union-logical and distinct).  ``ids``
+    ([H_kv][N]) is an execution order (groups of consecutive slots)."""
     import numpy as np
     P = -(-case.L // case.S)
     N, H, _ = case.sets.shape
@@ -149,9 +150,10 @@ def chunk_accounting(case):
     union_pages = 0
     distinct = set()
     for h in range(H):
+        order = range(N) if ids is None else [int(x) for x in ids[h]]
         for g0 in range(0, N, case.group):
             union = set()
-            for n in range(g0, min(N, g0 + case.group)):
+            for n in (order[k] for k in range(g0, min(N, g0 + case.group))):
                 s = {int(p) for p in case.sets[n, h] if 0 <= p < P}
                 union |= s
                 toks = sum(min(case.S, min(case.L, int(case.q_pos[n]) + 1) - p * case.S)
@@ -196,40 +198,89 @@ def bench_chunk(args):
     lse = torch.empty((NL, case.N, case.H_q), device="cuda")
     scale = 1.0 / math.sqrt(case.d)
 
-    def call(i):
+    window = 64
+    ids = [torch.empty((case.H_kv, case.N), dtype=torch.int32, device="cuda") for _ in range(NL)]
+
+    def regroup(i):
+        c = copies[i]
+        qas.qas_regroup_queries(c.db.batch, c.q_indptr, c.sets, c.S, window, c.group, ids[i])
+
+    def call(i, order=None):
         c = copies[i]
         qas.qas_chunk_attention(c.cache, c.db.batch, c.q_indptr, c.q_pos, c.q, c.sets,
-                                c.group, scale, out[i], lse[i])
+                                c.group, scale, out[i], lse[i], ids=order)
 
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        for w in range(max(NL, args.warmup)):
-            call(w % NL)
-    torch.cuda.current_stream().wait_stream(stream)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(NL):
-            call(i)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, math.ceil(args.steps / NL))
-    steps = reps * NL
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    rs = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(rs)
+    def timed(fn):
+        """Graph of one pass over the copies, replayed; returns (wall ms per
+        call, event-timed us per call, calls)."""
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for w in range(max(NL, args.warmup)):
+                fn(w % NL)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(NL):
+                fn(i)
+        torch.cuda.synchronize()
         graph.replay()
-        e1.record(rs)
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(args.steps / NL))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        rs = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(rs)
+            graph.replay()
+            e1.record(rs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        n = reps * NL
+        return (wall * 1e3 / n, float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL,
+                n)
+
+    # original order (the line's value), then the windowed regroup
+    ms, call_us, steps = timed(call)
+    for i in range(NL):
+        regroup(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / steps
-    call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL
+    _, pre_us, _ = timed(lambda i: call(i, ids[i]))
+    _, regroup_us, _ = timed(regroup)
+    _, online_us, _ = timed(lambda i: (regroup(i), call(i, ids[i])))
+    acct_rg = chunk_accounting(case, ids[0].cpu().numpy())
+    moved = int((ids[0].cpu().numpy() != np.arange(case.N)[None, :]).sum())
+    log(f"[bench] regroup W={window}: {moved} of {case.N * case.H_kv} slots moved, mean union "
+        f"{acct_rg['mean_union_pages']:.1f} pages; precomputed {pre_us:.2f} us, regroup alone "
+        f"{regroup_us:.2f} us, online {online_us:.2f} us")
+
+    # the same chunk with the query sets shuffled (per KV head), so that
+    # neighbouring queries no longer share pages: original order vs regroup
+    rng = np.random.default_rng(4)
+    shuf = torch.from_numpy(np.ascontiguousarray(np.stack(
+        [case.sets[rng.permutation(case.N), h, :] for h in range(case.H_kv)], axis=1))).cuda()
+    sets_nat = [c.sets for c in copies]
+    for c in copies:
+        c.sets = shuf
+    _, shuf_us, _ = timed(call)
+    for i in range(NL):
+        regroup(i)
+    torch.cuda.synchronize()
+    _, shuf_pre_us, _ = timed(lambda i: call(i, ids[i]))
+    _, shuf_online_us, _ = timed(lambda i: (regroup(i), call(i, ids[i])))
+    case_shuf = type(case).__new__(type(case))
+    case_shuf.__dict__.update(case.__dict__)
+    case_shuf.sets = shuf.cpu().numpy()
+    shuf_union = chunk_accounting(case_shuf)["mean_union_pages"]
+    shuf_union_rg = chunk_accounting(case_shuf, ids[0].cpu().numpy())["mean_union_pages"]
+    for c, st in zip(copies, sets_nat):
+        c.sets = st
+    log(f"[bench] shuffled sets: mean union {shuf_union:.1f} -> {shuf_union_rg:.1f} pages after "
+        f"regroup; original {shuf_us:.2f} us, precomputed {shuf_pre_us:.2f} us, online "
+        f"{shuf_online_us:.2f} us")
     exe = acct["executed_flops"] / (call_us * 1e-6) / 1e12
     use = acct["useful_flops"] / (call_us * 1e-6) / 1e12
     log(f"[bench] {steps} chunk calls: {ms * 1e3:.2f} us/call, executed {exe:.1f} TFLOP/s, "
@@ -242,7 +293,19 @@ def bench_chunk(args):
         "config": {"workload": "multi-query chunk, 64K context", "context": case.L,
                    "page_size": case.S, "queries": case.N, "pages_per_set": case.kq,
                    "q_heads": case.H_q, "kv_heads": case.H_kv, "head_dim": case.d,
-                   "group": case.group, "cache_copies": NL, "hip_graph": True, **acct},
+                   "group": case.group, "cache_copies": NL, "hip_graph": True, **acct,
+                   "regroup": {"window": window, "slots_moved": moved,
+                               "mean_union_pages": round(acct_rg["mean_union_pages"], 2),
+                               "original_ids_us": round(call_us, 3),
+                               "precomputed_pi_us": round(pre_us, 3),
+                               "regroup_alone_us": round(regroup_us, 3),
+                               "online_pi_us": round(online_us, 3),
+                               "shuffled_sets": {
+                                   "mean_union_pages": round(shuf_union, 2),
+                                   "mean_union_pages_regrouped": round(shuf_union_rg, 2),
+                                   "original_ids_us": round(shuf_us, 3),
+                                   "precomputed_pi_us": round(shuf_pre_us, 3),
+                                   "online_pi_us": round(shuf_online_us, 3)}}},
         "roofline": {"bound": "mfma", "achieved": round(exe, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(exe / FP8_PEAK_TFLOPS, 4),
                      "traffic": None, "kernel": "union_attn_kernel",

@@ -252,10 +252,34 @@ qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch
 int32_t qas_chunk_groups(int32_t num_queries, int32_t batch, int32_t group);
 
 /*
+ * qas_regroup_queries - windowed page-affinity regroup ([PageWeaver]
+ * Algorithm 1, annotations 69BMX58K / TT5ABQLD / AWLR3K97): for every KV
+ * head h, each request's queries are cut into windows of `window`
+ * consecutive queries; inside a window, the lowest unassigned query seeds a
+ * group with union U = its set, and the next member is the unassigned query
+ * j with the smallest (|S_j minus U|, j), U growing after every pick, until
+ * the group has `group` members.  S_j is query j's deduplicated set of valid
+ * page IDs (0 <= p < ceil(L_r / S)).  Writes ids[h][slot] = the original
+ * query executed in slot `slot`, a bijection inside every request (groups of
+ * `group` consecutive slots are the union kernel's groups).  Requests of more
+ * than 1024 pages keep the identity order; group = 1 is the identity.
+ *   sets   device [N][H_kv][kq] int32
+ *   ids    device [H_kv][N] int32
+ *   window in [1, 128] and a multiple of group; group in [1, 8].
+ */
+qas_status qas_regroup_queries(const qas_batch* batch, const int32_t* q_indptr,
+                               int32_t num_queries, const int32_t* sets,
+                               int32_t num_kv_heads, int32_t kq, int32_t page_size,
+                               int32_t window, int32_t group, int32_t* ids,
+                               void* stream);
+
+/*
  * qas_union_pages - union preparation alone: for every group g and KV head
  * h, the ascending union of the group's valid page IDs, its size, and one
- * membership byte per union page (bit i: query i of the group holds the
- * page).
+ * membership byte per union page (bit i: the query in slot i of the group
+ * holds the page).  ids (device [H_kv][N], may be NULL = identity) is an
+ * execution order from qas_regroup_queries: group g of head h is then the
+ * queries ids[h][slots of g].
  *   union_pages  device [groups][H_kv][group * kq] int32, -1 padded
  *   union_count  device [groups][H_kv] int32
  *   membership   device [groups][H_kv][group * kq] uint8
@@ -264,9 +288,9 @@ int32_t qas_chunk_groups(int32_t num_queries, int32_t batch, int32_t group);
 qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr,
                            int32_t num_queries, const int32_t* sets,
                            int32_t num_kv_heads, int32_t kq, int32_t group,
-                           int32_t page_size, int32_t* union_pages,
-                           int32_t* union_count, uint8_t* membership,
-                           void* stream);
+                           int32_t page_size, const int32_t* ids,
+                           int32_t* union_pages, int32_t* union_count,
+                           uint8_t* membership, void* stream);
 
 /*
  * qas_chunk_attention - attention of every query of the chunk over its own
@@ -276,14 +300,17 @@ qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr,
  * NULL).  Page size 32 or 64.  QK^T runs with the query row quantised to
  * e4m3 (per-row scale) and PV with probabilities scaled by 256 and
  * quantised to e4m3; running max/sum and accumulation are fp32.  No summary
- * is read and no workspace is needed.
+ * is read and no workspace is needed.  ids (may be NULL) is an execution
+ * order as in qas_union_pages; every query still reads its own Q row, set
+ * and causal limit and writes its own output row, so the result does not
+ * depend on the order beyond rounding.
  */
 qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
                                const int32_t* q_indptr, int32_t num_queries,
                                const int32_t* q_pos, const void* q, int32_t q_dtype,
                                int32_t num_q_heads, const int32_t* sets, int32_t kq,
-                               int32_t group, float sm_scale, void* out, float* lse,
-                               void* stream);
+                               int32_t group, const int32_t* ids, float sm_scale,
+                               void* out, float* lse, void* stream);
 
 enum { QAS_OP_SPARSE_DECODE = 1, QAS_OP_DECODE_LAYER = 2 };
 

@@ -62,9 +62,10 @@ _SIGNATURES = {
                                     _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "qas_workspace_bytes": (ctypes.c_size_t, [_I, _P, _P, _I, _I]),
     "qas_chunk_groups": (_I, [_I, _I, _I]),
-    "qas_union_pages": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
-    "qas_chunk_attention": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _I, _I, ctypes.c_float,
-                                 _P, _P, _P]),
+    "qas_regroup_queries": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "qas_union_pages": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "qas_chunk_attention": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _P,
+                                 ctypes.c_float, _P, _P, _P]),
     "qas_status_string": (ctypes.c_char_p, [_I]),
     "qas_last_error": (ctypes.c_char_p, []),
     "qas_version": (ctypes.c_char_p, []),
@@ -214,23 +215,33 @@ def qas_chunk_groups(num_queries, batch, group):
     return int(_load().qas_chunk_groups(int(num_queries), int(batch), int(group)))
 
 
+def qas_regroup_queries(batch, q_indptr, sets, page_size, window, group, ids, stream=None):
+    """sets: int32 [N][H_kv][kq]; ids: int32 [H_kv][N] (execution order out)."""
+    N, H_kv, kq = sets.shape
+    _check(_load().qas_regroup_queries(ctypes.byref(batch), _ptr(q_indptr), N, _ptr(sets), H_kv,
+                                       kq, int(page_size), int(window), int(group), _ptr(ids),
+                                       _stream(stream)))
+
+
 def qas_union_pages(batch, q_indptr, sets, group, page_size, union_pages, union_count,
-                    membership, stream=None):
-    """sets: int32 [N][H_kv][kq]; outputs sized by qas_chunk_groups()."""
+                    membership, ids=None, stream=None):
+    """sets: int32 [N][H_kv][kq]; outputs sized by qas_chunk_groups(); ids:
+    optional execution order [H_kv][N] from qas_regroup_queries."""
     N, H_kv, kq = sets.shape
     _check(_load().qas_union_pages(ctypes.byref(batch), _ptr(q_indptr), N, _ptr(sets), H_kv, kq,
-                               int(group), int(page_size), _ptr(union_pages), _ptr(union_count),
-                               _ptr(membership), _stream(stream)))
+                               int(group), int(page_size), _ptr(ids), _ptr(union_pages),
+                               _ptr(union_count), _ptr(membership), _stream(stream)))
 
 
 def qas_chunk_attention(cache, batch, q_indptr, q_pos, q, sets, group, sm_scale, out, lse=None,
-                        stream=None):
-    """q: bf16 [N][H_q][d]; sets: int32 [N][H_kv][kq]; out like q."""
+                        ids=None, stream=None):
+    """q: bf16 [N][H_q][d]; sets: int32 [N][H_kv][kq]; out like q; ids:
+    optional execution order [H_kv][N] from qas_regroup_queries."""
     N, H_q, _ = q.shape
     _check(_load().qas_chunk_attention(ctypes.byref(cache), ctypes.byref(batch), _ptr(q_indptr), N,
                                    _ptr(q_pos), _ptr(q), dtype_code(q), H_q, _ptr(sets),
-                                   sets.shape[-1], int(group), float(sm_scale), _ptr(out),
-                                   _ptr(lse), _stream(stream)))
+                                   sets.shape[-1], int(group), _ptr(ids), float(sm_scale),
+                                   _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def version():
@@ -238,6 +249,6 @@ def version():
 
 
 __all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
-           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_union_pages",
+           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

@@ -492,13 +492,49 @@ static qas::UnionArgs union_args(const qas_batch* batch, const int32_t* q_indptr
   a.group = group;
   a.S = S;
   a.max_groups = qas_chunk_groups(num_queries, batch->batch, group);
+  a.N = num_queries;
+  a.ids = nullptr;
   return a;
+}
+
+qas_status qas_regroup_queries(const qas_batch* batch, const int32_t* q_indptr,
+                               int32_t num_queries, const int32_t* sets, int32_t num_kv_heads,
+                               int32_t kq, int32_t page_size, int32_t window, int32_t group,
+                               int32_t* ids, void* stream) {
+  qas_status st = check_batch(batch);
+  if (st) return st;
+  if (!q_indptr || !sets || !ids) return fail(QAS_ERR_NULL, "q_indptr / sets / ids is NULL");
+  if (num_queries < 1) return fail(QAS_ERR_SHAPE, "num_queries %d < 1", num_queries);
+  if (num_kv_heads < 1 || kq < 1 || page_size < 1)
+    return fail(QAS_ERR_SHAPE, "num_kv_heads %d / kq %d / page_size %d", num_kv_heads, kq,
+                page_size);
+  if (group < 1 || group > 8 || window < 1 || window > qas::regroup_max_window() ||
+      window % group != 0)
+    return fail(QAS_ERR_SHAPE, "window %d must be a multiple of group %d (1..8), at most %d",
+                window, group, qas::regroup_max_window());
+  qas::RegroupArgs a;
+  a.seq_lens = batch->seq_lens;
+  a.page_indptr = batch->page_indptr;
+  a.q_indptr = q_indptr;
+  a.sets = sets;
+  a.ids = ids;
+  a.B = batch->batch;
+  a.N = num_queries;
+  a.H_kv = num_kv_heads;
+  a.kq = kq;
+  a.S = page_size;
+  a.window = window;
+  a.group = group;
+  a.max_windows = (num_queries + window - 1) / window + batch->batch;
+  hipError_t e = qas::launch_regroup(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "regroup launch");
+  return ok();
 }
 
 qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr, int32_t num_queries,
                            const int32_t* sets, int32_t num_kv_heads, int32_t kq, int32_t group,
-                           int32_t page_size, int32_t* union_pages, int32_t* union_count,
-                           uint8_t* membership, void* stream) {
+                           int32_t page_size, const int32_t* ids, int32_t* union_pages,
+                           int32_t* union_count, uint8_t* membership, void* stream) {
   qas_status st = check_chunk(batch, q_indptr, num_queries, sets, num_kv_heads, kq, group,
                               page_size);
   if (st) return st;
@@ -509,6 +545,7 @@ qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr, int3
   a.union_out = union_pages;
   a.count_out = union_count;
   a.member_out = membership;
+  a.ids = ids;
   hipError_t e = qas::launch_union_prep(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "union prep launch");
   return ok();
@@ -517,8 +554,9 @@ qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr, int3
 qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
                                const int32_t* q_indptr, int32_t num_queries, const int32_t* q_pos,
                                const void* q, int32_t q_dtype, int32_t num_q_heads,
-                               const int32_t* sets, int32_t kq, int32_t group, float sm_scale,
-                               void* out, float* lse, void* stream) {
+                               const int32_t* sets, int32_t kq, int32_t group,
+                               const int32_t* ids, float sm_scale, void* out, float* lse,
+                               void* stream) {
   if (!cache) return fail(QAS_ERR_NULL, "cache is NULL");
   qas_status st = check_chunk(batch, q_indptr, num_queries, sets, cache->num_kv_heads, kq, group,
                               cache->page_size);
@@ -549,6 +587,7 @@ qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
   a.H_q = num_q_heads;
   a.g = g;
   a.sm_scale = sm_scale;
+  a.ids = ids;
   hipError_t e = qas::launch_union_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "union attention launch");
   return ok();

@@ -111,6 +111,8 @@ struct UnionArgs {
   int32_t* union_out;        // union prep only: [groups][H_kv][group * kq]
   int32_t* count_out;        //                  [groups][H_kv]
   unsigned char* member_out; //                  [groups][H_kv][group * kq]
+  const int32_t* ids;        // [H_kv][N] execution order per KV head, NULL = identity
+  int N;
   int B, H_kv, H_q, g, S, kq, group, max_groups;
   float sm_scale;
 };
@@ -118,5 +120,17 @@ hipError_t launch_union_attn(const UnionArgs& a, hipStream_t s);
 hipError_t launch_union_prep(const UnionArgs& a, hipStream_t s);
 bool union_supported(int kv_dtype, int q_dtype, int d, int S, int g, int group, int kq);
 int union_max_pages();
+
+struct RegroupArgs {
+  const int32_t* seq_lens;
+  const int32_t* page_indptr;
+  const int32_t* q_indptr;   // [B+1]
+  const int32_t* sets;       // [N][H_kv][kq]
+  int32_t* ids;              // [H_kv][N] out: original query of each slot
+  int B, N, H_kv, kq, S, window, group, max_windows;
+};
+hipError_t launch_regroup(const RegroupArgs& a, hipStream_t s);
+int regroup_max_pages();      // bitmap capacity; longer requests keep their order
+int regroup_max_window();
 
 }  // namespace qas

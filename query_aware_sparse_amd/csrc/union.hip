@@ -48,6 +48,7 @@ struct UnionShared {
   int uphys[kUMaxUnion];
   unsigned char umask[kUMaxUnion];
   int cpos[kUMaxGroup];
+  int qid[kUMaxGroup];       // original query of each execution slot
   int wave_tot[kUWaves];
   int count;
 };
@@ -108,13 +109,20 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   const int tid = threadIdx.x;
   const int words = (n_pages + 31) / 32;
   for (int i = tid; i < kUMaxGroup * words; i += kUThreads) sh.bm[i / words][i % words] = 0;
-  // causal limits (the union preparation alone has none)
-  if (tid < kUMaxGroup) sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[gr.q0 + tid] : -1;
+  // the original query of every slot (an execution order from the regroup,
+  // else the identity) and its causal limit (the union preparation alone has
+  // none)
+  if (tid < kUMaxGroup) {
+    const int slot = gr.q0 + (tid < gr.nq ? tid : 0);
+    const int qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
+    sh.qid[tid] = qid;
+    sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[qid] : -1;
+  }
   __syncthreads();
   const int entries = gr.nq * a.kq;
   for (int e = tid; e < entries; e += kUThreads) {
     const int i = e / a.kq;
-    const int id = a.sets[((size_t)(gr.q0 + i) * a.H_kv + h) * a.kq + (e - i * a.kq)];
+    const int id = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
     if (id >= 0 && id < n_pages) atomicOr(&sh.bm[i][id >> 5], 1u << (id & 31));
   }
   __syncthreads();
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row
   float qf[64];
   {
-    const size_t qbase = ((size_t)(gr.q0 + (row_ok ? qi : 0)) * a.H_q + h * G + hq) * kUD;
+    const size_t qbase = ((size_t)sh.qid[row_ok ? qi : 0] * a.H_q + h * G + hq) * kUD;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
 
   // ---- outputs at the queries' own rows ----------------------------------------
   if (wave == 0 && row_ok) {
-    const size_t orow = (size_t)(gr.q0 + qi) * a.H_q + h * G + hq;
+    const size_t orow = (size_t)sh.qid[qi] * a.H_q + h * G + hq;
     const float oscale = l_run > 0.f ? a.v_scale[h] / (256.f * l_run) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

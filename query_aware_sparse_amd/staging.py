@@ -107,6 +107,7 @@ class ChunkBatch:
     def __init__(self, cases, device="cuda"):
         c0 = cases[0]
         H, S, d = c0.H_kv, c0.S, c0.d
+        self.S = S
         pool = sum(c.num_pool_pages for c in cases)
         shape = (pool, H, S, d)
         self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)   # e4m3 NaN

@@ -127,3 +127,138 @@ def test_chunk_attention_full_size(qas):
                     + [0, 7, 8, 511]))
     _check(case, got, lse, qs)
     assert np.all(np.isfinite(got))
+
+
+# ------------------------------------------------------------- regroup ----
+
+REGROUP_CAPACITY = 1024     # pages a request may have and still be regrouped
+
+
+def _shuffled(case, seed):
+    """Move the queries' sets around (per KV head) so that neighbours no longer
+    share pages and the regroup has something to find."""
+    rng = np.random.default_rng(seed)
+    sets = case.sets.copy()
+    for h in range(case.H_kv):
+        sets[:, h, :] = sets[rng.permutation(case.N), h, :]
+    case.sets = sets
+    return case
+
+
+def _regroup_ref(cases, window, group):
+    """Oracle execution order [H_kv][N] over the requests of a ChunkBatch."""
+    sets = np.concatenate([c.sets for c in cases])
+    q_indptr = np.concatenate([[0], np.cumsum([c.N for c in cases])])
+    n_pages = [-(-c.L // c.S) for c in cases]
+    H = cases[0].H_kv
+    return np.array([quest.regroup(sets[:, h, :], n_pages, q_indptr, window, group,
+                                   REGROUP_CAPACITY) for h in range(H)])
+
+
+def _regroup(qas, cb, window, group):
+    ids = torch.full((cb.sets.shape[1], cb.N), -1, dtype=torch.int32, device="cuda")
+    qas.qas_regroup_queries(cb.db.batch, cb.q_indptr, cb.sets, cb.S, window, group,
+                            ids)
+    torch.cuda.synchronize()
+    return ids
+
+
+@pytest.mark.parametrize("window,group", [(64, 8), (16, 4), (128, 8), (24, 8), (8, 8), (6, 2)])
+def test_regroup_matches_oracle(qas, window, group):
+    """Execution order equal to the oracle's for every KV head, on the
+    chunk's own sets and on shuffled ones, with duplicates and invalid IDs."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    for variant, case in (("natural", _corrupt(multiquery_chunk(L=8192, N=61), 3)),
+                          ("shuffled", _shuffled(_corrupt(multiquery_chunk(L=8192, N=61), 4), 5))):
+        say(f"[regroup] {variant} W={window} g={group}")
+        cb = ChunkBatch([case])
+        ids = _regroup(qas, cb, window, group).cpu().numpy()
+        assert np.array_equal(ids, _regroup_ref([case], window, group)), variant
+
+
+def test_regroup_two_requests_and_identity_beyond_capacity(qas):
+    """Windows stay inside their request; a request of more than 1024 pages
+    keeps its order."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    a = _shuffled(multiquery_chunk(seed=41, L=6000, S=32, N=21, kq=40, keep=28), 6)
+    b = _shuffled(multiquery_chunk(seed=42, L=33000, S=32, N=13, kq=40, keep=28,
+                                   scales=(a.k_scale, a.v_scale)), 7)
+    assert -(-b.L // b.S) > REGROUP_CAPACITY
+    cb = ChunkBatch([a, b])
+    ids = _regroup(qas, cb, 16, 4).cpu().numpy()
+    ref = _regroup_ref([a, b], 16, 4)
+    assert np.array_equal(ids, ref)
+    assert np.all(ids[:, a.N:] == np.arange(a.N, a.N + b.N))
+    assert not np.array_equal(ids[:, :a.N], np.tile(np.arange(a.N), (a.H_kv, 1)))
+
+
+def test_union_pages_through_regroup(qas):
+    """Union lists and membership of the regrouped groups: group g of head h
+    is the queries ids[h][8g : 8g + 8]."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    case = _shuffled(_corrupt(multiquery_chunk(L=8192, N=61), 8), 9)
+    cb = ChunkBatch([case])
+    ids = _regroup(qas, cb, 64, case.group)
+    G = qas.qas_chunk_groups(cb.N, 1, case.group)
+    cap = case.group * case.kq
+    ul = torch.full((G, case.H_kv, cap), -9, dtype=torch.int32, device="cuda")
+    uc = torch.full((G, case.H_kv), -9, dtype=torch.int32, device="cuda")
+    um = torch.zeros((G, case.H_kv, cap), dtype=torch.uint8, device="cuda")
+    qas.qas_union_pages(cb.db.batch, cb.q_indptr, cb.sets, case.group, case.S, ul, uc, um,
+                        ids=ids)
+    torch.cuda.synchronize()
+    ids, ul, uc, um = ids.cpu().numpy(), ul.cpu().numpy(), uc.cpu().numpy(), um.cpu().numpy()
+    P = -(-case.L // case.S)
+    total_regrouped = total_plain = 0
+    for gi in range(-(-case.N // case.group)):
+        for h in range(case.H_kv):
+            slots = range(gi * case.group, min(case.N, (gi + 1) * case.group))
+            valid = [[int(p) for p in case.sets[ids[h, s], h] if 0 <= p < P] for s in slots]
+            union, member = quest.union_with_membership(valid)
+            U = len(union)
+            assert uc[gi, h] == U and ul[gi, h, :U].tolist() == union
+            bits = np.zeros(U, dtype=np.int64)
+            for i in range(len(valid)):
+                bits |= member[i].astype(np.int64) << i
+            assert np.array_equal(um[gi, h, :U], bits)
+            total_regrouped += U
+            plain = [[int(p) for p in case.sets[s, h] if 0 <= p < P] for s in slots]
+            total_plain += len(quest.union_with_membership(plain)[0])
+    say(f"[regroup] union pages: original order {total_plain}, regrouped {total_regrouped}")
+    assert total_regrouped < total_plain
+
+
+def test_chunk_attention_through_regroup(qas):
+    """Every query executed through a regrouped order still matches the oracle
+    (support and causal limit follow the original query)."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    case = _shuffled(_corrupt(multiquery_chunk(L=8192, N=61), 10), 11)
+    cb = ChunkBatch([case])
+    ids = _regroup(qas, cb, 64, case.group)
+    out = torch.full((cb.N, cb.q.shape[1], cb.q.shape[2]), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((cb.N, cb.q.shape[1]), float("nan"), device="cuda")
+    qas.qas_chunk_attention(cb.cache, cb.db.batch, cb.q_indptr, cb.q_pos, cb.q, cb.sets,
+                            cb.group, 1.0 / np.sqrt(cb.q.shape[2]), out, lse, ids=ids)
+    torch.cuda.synchronize()
+    _check(case, out_to_numpy(out), lse.cpu().numpy().astype(np.float64), list(range(case.N)))
+
+
+def test_chunk_attention_full_size_regrouped(qas):
+    """The 64K-context 512-query chunk through the W=64 regroup, sampled."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    case = multiquery_chunk()
+    cb = ChunkBatch([case])
+    ids = _regroup(qas, cb, 64, case.group)
+    assert np.array_equal(ids.cpu().numpy(), _regroup_ref([case], 64, case.group))
+    out = torch.full((cb.N, cb.q.shape[1], cb.q.shape[2]), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((cb.N, cb.q.shape[1]), float("nan"), device="cuda")
+    qas.qas_chunk_attention(cb.cache, cb.db.batch, cb.q_indptr, cb.q_pos, cb.q, cb.sets,
+                            cb.group, 1.0 / np.sqrt(case.d), out, lse, ids=ids)
+    torch.cuda.synchronize()
+    got = out_to_numpy(out)
+    qs = sorted(set(np.random.default_rng(12).choice(case.N, 16, replace=False).tolist()
+                    + [0, 511]))
+    _check(case, got, lse.cpu().numpy().astype(np.float64), qs)
+    assert np.all(np.isfinite(got))
