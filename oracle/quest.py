@@ -33,6 +33,8 @@ import math
 
 import numpy as np
 
+from .formats import decode_e4m3fn
+
 
 # ---------------------------------------------------------------- pages ----
 
@@ -110,6 +112,70 @@ def kv_head_scores(U_heads, H_kv):
     for h in range(H_kv):
         out[h] = U_heads[h * g:(h + 1) * g].max(axis=0)
     return out
+
+
+# ------------------------------------------------- fp8 page summaries -----
+#
+# [Quest] §3 (summary dtype): an FP8 summary saves scan bytes but must stay
+# an outer interval: the min is quantised toward -inf and the max toward
+# +inf, so the bound of eq. (2)-(3) over the stored box is still >= every
+# dot product in the page (eq. (4) kept), at the cost of more false
+# positives.  Reading taken here: OCP e4m3fn codes with one power-of-two
+# scale per (page, KV head), the smallest 2^k with max |m|, |M| <= 448 * 2^k,
+# so that scaling is exact and the rounding direction is decided once, on
+# the code.
+
+def _e4m3_finite_values():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = decode_e4m3fn(codes)
+    return np.unique(vals[np.isfinite(vals)])          # sorted, -0 == +0
+
+
+E4M3_MAX = 448.0
+
+
+def e4m3_down(x):
+    """Largest finite e4m3 value <= x (x >= -448), from the value table."""
+    vals = _e4m3_finite_values()
+    return float(vals[np.searchsorted(vals, x, side="right") - 1])
+
+
+def e4m3_up(x):
+    """Smallest finite e4m3 value >= x (x <= 448), from the value table."""
+    vals = _e4m3_finite_values()
+    return float(vals[np.searchsorted(vals, x, side="left")])
+
+
+def summary_scale_exponent(amax):
+    """Smallest integer k with amax <= 448 * 2^k (k = 0 for amax = 0)."""
+    if amax == 0:
+        return 0
+    k = 0
+    while E4M3_MAX * 2.0 ** k < amax:
+        k += 1
+    while E4M3_MAX * 2.0 ** (k - 1) >= amax:
+        k -= 1
+    return k
+
+
+def fp8_summaries(m, M):
+    """Outward-quantised copy of summaries m, M ([P][H][d]): per (page, head)
+    the scale s = 2^k of summary_scale_exponent(max |m|, |M|), then
+    m_hat = s * e4m3_down(m / s) <= m and M_hat = s * e4m3_up(M / s) >= M.
+    Returns (m_hat, M_hat, s [P][H])."""
+    P, H, d = m.shape
+    m_hat = np.zeros_like(m, dtype=np.float64)
+    M_hat = np.zeros_like(M, dtype=np.float64)
+    scale = np.ones((P, H))
+    for p in range(P):
+        for h in range(H):
+            amax = max(np.abs(m[p, h]).max(), np.abs(M[p, h]).max())
+            s = 2.0 ** summary_scale_exponent(amax)
+            scale[p, h] = s
+            for j in range(d):
+                m_hat[p, h, j] = s * e4m3_down(m[p, h, j] / s)
+                M_hat[p, h, j] = s * e4m3_up(M[p, h, j] / s)
+    return m_hat, M_hat, scale
 
 
 # ---------------------------------------------------------------- top-K ----

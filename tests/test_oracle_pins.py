@@ -343,6 +343,52 @@ def test_mixed_pages_union_bruteforce():
         assert quest.mixed_pages(s, K, L, S, 0, 0) == quest.top_k_pages(s, K)
 
 
+# ------------------------------------------------------- fp8 summaries ----
+
+def test_e4m3_directed_rounding_by_hand():
+    """e4m3fn (3 fraction bits, bias 7, subnormal step 2^-9): 0.3 = 1.2 * 2^-2
+    lies between 1.125 * 2^-2 and 1.25 * 2^-2."""
+    assert quest.e4m3_down(0.3) == 0.28125 and quest.e4m3_up(0.3) == 0.3125
+    assert quest.e4m3_down(-0.3) == -0.3125 and quest.e4m3_up(-0.3) == -0.28125
+    for x in (0.0, 1.0, -1.0, 448.0, -448.0, 2.0 ** -9, 0.875 * 2.0 ** -6, 240.0):
+        assert quest.e4m3_down(x) == x and quest.e4m3_up(x) == x
+    assert quest.e4m3_down(1e-4) == 0.0 and quest.e4m3_up(1e-4) == 2.0 ** -9
+    assert quest.e4m3_down(-1e-4) == -(2.0 ** -9) and quest.e4m3_up(-1e-4) == 0.0
+    assert quest.e4m3_down(447.0) == 416.0 and quest.e4m3_up(417.0) == 448.0
+
+
+def test_summary_scale_is_the_smallest_power_of_two():
+    e = quest.summary_scale_exponent
+    assert e(0.0) == 0 and e(448.0) == 0 and e(448.0001) == 1
+    assert e(224.0) == -1 and e(224.5) == 0 and e(1.0) == -8 and e(1.75) == -8
+    assert e(1.7500001) == -7 and e(65504.0) == 8
+
+
+def test_fp8_summaries_are_outer_bounds():
+    """[Quest] §3: min toward -inf, max toward +inf keeps eq. (4); each
+    bound moves by at most one e4m3 step (1/8 of its magnitude, or the
+    subnormal step 2^-9 * s near zero)."""
+    rng = _rng(41)
+    for _ in range(20):
+        S, d = 8, 16
+        keys = rng.standard_normal((40, 3, d)) * rng.choice([1e-3, 1.0, 300.0])
+        keys = keys.astype(np.float16).astype(np.float64)
+        m, M = quest.page_summaries(keys, 40, S)
+        mh, Mh, s = quest.fp8_summaries(m, M)
+        assert np.all(mh <= m) and np.all(Mh >= M)
+        step = np.maximum(np.abs(np.stack([m, M])) / 8, 2.0 ** -9 * s[None, :, :, None])
+        assert np.all(m - mh <= step[0]) and np.all(Mh - M <= step[1])
+        assert np.all(np.maximum(np.abs(mh), np.abs(Mh)) <= 448 * s[:, :, None])
+        q = rng.standard_normal((3, d))
+        U = quest.head_bounds(q, m, M)
+        U8 = quest.head_bounds(q, mh, Mh)
+        assert np.all(U8 >= U - 1e-9)
+        for h in range(3):
+            for p in range(len(m)):
+                toks = keys[p * S:(p + 1) * S, h]
+                assert U8[h, p] >= (toks @ q[h]).max() - 1e-9
+
+
 # ------------------------------------------------------------- attention ----
 
 def _sdpa(q, k, v, scale):
