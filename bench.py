@@ -315,6 +315,45 @@ def bench_chunk(args):
     print(json.dumps(result), flush=True)
 
 
+def time_decode_calls(torch, args, NL, call, out):
+    """Eager warm-up, one pass over the layers captured in a HIP graph and
+    replayed; the graph's outputs must equal the eager ones.  Returns (wall
+    ms per call, event-timed us per call, calls timed)."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for w in range(max(NL, args.warmup)):
+            call(w % NL)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(NL):
+            call(i)
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup // NL)):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager_out):
+        raise RuntimeError("graph replay differs from the eager calls")
+    reps = max(1, math.ceil(args.steps / NL))
+    steps = reps * NL
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    replay_stream = torch.cuda.current_stream()   # graph.replay() launches here
+    for e0, e1 in evs:
+        e0.record(replay_stream)
+        graph.replay()
+        e1.record(replay_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL
+    return wall * 1e3 / steps, call_us, steps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -355,17 +394,23 @@ def main():
     log(f"[bench] workload {case.name}: L={L} P={L // case.S} K={case.K} "
         f"H={case.H_q}x{case.d} layers={NL}")
 
-    # layer 0 filled through the library's append; other layers are copies
-    base = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+    # layer 0 filled through the library's append (exact summaries and their
+    # e4m3 copy); other layers are copies.  The line's value uses the exact
+    # summaries; the e4m3-copy variant is reported beside it.
+    base = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype,
+                      fp8_summaries=True)
     db = prefill(base, case)
     layers = [base]
     for _ in range(1, NL):
         pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype,
-                        poison=False)
+                        poison=False, fp8_summaries=True)
         pc.k_pool.copy_(base.k_pool)
         pc.v_pool.copy_(base.v_pool)
         pc.summary.copy_(base.summary)
+        pc.summary_fp8.copy_(base.summary_fp8)
+        pc.summary_fp8_scale.copy_(base.summary_fp8_scale)
         layers.append(pc)
+    exact = [qas.make_cache(pc.k_pool, pc.v_pool, pc.summary) for pc in layers]
     qs = to_device(layer_queries(case, NL), case.q_dtype)          # [NL][1][H][d]
     k_new = to_device(case.keys[0][L - 1:L], case.kv_dtype)      # current token
     v_new = to_device(case.values[0][L - 1:L], case.kv_dtype)
@@ -376,44 +421,21 @@ def main():
     torch.cuda.synchronize()
 
     def call(i):
+        qas.qas_decode_layer(exact[i], db.batch, qs[i], case.K, case.sm_scale,
+                             out[i], lse[i], ws, k_new=k_new, v_new=v_new)
+
+    def call_fp8(i):
         qas.qas_decode_layer(layers[i].cache, db.batch, qs[i], case.K, case.sm_scale,
                              out[i], lse[i], ws, k_new=k_new, v_new=v_new)
 
-    # eager warm-up, then capture one pass over the layers into a graph
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        for w in range(max(NL, args.warmup)):
-            call(w % NL)
-    torch.cuda.current_stream().wait_stream(stream)
-    torch.cuda.synchronize()
-    eager_out = out.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(NL):
-            call(i)
-    torch.cuda.synchronize()
-    for _ in range(max(1, args.warmup // NL)):
-        graph.replay()
-    torch.cuda.synchronize()
-    if not torch.equal(out, eager_out):
-        raise RuntimeError("graph replay differs from the eager calls")
-
-    reps = max(1, math.ceil(args.steps / NL))
-    steps = reps * NL
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    replay_stream = torch.cuda.current_stream()   # graph.replay() launches here
-    for e0, e1 in evs:
-        e0.record(replay_stream)
-        graph.replay()
-        e1.record(replay_stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / steps
-    call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL
+    ms_per_step, call_us, steps = time_decode_calls(torch, args, NL, call, out)
+    ms_fp8, us_fp8, _ = time_decode_calls(torch, args, NL, call_fp8, out)
+    bytes_fp8 = traffic.decode_layer_bytes(
+        B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
+        pages_scanned=L // case.S, page_heads_selected=case.H_kv * case.K,
+        append_tokens=1, fp8_summaries=True)["total"]
+    log(f"[bench] e4m3 summary copy: {us_fp8:.2f} us/call (events), "
+        f"{bytes_fp8 / (us_fp8 * 1e-6) / 1e9:.1f} GB/s on {bytes_fp8} B")
 
     nbytes = traffic.decode_layer_bytes(
         B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
@@ -436,7 +458,11 @@ def main():
                    "pages": L // case.S, "top_k_pages": case.K, "kv_dtype": "f16",
                    "layer_caches": NL, "append_current_token": True,
                    "hip_graph": True, "us_per_call": round(ms_per_step * 1e3, 3),
-                   "bytes_per_call": total, "bytes_parts": nbytes},
+                   "bytes_per_call": total, "bytes_parts": nbytes,
+                   "fp8_summary_copy": {
+                       "us_per_call": round(us_fp8, 3), "bytes_per_call": bytes_fp8,
+                       "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
+                       "ms_per_step_wall": round(ms_fp8, 6)}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic_bytes(),

@@ -82,6 +82,18 @@ typedef struct qas_cache {
   void* summary;          /* device [num_pool_pages][H_kv][2][d]              */
   const float* k_scale;   /* device [H_kv] dequantisation scales (fp8 only, else NULL) */
   const float* v_scale;   /* device [H_kv]                                    */
+  /* Optional e4m3 copy of the summaries ([Quest] §3, summary dtype; NULL
+   * for none): codes [num_pool_pages][H_kv][2][d] and one scale per
+   * (page, KV head) [num_pool_pages][H_kv] float, the smallest power of two
+   * 2^k with max |m|, |M| <= 448 * 2^k; min codes round toward -inf and max
+   * codes toward +inf, so the copy is an outer interval of the exact record.
+   * When given, qas_append and the decode-layer append keep it current next
+   * to the exact summary, and page scores (qas_score_pages, the decode
+   * layer) are taken from it: half the scan bytes, a bound that is still
+   * >= every dot product of the page, and a looser one (more false
+   * positives) than the exact summary's. */
+  void* summary_fp8;
+  float* summary_fp8_scale;
 } qas_cache;
 
 /* A batch of B requests (ragged, [Quest] §2.1 continuous batching). */

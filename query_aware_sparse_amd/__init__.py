@@ -36,7 +36,8 @@ class qas_cache(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("summary", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
-                ("v_scale", ctypes.c_void_p)]
+                ("v_scale", ctypes.c_void_p), ("summary_fp8", ctypes.c_void_p),
+                ("summary_fp8_scale", ctypes.c_void_p)]
 
 
 class qas_batch(ctypes.Structure):
@@ -118,15 +119,20 @@ def dtype_code(t):
     return _TORCH_DTYPE[t.dtype]
 
 
-def make_cache(k_pool, v_pool, summary, k_scale=None, v_scale=None):
+def make_cache(k_pool, v_pool, summary, k_scale=None, v_scale=None, summary_fp8=None,
+               summary_fp8_scale=None):
     """qas_cache over caller-owned tensors: pools [pages][H_kv][S][d],
-    summary [pages][H_kv][2][d].  The tensors must outlive every call."""
+    summary [pages][H_kv][2][d], optional e4m3 summary copy (uint8 codes
+    [pages][H_kv][2][d] and float scales [pages][H_kv]).  The tensors must
+    outlive every call."""
     pages, H_kv, S, d = k_pool.shape
     c = qas_cache(S, d, H_kv, pages, dtype_code(k_pool), 0, k_pool.data_ptr(),
                   v_pool.data_ptr(), 0 if summary is None else summary.data_ptr(),
                   0 if k_scale is None else k_scale.data_ptr(),
-                  0 if v_scale is None else v_scale.data_ptr())
-    c._keep = (k_pool, v_pool, summary, k_scale, v_scale)
+                  0 if v_scale is None else v_scale.data_ptr(),
+                  0 if summary_fp8 is None else summary_fp8.data_ptr(),
+                  0 if summary_fp8_scale is None else summary_fp8_scale.data_ptr())
+    c._keep = (k_pool, v_pool, summary, k_scale, v_scale, summary_fp8, summary_fp8_scale)
     return c
 
 

@@ -4,6 +4,12 @@
 // max = -inf / min = +inf, so a recycled physical page never keeps stale
 // extremes (§3, page recycling).
 //
+// With an fp8 summary copy (the Quest page, §3 on the summary dtype), each
+// written record is also stored as e4m3 codes with one power-of-two scale per
+// (page, KV head): the smallest 2^k with max |m|, |M| <= 448 * 2^k, the min
+// rounded toward -inf and the max toward +inf, so the copy stays an outer
+// interval of the exact record.
+//
 // One workgroup per (page touched, KV head, request).  Lanes own 16-byte
 // chunks of a token row (RL lanes per row, TS rows in flight), copy K and V
 // into the pool, reduce min/max over their tokens, then the workgroup
@@ -26,6 +32,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   constexpr int BYTES = DType<DT>::bytes;
   __shared__ float red_min[TS][D];
   __shared__ float red_max[TS][D];
+  __shared__ float red_amax[D];
 
   const int u = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int H = a.H_kv, S = a.S;
@@ -95,7 +102,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     }
     sum[dim] = Store<DT>::from(m);
     sum[D + dim] = Store<DT>::from(M);
+    red_amax[dim] = fmaxf(fabsf(m), fabsf(M));
+    red_min[0][dim] = m;            // this thread's own column: no other reader
+    red_max[0][dim] = M;
   }
+  if (a.summary_fp8 == nullptr) return;
+  __syncthreads();
+  float amax = 0.f;
+  for (int j = 0; j < D; ++j) amax = fmaxf(amax, red_amax[j]);
+  const int k = summary_scale_exponent(amax);
+  unsigned char* codes = reinterpret_cast<unsigned char*>(a.summary_fp8) + (phys * H + h) * 2 * D;
+  for (int dim = tid; dim < D; dim += kAppendThreads) {
+    codes[dim] = (unsigned char)e4m3_down(ldexpf(red_min[0][dim], -k));
+    codes[D + dim] = (unsigned char)e4m3_up(ldexpf(red_max[0][dim], -k));
+  }
+  if (tid == 0) a.summary_fp8_scale[phys * H + h] = ldexpf(1.f, k);
 }
 
 template <int DT, int D>

@@ -39,7 +39,7 @@ namespace qas {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
 // token groups in flight per wave (bounded by registers)
-template <int G> constexpr int dec_unroll() { return G <= 2 ? 16 : 8; }
+template <int G> constexpr int dec_unroll() { return G <= 2 ? 16 : G <= 4 ? 8 : 4; }
 constexpr int kDecMaxList = 1024;      // selected entries per split
 constexpr int kDecMaxRow = 4096;       // entries of a row when deduplicating
 constexpr int kDecFusedTopkPT = 16;    // in-kernel top-K: scores per thread at most
@@ -218,23 +218,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   for (int u0 = wave; u0 < units; u0 += kDecWaves * UNR) {
     uint4 kr[UNR], vr[UNR];
     bool ok[UNR];
+    // Every load is unconditional: a unit past the end is clamped to the last
+    // unit and a token row past the page's tokens to the page's last row, so
+    // each address stays inside an allocated page, and `ok` drops the value.
+    // (A load under a branch makes the compiler wait for every earlier load
+    // before it.)  All K loads go first, so the logits start while V is still
+    // in flight.
+    size_t offs[UNR];
 #pragma unroll
     for (int b = 0; b < UNR; ++b) {
-      const int u = u0 + b * kDecWaves;
-      kr[b] = make_uint4(0, 0, 0, 0);
-      vr[b] = make_uint4(0, 0, 0, 0);
-      ok[b] = false;
-      if (u < units) {
-        const int pi = u / NI, gi = u - (u / NI) * NI;
-        const int tip = gi * TPI + trow;
-        ok[b] = tip < s_ntok[pi];
-        if (ok[b]) {
-          const size_t off = ((((size_t)s_phys[pi] * H + h) * S + tip) * D) * BYTES + c * 16;
-          kr[b] = load16(kbase + off);
-          vr[b] = load16(vbase + off);
-        }
-      }
+      const int u = min(u0 + b * kDecWaves, units - 1);
+      const int pi = u / NI, gi = u - (u / NI) * NI;
+      const int tip = gi * TPI + trow;
+      ok[b] = (u0 + b * kDecWaves < units) & (tip < s_ntok[pi]);
+      offs[b] = ((((size_t)s_phys[pi] * H + h) * S + min(tip, S - 1)) * D) * BYTES + c * 16;
     }
+#pragma unroll
+    for (int b = 0; b < UNR; ++b) kr[b] = load16(kbase + offs[b]);
+#pragma unroll
+    for (int b = 0; b < UNR; ++b) vr[b] = load16(vbase + offs[b]);
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       float z[UNR];
@@ -250,17 +252,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
         z[b] = ok[b] ? dot : -INFINITY;
         zmax = fmaxf(zmax, z[b]);
       }
-      if (zmax == -INFINITY) continue;
-      const float alpha = fast_exp2(m_run[gg] - zmax);
+      // No branch on the batch's content: a branch here lets the compiler
+      // sink the V loads below the logits, a second round trip per batch.
+      // With no valid logit yet the stand-in maximum 0 gives alpha = 0 and
+      // p = 0 on a zero state; rows not loaded read as zero words.
+      const float zm = zmax == -INFINITY ? 0.f : zmax;
+      const float alpha = fast_exp2(m_run[gg] - zm);
       float l = l_run[gg] * alpha;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[gg][e] *= alpha;
 #pragma unroll
       for (int b = 0; b < UNR; ++b) {
-        if (!ok[b]) continue;
-        const float p = fast_exp2(z[b] - zmax);
+        const float p = ok[b] ? fast_exp2(z[b] - zm) : 0.f;
+        const uint4 w = ok[b] ? vr[b] : make_uint4(0, 0, 0, 0);
         float vf[EPL];
-        unpack16<DT>(vr[b], vf);
+        unpack16<DT>(w, vf);
         l += p;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[gg][e] += p * vf[e];

@@ -49,6 +49,13 @@ qas_status check_cache(const qas_cache* c, bool need_pools, bool need_summary) {
                 c->kv_dtype);
   if (need_pools && (!c->k_pool || !c->v_pool)) return fail(QAS_ERR_NULL, "k_pool/v_pool is NULL");
   if (need_summary && !c->summary) return fail(QAS_ERR_NULL, "summary is NULL");
+  if ((c->summary_fp8 == nullptr) != (c->summary_fp8_scale == nullptr))
+    return fail(QAS_ERR_NULL, "summary_fp8 and summary_fp8_scale must both be given or NULL");
+  if (c->summary_fp8 && !qas::score8_supported(c->head_dim, c->num_kv_heads))
+    return fail(QAS_ERR_UNSUPPORTED, "fp8 summaries: %d KV heads of d=%d exceed 512 lanes",
+                c->num_kv_heads, c->head_dim);
+  if (c->summary_fp8 && !c->summary)
+    return fail(QAS_ERR_NULL, "an fp8 summary copy needs the exact summary");
   return QAS_OK;
 }
 
@@ -131,7 +138,11 @@ qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q,
   a.max_pages = b->max_pages;
   a.kv_dtype = c->kv_dtype;
   a.g = g;
-  a.pages_per_iter = qas::score_pages_per_iter(c->kv_dtype, c->head_dim, c->num_kv_heads);
+  a.summary_fp8 = c->summary_fp8;
+  a.summary_fp8_scale = c->summary_fp8_scale;
+  a.pages_per_iter = c->summary_fp8
+                         ? qas::score8_pages_per_iter(c->head_dim, c->num_kv_heads)
+                         : qas::score_pages_per_iter(c->kv_dtype, c->head_dim, c->num_kv_heads);
   a.tickets = nullptr;
   a.row_stride = 0;
   return a;
@@ -194,6 +205,8 @@ qas::AppendArgs append_args(const qas_cache* c, const qas_batch* b, const int32_
   a.S = c->page_size;
   a.kv_dtype = c->kv_dtype;
   a.max_new = max_new;
+  a.summary_fp8 = c->summary_fp8;
+  a.summary_fp8_scale = c->summary_fp8_scale;
   return a;
 }
 

@@ -152,4 +152,39 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- e4m3 (OCP fn) codes with a chosen rounding direction ----------------
+// Codes are sign-magnitude: for a non-negative code one step up in value is
+// code + 1; for a negative code (bit 7) it is code - 1.  -0 (0x80) and +0
+// both mean zero.
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+}
+
+// nearest-even code of x, |x| <= 448 (the conversion would not saturate)
+__device__ __forceinline__ uint32_t e4m3_nearest(float x) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xffu;
+}
+
+// largest e4m3 value <= x and smallest e4m3 value >= x, for |x| <= 448
+__device__ __forceinline__ uint32_t e4m3_down(float x) {
+  uint32_t c = e4m3_nearest(x);
+  if (e4m3_value(c) > x) c = (c & 0x80u) ? c + 1u : (c == 0u ? 0x81u : c - 1u);
+  return c;
+}
+__device__ __forceinline__ uint32_t e4m3_up(float x) {
+  uint32_t c = e4m3_nearest(x);
+  if (e4m3_value(c) < x) c = (c & 0x80u) ? (c == 0x80u ? 0x01u : c - 1u) : c + 1u;
+  return c;
+}
+
+// Smallest k with amax <= 448 * 2^k (0 for amax = 0): with amax = f * 2^e,
+// f in [0.5, 1), 448 = 0.875 * 2^9 gives k = e - 9, or e - 8 if f > 0.875.
+__device__ __forceinline__ int summary_scale_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  const float f = frexpf(amax, &e);
+  return e - 9 + (f > 0.875f ? 1 : 0);
+}
+
 }  // namespace qas

@@ -25,10 +25,16 @@ struct ScoreArgs {
   int kv_dtype, g;
   int pages_per_iter;        // pages one workgroup covers per lane step
   unsigned int* tickets;     // optional [B][H_kv] counters zeroed for the attention kernel
+  // optional e4m3 summary copy: scores are taken from it (the append keeps
+  // both the exact record and the copy current)
+  void* summary_fp8;         // [pool][H_kv][2][d] codes
+  float* summary_fp8_scale;  // [pool][H_kv]
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 bool score_supported(int kv_dtype, int d, int g, int H_kv);
 int score_pages_per_iter(int kv_dtype, int d, int H_kv);
+int score8_pages_per_iter(int d, int H_kv);
+bool score8_supported(int d, int H_kv);   // scores from the e4m3 summary copy
 
 struct TopkArgs {
   const float* scores;
@@ -56,6 +62,8 @@ struct AppendArgs {
   const int32_t* new_indptr;   // NULL: one token per request at seq_lens[r]-1
   const int32_t* page_indptr;
   const int32_t* page_indices;
+  void* summary_fp8;         // optional e4m3 copy [pool][H_kv][2][d]
+  float* summary_fp8_scale;  //   and its scale [pool][H_kv]
   int B, H_kv, d, S, kv_dtype;
   int max_new;
 };

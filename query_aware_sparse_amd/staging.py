@@ -38,7 +38,7 @@ class PagedCache:
     method must not touch poisons the result."""
 
     def __init__(self, num_pool_pages, H_kv, S, d, kv_dtype, device="cuda",
-                 poison=True):
+                 poison=True, fp8_summaries=False):
         tdt = TORCH_KV[kv_dtype]
         shape = (num_pool_pages, H_kv, S, d)
         fill = float("nan") if poison else 0.0
@@ -46,9 +46,16 @@ class PagedCache:
         self.v_pool = torch.full(shape, fill, dtype=tdt, device=device)
         self.summary = torch.full((num_pool_pages, H_kv, 2, d), fill, dtype=tdt,
                                   device=device)
+        self.summary_fp8 = self.summary_fp8_scale = None
+        if fp8_summaries:   # e4m3 copy: codes 0x7F (NaN) and NaN scales until written
+            self.summary_fp8 = torch.full((num_pool_pages, H_kv, 2, d), 0x7F, dtype=torch.uint8,
+                                          device=device)
+            self.summary_fp8_scale = torch.full((num_pool_pages, H_kv), fill, device=device)
         self.kv_dtype, self.S, self.H_kv, self.d = kv_dtype, S, H_kv, d
         self.device = device
-        self.cache = make_cache(self.k_pool, self.v_pool, self.summary)
+        self.cache = make_cache(self.k_pool, self.v_pool, self.summary,
+                                summary_fp8=self.summary_fp8,
+                                summary_fp8_scale=self.summary_fp8_scale)
 
 
 class DeviceBatch:
