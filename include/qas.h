@@ -58,7 +58,7 @@ typedef enum qas_status {
   QAS_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree        */
   QAS_ERR_DTYPE = 3,       /* dtype not accepted for this operand             */
   QAS_ERR_UNSUPPORTED = 4, /* valid request outside this build (e.g. head_dim) */
-  QAS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+  QAS_ERR_WORKSPACE = 5,   /* workspace NULL, not 16-byte aligned, too small  */
   QAS_ERR_HIP = 6          /* a HIP runtime call or launch failed             */
 } qas_status;
 
@@ -329,7 +329,9 @@ enum { QAS_OP_SPARSE_DECODE = 1, QAS_OP_DECODE_LAYER = 2 };
 /*
  * qas_workspace_bytes - workspace size an operation needs for these
  * arguments (k = sel_len for QAS_OP_SPARSE_DECODE, the budget for
- * QAS_OP_DECODE_LAYER).  Returns 0 for invalid arguments.
+ * QAS_OP_DECODE_LAYER).  Returns 0 for invalid arguments.  A workspace must
+ * be 16-byte aligned (the decode layer reads its page scores as 16-byte
+ * words); allocations of hipMalloc and torch are.
  */
 size_t qas_workspace_bytes(int32_t op, const qas_cache* cache,
                            const qas_batch* batch, int32_t num_q_heads,

@@ -112,6 +112,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int H = a.H_kv, S = a.S;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // in-kernel top-K: the row's scores and physical pages sit at a fixed
+  // stride (a multiple of 4 entries in a 16-byte aligned workspace), so their
+  // 16-byte loads go out first, before the request's bounds are known
+  TopkRow<(TPT > 0 ? TPT : 4)> t;
+  const int cap = min(a.max_pages, kTkThreads * TPT);   // the host keeps rows within this
+  if constexpr (TPT > 0)
+    t.issue_x4(a.scores + ((size_t)r * H + h) * a.score_stride,
+               a.phys_rows + (size_t)r * a.score_stride, cap);
   const int L = a.seq_lens[r];
   const int pbeg = a.page_indptr[r];
   const int P_r = a.page_indptr[r + 1] - pbeg;
@@ -124,14 +132,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   if constexpr (TPT > 0) {
     // ---- 1. top-K of the row's scores; keep selected positions [e0, e1) ---
     __shared__ TopkShared tsh;
-    // scores of row (r, h) sit at a fixed stride of max_pages, so their loads
-    // do not wait for the request's page-table bounds
-    const int cap = min(a.max_pages, kTkThreads * TPT);   // the host keeps rows within this
-    TopkRow<TPT> t;
-    t.load_scores(a.scores + ((size_t)r * H + h) * a.max_pages, cap);
     const int n_tk = min(n_pages, cap);
     const int take = min(a.k, n_tk);
-    t.load_pages(a.page_indices + pbeg, n_tk);
+    t.finish_x4(cap, n_tk);
     t.set_fixed(L, S, a.sink_tokens, a.local_tokens);
     t.select(take, tsh);
     int count;

@@ -83,7 +83,7 @@ qas_status check_heads(const qas_cache* c, int num_q_heads, int* g) {
 
 // Workspace layout:
 //   sparse decode: [split partials][tickets]
-//   decode layer:  [scores][split partials][tickets], plus [sel][sel_phys]
+//   decode layer:  [scores][physical pages][split partials][tickets], plus [sel][sel_phys]
 //                  for rows too long for the in-kernel top-K
 struct DecodePlan {
   int n_split;
@@ -103,9 +103,22 @@ DecodePlan plan_decode(const qas_cache* c, const qas_batch* b, int num_q_heads, 
 // Scores of the decode layer: [B][H_kv][max_pages] when the attention kernel
 // selects in-kernel (fixed row stride), else the packed qas_score_pages layout.
 bool layer_fused_topk(const qas_batch* b);
+// Row stride of the fixed-stride layout: max_pages rounded up to 4 entries,
+// so that with a 16-byte aligned workspace every row starts 16-byte aligned
+// and the attention kernel reads its row as 16-byte words.
+int layer_score_stride(const qas_batch* b) { return (b->max_pages + 3) & ~3; }
 size_t layer_scores_bytes(const qas_cache* c, const qas_batch* b) {
-  const size_t n = layer_fused_topk(b) ? (size_t)b->batch * b->max_pages : (size_t)b->total_pages;
+  const size_t n = layer_fused_topk(b) ? (size_t)b->batch * layer_score_stride(b)
+                                       : (size_t)b->total_pages;
   return align256(n * c->num_kv_heads * sizeof(float));
+}
+
+// Physical page of each scored page, [B][stride] int32, beside the scores:
+// the attention kernel reads it as 16-byte words instead of the caller's
+// page table (whose rows need not be aligned).
+size_t layer_phys_bytes(const qas_batch* b) {
+  return layer_fused_topk(b) ? align256((size_t)b->batch * layer_score_stride(b) * sizeof(int32_t))
+                             : 0;
 }
 
 bool layer_fused_topk(const qas_batch* b) {
@@ -145,6 +158,7 @@ qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q,
                          : qas::score_pages_per_iter(c->kv_dtype, c->head_dim, c->num_kv_heads);
   a.tickets = nullptr;
   a.row_stride = 0;
+  a.phys_out = nullptr;
   return a;
 }
 
@@ -178,6 +192,8 @@ qas::DecodeArgs decode_args(const qas_cache* c, const qas_batch* b, const void* 
   a.sm_scale = sm_scale;
   a.tickets = nullptr;
   a.scores = nullptr;
+  a.score_stride = 0;
+  a.phys_rows = nullptr;
   a.sel_out = nullptr;
   a.max_pages = b->max_pages;
   a.clear_tickets = 0;
@@ -239,8 +255,8 @@ size_t qas_workspace_bytes(int32_t op, const qas_cache* cache, const qas_batch* 
   const DecodePlan p = plan_decode(cache, batch, num_q_heads, k);
   if (op == QAS_OP_SPARSE_DECODE) return p.partial_bytes + p.ticket_bytes;
   if (op == QAS_OP_DECODE_LAYER)
-    return layer_scores_bytes(cache, batch) + p.partial_bytes + p.ticket_bytes +
-           2 * layer_sel_bytes(cache, batch, k);
+    return layer_scores_bytes(cache, batch) + layer_phys_bytes(batch) + p.partial_bytes +
+           p.ticket_bytes + 2 * layer_sel_bytes(cache, batch, k);
   return 0;
 }
 
@@ -359,6 +375,8 @@ qas_status qas_sparse_decode(const qas_cache* cache, const qas_batch* batch, con
   const size_t need = p.partial_bytes + p.ticket_bytes;
   if (!workspace || workspace_bytes < need)
     return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(QAS_ERR_WORKSPACE, "workspace %p is not 16-byte aligned", workspace);
   qas::DecodeArgs a = decode_args(cache, batch, q, num_q_heads, g, sel, sel_stride, sel_len,
                                   sm_scale, out, lse, (float*)workspace, p.n_split, 1);
   a.tickets = (unsigned int*)((char*)workspace + p.partial_bytes);
@@ -395,6 +413,8 @@ qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch
   const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, cap);
   if (!workspace || workspace_bytes < need)
     return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(QAS_ERR_WORKSPACE, "workspace %p is not 16-byte aligned", workspace);
   if (!qas::score_supported(cache->kv_dtype, cache->head_dim, g, cache->num_kv_heads))
     return fail(QAS_ERR_UNSUPPORTED, "score: %d KV heads of d=%d", cache->num_kv_heads,
                 cache->head_dim);
@@ -403,6 +423,8 @@ qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch
   char* ws = (char*)workspace;
   float* scores = (float*)ws;
   ws += layer_scores_bytes(cache, batch);
+  int32_t* phys_rows = (int32_t*)ws;
+  ws += layer_phys_bytes(batch);
   float* partials = (float*)ws;
   ws += p.partial_bytes;
   unsigned int* tickets = (unsigned int*)ws;
@@ -415,7 +437,8 @@ qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch
   sa.k_new = k_new;
   sa.v_new = v_new;
   sa.tickets = tickets;
-  sa.row_stride = layer_fused_topk(batch) ? batch->max_pages : 0;
+  sa.row_stride = layer_fused_topk(batch) ? layer_score_stride(batch) : 0;
+  sa.phys_out = layer_fused_topk(batch) ? phys_rows : nullptr;
   if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
   // lists hold the top-k joined with the fixed pages: cap entries per row
   qas::DecodeArgs da = decode_args(cache, batch, q, num_q_heads, g, nullptr, cap, cap, sm_scale,
@@ -427,6 +450,8 @@ qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch
   if (layer_fused_topk(batch)) {
     // 2. top-k per (request, KV head) inside the attention kernel
     da.scores = scores;
+    da.score_stride = layer_score_stride(batch);
+    da.phys_rows = phys_rows;
     da.sel_out = sel_out;
   } else {
     // 2. top-k per (request, KV head) in a kernel of its own (long rows)

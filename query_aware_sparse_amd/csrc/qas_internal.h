@@ -16,6 +16,7 @@ struct ScoreArgs {
   const int32_t* page_indices;
   float* scores;             // row_stride 0: [pbeg*H_kv + h*P_r + j], else [(r*H_kv + h)*row_stride + j]
   int row_stride;
+  int32_t* phys_out;         // optional (row_stride > 0): [r*row_stride + j] physical page of page j
   // optional decode append of the token at seq_lens[r] - 1 (k_new != NULL)
   const void* k_new;         // [B][H_kv][d]
   const void* v_new;
@@ -84,8 +85,10 @@ struct DecodeArgs {
   float* partials;           // [B][H_q][n_split][2 + d]
   unsigned int* tickets;     // [B][H_kv] split arrival counters, zero on entry
   // in-kernel top-K (scores != NULL): select sel_len pages per (request, KV
-  // head) from scores laid out [B][H_kv][max_pages]; sel / sel_phys unused
+  // head) from scores laid out [B][H_kv][score_stride]; sel / sel_phys unused
   const float* scores;
+  int score_stride;          // row stride of scores (>= max_pages, a multiple of 4)
+  const int32_t* phys_rows;  // [B][score_stride] physical page of each scored page
   int32_t* sel_out;          // optional [B][H_kv][sel_len] copy of the selection
   int max_pages;
   int k;                     // in-kernel top-K: pages Quest selects per row

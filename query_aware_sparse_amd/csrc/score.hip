@@ -147,6 +147,8 @@ __global__ __launch_bounds__(1024) void score_kernel(ScoreArgs a) {
       best = fmaxf(best, s);                      // group max
     }
     if (c == 0 && j[u] < lim) srow[j[u]] = j[u] < n_used ? best : -INFINITY;
+    if (a.phys_out && h == 0 && c == 0 && j[u] < lim)
+      a.phys_out[(size_t)r * a.row_stride + j[u]] = pp[u];
   }
 }
 
@@ -325,6 +327,8 @@ __global__ __launch_bounds__(512) void score8_kernel(ScoreArgs a) {
       best = fmaxf(best, s);
     }
     if (c == 0 && j[u] < lim) srow[j[u]] = j[u] < n_used ? best : -INFINITY;
+    if (a.phys_out && h == 0 && c == 0 && j[u] < lim)
+      a.phys_out[(size_t)r * a.row_stride + j[u]] = pp[u];
   }
 }
 

@@ -194,6 +194,40 @@ struct TopkRow {
     }
   }
 
+  // Scores and physical pages of a row as 16-byte words, in two steps so
+  // that the loads can be issued at kernel entry, before the row's length is
+  // known: issue_x4 loads quads [j0, j0 + PT) of srow and prow (both 16-byte
+  // aligned, holding at least cap rounded up to 4 entries; a quad past cap
+  // reads the row's first quad), finish_x4 keeps scores below cap and pages
+  // below n_.
+  float4 xs[PT / 4];
+  int4 xp[PT / 4];
+  __device__ __forceinline__ void issue_x4(const float* srow, const int32_t* prow, int cap) {
+    static_assert(PT % 4 == 0, "quads per thread");
+    j0 = threadIdx.x * PT;
+#pragma unroll
+    for (int q = 0; q < PT / 4; ++q) {
+      const int o = j0 + 4 * q < cap ? j0 + 4 * q : 0;
+      xs[q] = *reinterpret_cast<const float4*>(srow + o);
+      xp[q] = *reinterpret_cast<const int4*>(prow + o);
+    }
+  }
+  __device__ __forceinline__ void finish_x4(int cap, int n_) {
+    n = n_;
+#pragma unroll
+    for (int q = 0; q < PT / 4; ++q) {
+      const int j = j0 + 4 * q;
+      v[4 * q] = j < cap ? xs[q].x : 0.f;
+      v[4 * q + 1] = j + 1 < cap ? xs[q].y : 0.f;
+      v[4 * q + 2] = j + 2 < cap ? xs[q].z : 0.f;
+      v[4 * q + 3] = j + 3 < cap ? xs[q].w : 0.f;
+      pv[4 * q] = j < n ? xp[q].x : 0;
+      pv[4 * q + 1] = j + 1 < n ? xp[q].y : 0;
+      pv[4 * q + 2] = j + 2 < n ? xp[q].z : 0;
+      pv[4 * q + 3] = j + 3 < n ? xp[q].w : 0;
+    }
+  }
+
   __device__ __forceinline__ void load(const float* srow, const int32_t* pt, int n_) {
     load_scores(srow, n_);
     load_pages(pt, n_);

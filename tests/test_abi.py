@@ -77,6 +77,10 @@ def test_validation_happens_before_any_launch(qas):
     assert need > 0
     assert lib.qas_decode_layer(byref(c), byref(b), 8, 1, 32, 64, 0.1, None, None, None,
                                 8, None, 8, need - 1, None) == 5
+    # workspace large enough but not 16-byte aligned (checked before any launch)
+    assert lib.qas_decode_layer(byref(c), byref(b), 8, 1, 32, 64, 0.1, None, None, None,
+                                8, None, 8, need, None) == 5
+    assert b"aligned" in lib.qas_last_error()
     # top-k: k < 1
     assert lib.qas_topk_pages(8, byref(b), 8, 16, 0, 8, None, None) == 2
     # sparse decode: sel_stride < sel_len
