@@ -6,17 +6,20 @@
 //
 // A workgroup of kTkThreads threads holds the row in registers: thread t
 // keeps the run of scores j in [t*PT, t*PT + PT) and their physical pages.
-// Every per-element step is branch-free (invalid elements go to a dummy
-// histogram bin or LDS slot), and block-uniform values are moved to scalar
-// registers, so one select costs a few thousand cycles.  Selection narrows a closed score interval [lo, hi] that holds the
-// K-th largest score:
+// Per-element steps are branch-free (invalid elements go to a dummy
+// histogram bin), block-uniform values live in scalar registers, and
+// reductions within a wave use DPP, so one select costs a few thousand
+// cycles (a wave64 vector instruction occupies its SIMD for four cycles, so
+// the instruction count is the cost).  Selection narrows a closed score
+// interval [lo, hi] that holds the K-th largest score:
 //   * histogram the candidates into kTkBins bins through a monotone map
 //     (lo in bin 0, hi in the top bin);
-//   * one wave walks the bins from the top to the one holding the K-th
-//     score; scores in higher bins are taken and that bin's scores are the
-//     candidates (if still too many, [lo, hi] shrinks to their exact
-//     min/max and the step repeats; the bin misses lo or hi, so each repeat
-//     drops at least one distinct value);
+//   * every wave walks the bins from the top to the one holding the K-th
+//     score (a scan over the lanes' 16-bin sums finds the lane, a row scan
+//     over that lane's bins the bin); scores in higher bins are taken and
+//     that bin's scores are the candidates (if still too many, [lo, hi]
+//     shrinks to their exact min/max and the step repeats; the bin misses
+//     lo or hi, so each repeat drops at least one distinct value);
 //   * rank the candidates exactly by (score desc, index asc).  The last one
 //     taken is the threshold (T_s, T_j): page j is selected iff s_j > T_s,
 //     or s_j == T_s and j <= T_j.
@@ -42,8 +45,8 @@ constexpr float kTkMinRange = 1e-30f;
 
 struct TopkShared {
   __align__(16) int hist[kTkBins + 4];   // + a dummy bin for skipped elements
-  int cidx[kTkCand + kTkThreads];        // + one dummy slot per thread
-  float cval[kTkCand + kTkThreads];
+  int cidx[kTkCand];
+  float cval[kTkCand];
   int scan[2][kTkWaves];
   float mm[2 * kTkWaves];
   int nslot, tj;
@@ -99,10 +102,35 @@ __device__ __forceinline__ float wave_min(float v) {
   return fminf(v, __shfl_xor(v, 32, kWave));
 }
 
+// min and max over the wave, returned in every lane: DPP within rows of 16
+// lanes, then row_bcast:15 / row_bcast:31 carry the row results upwards
+// (rows outside the row mask keep their value), so lane 63 holds the
+// wave's result; no LDS traffic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_keep_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ void wave_minmax(float& lo, float& hi) {
+  lo = fminf(lo, dpp_f<0xB1>(lo));
+  hi = fmaxf(hi, dpp_f<0xB1>(hi));
+  lo = fminf(lo, dpp_f<0x4E>(lo));
+  hi = fmaxf(hi, dpp_f<0x4E>(hi));
+  lo = fminf(lo, dpp_f<0x141>(lo));
+  hi = fmaxf(hi, dpp_f<0x141>(hi));
+  lo = fminf(lo, dpp_f<0x140>(lo));
+  hi = fmaxf(hi, dpp_f<0x140>(hi));
+  lo = fminf(lo, dpp_keep_f<0x142, 0xA>(lo));
+  hi = fmaxf(hi, dpp_keep_f<0x142, 0xA>(hi));
+  lo = fminf(lo, dpp_keep_f<0x143, 0xC>(lo));
+  hi = fmaxf(hi, dpp_keep_f<0x143, 0xC>(hi));
+  lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo), kWave - 1));
+  hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi), kWave - 1));
+}
+
 // (min, max) over the workgroup; one barrier.
 __device__ __forceinline__ void block_minmax(float& lo, float& hi, float* scratch) {
-  lo = wave_min(lo);
-  hi = group_max<kWave>(hi);
+  wave_minmax(lo, hi);
   if (lane_id() == 0) {
     scratch[2 * wave_id()] = lo;
     scratch[2 * wave_id() + 1] = hi;
@@ -139,9 +167,9 @@ struct Binner {
     inv = uniform_f(by_key ? 0.f : (float)kTkBins / range);
     klo = order_key(l);
     const uint32_t span = order_key(h) - klo;
-    int sh = 0;
-    while ((span >> sh) >= (uint32_t)kTkBins) ++sh;
-    kshift = uniform_i(sh);
+    // smallest shift with (span >> shift) < kTkBins (= 2^10)
+    const int bits = span ? 32 - __clz((int)span) : 0;
+    kshift = uniform_i(bits > 10 ? bits - 10 : 0);
   }
   // the two maps; callers branch once on the uniform by_key
   __device__ __forceinline__ int by_value(float s) const {
@@ -283,7 +311,10 @@ struct TopkRow {
       if (bin.by_key) {
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
-          const int b = bin.by_order_key(v[k]);
+          // the empty asm keeps the key computation on this (rare) path
+          float x = v[k];
+          asm volatile("" : "+v"(x));
+          const int b = bin.by_order_key(x);
           bk[k] = (valid(k) & (v[k] >= lo) & (v[k] <= hi)) ? b : kTkBins;
         }
       } else {
@@ -301,38 +332,37 @@ struct TopkRow {
         // result; lane l owns bins NB-1-16l ... NB-16-16l (lane order walks
         // downward)
         constexpr int PER = kTkBins / kWave;
+        static_assert(PER == 16, "one row of 16 lanes re-reads a lane's bins");
         const int lane = lane_id();
-        int c[PER], local = 0;
+        int local = 0;
         const int4* hv = reinterpret_cast<const int4*>(sh.hist + kTkBins - PER * (lane + 1));
 #pragma unroll
         for (int q4 = 0; q4 < PER / 4; ++q4) {
           const int4 x = hv[q4];
-          // bins ascend in memory; c[] walks them descending
-          c[PER - 1 - 4 * q4] = x.x;
-          c[PER - 2 - 4 * q4] = x.y;
-          c[PER - 3 - 4 * q4] = x.z;
-          c[PER - 4 - 4 * q4] = x.w;
+          local += (x.x + x.y) + (x.z + x.w);
         }
-#pragma unroll
-        for (int k = 0; k < PER; ++k) local += c[k];
         const int incl = wave_incl_scan(local);
         const int excl = incl - local;
-        int b_here = 0, above_here = 0, cnt_here = 0, run = excl;
-        bool found = false;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const bool hit = !found && run + c[k] >= kk;
-          b_here = hit ? kTkBins - 1 - (lane * PER + k) : b_here;
-          above_here = hit ? run : above_here;
-          cnt_here = hit ? c[k] : cnt_here;
-          found = found || hit;
-          run += c[k];
-        }
+        // the lane whose 16 bins hold the kk-th largest element
         const uint64_t here = __ballot(excl < kk && incl >= kk);
         const int src = uniform_i(__ffsll((unsigned long long)here) - 1);
-        cbin = __builtin_amdgcn_readlane(b_here, src);
-        kk -= __builtin_amdgcn_readlane(above_here, src);
-        ncand = __builtin_amdgcn_readlane(cnt_here, src);
+        const int above_src = __builtin_amdgcn_readlane(excl, src);
+        // lanes 16m + i (every row alike) take bin i of that lane in walk
+        // order (descending bins); a row scan finds the crossing bin
+        const int i = lane & (PER - 1);
+        const int bi = kTkBins - 1 - (src * PER + i);
+        const int ci = sh.hist[bi];
+        int run = ci;
+        run += dpp_shift<0x111, 0xF>(run);   // row_shr:1
+        run += dpp_shift<0x112, 0xF>(run);   // row_shr:2
+        run += dpp_shift<0x114, 0xF>(run);   // row_shr:4
+        run += dpp_shift<0x118, 0xF>(run);   // row_shr:8
+        const int before = above_src + run - ci;
+        const uint64_t hit = __ballot((before < kk) & (before + ci >= kk)) & 0xFFFFull;
+        const int at = uniform_i(__ffsll((unsigned long long)hit) - 1);
+        cbin = __builtin_amdgcn_readlane(bi, at);
+        kk -= __builtin_amdgcn_readlane(before, at);
+        ncand = __builtin_amdgcn_readlane(ci, at);
       }
       ++round;
       if (ncand <= kTkCand) break;
@@ -378,17 +408,21 @@ struct TopkRow {
 #pragma unroll
       for (int k = 0; k < PT; ++k) mine += is_cand(k) ? 1 : 0;
       const int incl = wave_incl_scan(mine);
-      int base = 0;
-      if (lane_id() == kWave - 1) base = atomicAdd(&sh.nslot, incl);
-      int at = __builtin_amdgcn_readlane(base, kWave - 1) + incl - mine;
-      const int dummy = kTkCand + tid;
+      const int wave_total = __builtin_amdgcn_readlane(incl, kWave - 1);
+      if (wave_total > 0) {                    // uniform; most waves hold none
+        int base = 0;
+        if (lane_id() == kWave - 1) base = atomicAdd(&sh.nslot, incl);
+        int at = __builtin_amdgcn_readlane(base, kWave - 1) + incl - mine;
+        if (mine > 0) {
 #pragma unroll
-      for (int k = 0; k < PT; ++k) {
-        const bool c = is_cand(k);
-        const int slot = c ? at : dummy;
-        sh.cidx[slot] = j0 + k;
-        sh.cval[slot] = v[k];
-        at += c ? 1 : 0;
+          for (int k = 0; k < PT; ++k) {
+            if (is_cand(k)) {
+              sh.cidx[at] = j0 + k;
+              sh.cval[at] = v[k];
+              ++at;
+            }
+          }
+        }
       }
       __syncthreads();
       const int total = ncand;
