@@ -25,7 +25,7 @@ bool decode_supported(int kv_dtype, int d, int g) {
 
 int decode_num_splits(int rows, int sel_len) {
   if (sel_len < 1) sel_len = 1;
-  int n = (512 + rows - 1) / rows;
+  int n = (256 + rows - 1) / rows;            // one workgroup per CU
   const int cap = (sel_len + 3) / 4;
   if (n > cap) n = cap;
   const int need = (sel_len + kDecMaxList - 1) / kDecMaxList;
@@ -36,7 +36,7 @@ int decode_num_splits(int rows, int sel_len) {
 
 int decode_max_dedupe_row() { return kDecMaxRow; }
 
-int decode_fused_topk_max_pages() { return kTkThreads * kDecFusedTopkPT; }
+int decode_fused_topk_max_pages() { return kDecThreads * kDecFusedTopkPT; }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.clear_tickets && a.n_split > 1) {

@@ -36,13 +36,17 @@
 
 namespace qas {
 
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / kWave;
 // token groups in flight per wave (bounded by registers)
-template <int G> constexpr int dec_unroll() { return G <= 2 ? 16 : G <= 4 ? 8 : 4; }
+// K/V rows each wave loads per batch: as many as the registers hold at two
+// waves per SIMD (f16 products read packed halves; bf16/f32 unpack to fp32)
+template <int DT, int G> constexpr int dec_unroll() {
+  return DT == kBF16 && G == 8 ? 1 : (DT == kF16 ? 16 : 8) / (G <= 2 ? 1 : G <= 4 ? 2 : 4);
+}
 constexpr int kDecMaxList = 1024;      // selected entries per split
 constexpr int kDecMaxRow = 4096;       // entries of a row when deduplicating
-constexpr int kDecFusedTopkPT = 16;    // in-kernel top-K: scores per thread at most
+constexpr int kDecFusedTopkPT = 8;    // in-kernel top-K: scores per thread at most
 constexpr float kLog2e = 1.4426950408889634f;
 
 namespace decode_detail {
@@ -115,8 +119,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   // in-kernel top-K: the row's scores and physical pages sit at a fixed
   // stride (a multiple of 4 entries in a 16-byte aligned workspace), so their
   // 16-byte loads go out first, before the request's bounds are known
-  TopkRow<(TPT > 0 ? TPT : 4)> t;
-  const int cap = min(a.max_pages, kTkThreads * TPT);   // the host keeps rows within this
+  TopkRow<(TPT > 0 ? TPT : 4), kDecThreads> t;
+  const int cap = min(a.max_pages, kDecThreads * TPT);  // the host keeps rows within this
   if constexpr (TPT > 0)
     t.issue_x4(a.scores + ((size_t)r * H + h) * a.score_stride,
                a.phys_rows + (size_t)r * a.score_stride, cap);
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
 
-  constexpr int UNR = dec_unroll<G>();
+  constexpr int UNR = dec_unroll<DT, G>();
   for (int u0 = wave; u0 < units; u0 += kDecWaves * UNR) {
     uint4 kr[UNR], vr[UNR];
     bool ok[UNR];
@@ -372,9 +376,9 @@ template <int DT, int D, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.H_kv, a.B);
   if (a.scores) {
-    if (a.max_pages <= kTkThreads * 8)
-      hipLaunchKernelGGL((decode_kernel<DT, D, G, 8>), grid, dim3(kDecThreads), 0, s, a);
-    else if (a.max_pages <= kTkThreads * kDecFusedTopkPT)
+    if (a.max_pages <= kDecThreads * 4)
+      hipLaunchKernelGGL((decode_kernel<DT, D, G, 4>), grid, dim3(kDecThreads), 0, s, a);
+    else if (a.max_pages <= kDecThreads * kDecFusedTopkPT)
       hipLaunchKernelGGL((decode_kernel<DT, D, G, kDecFusedTopkPT>), grid, dim3(kDecThreads), 0, s, a);
     else
       return hipErrorInvalidValue;

@@ -4,7 +4,8 @@
 // Used by the standalone top-K kernel and inside the attention kernel of the
 // decode layer.
 //
-// A workgroup of kTkThreads threads holds the row in registers: thread t
+// A workgroup of NT threads (kTkThreads in the standalone kernel, the
+// attention kernel's workgroup inside it) holds the row in registers: thread t
 // keeps the run of scores j in [t*PT, t*PT + PT) and their physical pages.
 // Per-element steps are branch-free (invalid elements go to a dummy
 // histogram bin), block-uniform values live in scalar registers, and
@@ -37,8 +38,8 @@
 
 namespace qas {
 
-constexpr int kTkThreads = 256;
-constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kTkThreads = 256;      // workgroup of the standalone top-K kernel
+constexpr int kTkMaxWaves = 8;       // largest workgroup a row select runs in
 constexpr int kTkBins = 1024;
 constexpr int kTkCand = 512;         // candidates ranked from LDS
 constexpr float kTkMinRange = 1e-30f;
@@ -47,8 +48,8 @@ struct TopkShared {
   __align__(16) int hist[kTkBins + 4];   // + a dummy bin for skipped elements
   int cidx[kTkCand];
   float cval[kTkCand];
-  int scan[2][kTkWaves];
-  float mm[2 * kTkWaves];
+  int scan[2][kTkMaxWaves];
+  float mm[2 * kTkMaxWaves];
   int nslot, tj;
   float ts;
 };
@@ -76,15 +77,16 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive prefix sum over the workgroup in thread order; one barrier.
-// `scratch` (kTkWaves ints) must not be rewritten before another barrier.
+// Exclusive prefix sum over the workgroup (NW waves) in thread order; one
+// barrier.  `scratch` (NW ints) must not be rewritten before another barrier.
+template <int NW>
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
   const int incl = wave_incl_scan(v);
   if (lane_id() == kWave - 1) scratch[wave_id()] = incl;
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int c = scratch[w];
     before += w < wave_id() ? c : 0;
     all += c;
@@ -128,7 +130,8 @@ __device__ __forceinline__ void wave_minmax(float& lo, float& hi) {
   hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi), kWave - 1));
 }
 
-// (min, max) over the workgroup; one barrier.
+// (min, max) over the workgroup (NW waves); one barrier.
+template <int NW>
 __device__ __forceinline__ void block_minmax(float& lo, float& hi, float* scratch) {
   wave_minmax(lo, hi);
   if (lane_id() == 0) {
@@ -139,7 +142,7 @@ __device__ __forceinline__ void block_minmax(float& lo, float& hi, float* scratc
   lo = scratch[0];
   hi = scratch[1];
 #pragma unroll
-  for (int w = 1; w < kTkWaves; ++w) {
+  for (int w = 1; w < NW; ++w) {
     lo = fminf(lo, scratch[2 * w]);
     hi = fmaxf(hi, scratch[2 * w + 1]);
   }
@@ -184,8 +187,10 @@ struct Binner {
 }  // namespace tk
 
 // One row held by the workgroup: PT scores per thread.
-template <int PT>
+template <int PT, int NT = kTkThreads>
 struct TopkRow {
+  static constexpr int NW = NT / kWave;
+  static_assert(NT % kWave == 0 && NW <= kTkMaxWaves, "workgroup of whole waves");
   float v[PT];
   int pv[PT];
   int j0, n;
@@ -289,9 +294,9 @@ struct TopkRow {
     Tj = n;                                    // take == n: everything
     if (take >= n) return;
 
-    for (int b = tid; b < kTkBins + 4; b += kTkThreads) sh.hist[b] = 0;
+    for (int b = tid; b < kTkBins + 4; b += NT) sh.hist[b] = 0;
     if (tid == 0) sh.nslot = 0;
-    block_minmax(lo, hi, sh.mm);
+    block_minmax<NW>(lo, hi, sh.mm);
     lo = uniform_f(lo);
     hi = uniform_f(hi);
     int kk = take;                             // still to take among candidates
@@ -303,7 +308,7 @@ struct TopkRow {
     while (ncand > kTkCand && lo < hi) {
       bin.init(lo, hi);
       if (round > 0) {
-        for (int b = tid; b < kTkBins + 4; b += kTkThreads) sh.hist[b] = 0;
+        for (int b = tid; b < kTkBins + 4; b += NT) sh.hist[b] = 0;
         __syncthreads();
       }
       // skipped elements go to the dummy bin; out-of-range values may map
@@ -375,7 +380,7 @@ struct TopkRow {
         nlo = fminf(nlo, in ? v[k] : FLT_MAX);
         nhi = fmaxf(nhi, in ? v[k] : -FLT_MAX);
       }
-      block_minmax(nlo, nhi, sh.mm);
+      block_minmax<NW>(nlo, nhi, sh.mm);
       lo = uniform_f(nlo);
       hi = uniform_f(nhi);
       cbin = -1;
@@ -391,7 +396,7 @@ struct TopkRow {
 #pragma unroll
       for (int k = 0; k < PT; ++k) mine += (valid(k) & (v[k] == lo)) ? 1 : 0;
       int total;
-      int seen = block_excl_scan(mine, sh.scan[0], &total);
+      int seen = block_excl_scan<NW>(mine, sh.scan[0], &total);
 #pragma unroll
       for (int k = 0; k < PT; ++k) {
         const bool eq = valid(k) & (v[k] == lo);
@@ -426,7 +431,7 @@ struct TopkRow {
       }
       __syncthreads();
       const int total = ncand;
-      for (int i = tid; i < total; i += kTkThreads) {
+      for (int i = tid; i < total; i += NT) {
         const float si = sh.cval[i];
         const int ji = sh.cidx[i];
         int rank = 0;
@@ -452,7 +457,7 @@ struct TopkRow {
     int mine = 0;
 #pragma unroll
     for (int k = 0; k < PT; ++k) mine += selected(k) ? 1 : 0;
-    return tk::block_excl_scan(mine, sh.scan[1], count);
+    return tk::block_excl_scan<NW>(mine, sh.scan[1], count);
   }
 };
 
