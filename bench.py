@@ -48,9 +48,12 @@ CHUNK_METRIC = "µs per multi-query chunk call + fp8 MFMA TFLOP/s, 64K ctx, 512 
 # 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write x1.0.  Valid only
 # for the kernel sources they were taken on (sha256 of csrc/).
 PMC_TRAFFIC = {
-    "csrc_sha256": "5ebf4dbe3403c1f5dfa9875672d7444b088c95aa69b007f55939e34dea917d67",
-    "fetch_kib": {"score_kernel": 16560.9, "decode_kernel": 34176.1},
-    "write_kib": {"score_kernel": 544.1, "decode_kernel": 337.3},
+    "csrc_sha256": "24aa17043df6fac23bec6b8f7695ad1b21a590bd52e6ec94aa553289a6ec58d5",
+    "fetch_kib": {"score_kernel": 16557.8, "decode_kernel": 34082.0},
+    "write_kib": {"score_kernel": 614.8, "decode_kernel": 173.3},
+    # the same passes, call on the e4m3 summary copy
+    "fetch_kib_fp8": {"score8_kernel": 8495.9, "decode_kernel": 34082.0},
+    "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.3},
     "fetch_factor": 2.0,
     "write_factor": 1.0,
 }
@@ -68,14 +71,16 @@ def csrc_sha256():
     return h.hexdigest()
 
 
-def pmc_traffic_bytes():
-    """HBM bytes per decode-layer call from the recorded counters, or None if
-    the kernels changed since they were taken."""
+def pmc_traffic_bytes(fp8=False):
+    """HBM bytes per decode-layer call from the recorded counters (the call on
+    the e4m3 summary copy if fp8), or None if the kernels changed since they
+    were taken."""
     t = PMC_TRAFFIC
     if t["csrc_sha256"] is None or t["csrc_sha256"] != csrc_sha256():
         return None
-    kib = (sum(t["fetch_kib"].values()) * t["fetch_factor"] +
-           sum(t["write_kib"].values()) * t["write_factor"])
+    sfx = "_fp8" if fp8 else ""
+    kib = (sum(t["fetch_kib" + sfx].values()) * t["fetch_factor"] +
+           sum(t["write_kib" + sfx].values()) * t["write_factor"])
     return int(round(kib * 1024))
 
 
@@ -462,7 +467,8 @@ def main():
                    "fp8_summary_copy": {
                        "us_per_call": round(us_fp8, 3), "bytes_per_call": bytes_fp8,
                        "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
-                       "ms_per_step_wall": round(ms_fp8, 6)}},
+                       "ms_per_step_wall": round(ms_fp8, 6),
+                       "traffic": pmc_traffic_bytes(fp8=True)}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic_bytes(),
