@@ -288,6 +288,120 @@ def decode_request(q, keys, values, L, S, K, scale=None, page_ids=None, sink_tok
             "out": out, "lse": lse}
 
 
+# ------------------------------------------ cache lifecycle (rollback) ----
+
+def rollback_summaries(m, M, keys, L_new, S):
+    """[Quest] §3 (cache lifecycle, rollback): when the cache is cut back to
+    L_new tokens, pages wholly past the cut are dropped; if the cut falls
+    inside a page, the revoked tokens cannot be taken out of its min/max (one
+    of them may hold an extreme, and the summary would keep covering a point
+    that no longer exists), so that page is rescanned over its surviving
+    keys.  Pages before it are full and keep their summaries.
+
+    m, M: [>= ceil(L_new/S)][H_kv][d] summaries before the cut; keys:
+    [>= L_new][H_kv][d].  Returns (m, M) of the ceil(L_new/S) kept pages."""
+    P = num_pages(L_new, S)
+    m2 = np.array(m[:P], dtype=np.float64)
+    M2 = np.array(M[:P], dtype=np.float64)
+    if L_new % S:
+        p = P - 1
+        block = keys[p * S:L_new]
+        m2[p] = block.min(axis=0)
+        M2[p] = block.max(axis=0)
+    return m2, M2
+
+
+# -------------------------------------- per-position speculative selection ---
+
+def speculative_positions(q_block, keys, values, L, S, K, scale=None):
+    """[Quest] §1.2 (speculative decoding): a draft of gamma tokens occupies
+    positions L - gamma .. L - 1 of the cache (already appended); the query
+    of draft position i may see only tokens t <= c_i = L - gamma + i, and it
+    depends on the earlier draft tokens, so it ranks pages with its own
+    bound instead of reusing another position's set.  Reading taken: every
+    position scores the pages that hold a token it may see, pages
+    [0, ceil((c_i + 1)/S)), on the summaries of the cache as it stands (all L
+    tokens: a bound for every token the position sees), and attends over its
+    own top-K support with causal limit c_i.
+
+    q_block: [gamma][H_q][d]; keys, values: [>= L][H_kv][d].  Returns one
+    dict per position with its length L_i = c_i + 1, scores U [H_kv][P_i],
+    lists sel, out [H_q][d] and lse [H_q]."""
+    gamma, H_q, d = q_block.shape
+    H_kv = keys.shape[1]
+    g = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m, M = page_summaries(keys, L, S)
+    res = []
+    for i in range(gamma):
+        c = L - gamma + i
+        P_i = num_pages(c + 1, S)
+        U = kv_head_scores(head_bounds(q_block[i], m[:P_i], M[:P_i]), H_kv)
+        sel = [top_k_pages(U[h], K) for h in range(H_kv)]
+        out = np.zeros((H_q, d))
+        lse = np.zeros(H_q)
+        for qi in range(H_q):
+            h = qi // g
+            A = support(sel[h], L, c, S)
+            out[qi], lse[qi] = attend(q_block[i][qi], keys[:, h, :], values[:, h, :], A, scale)
+        res.append({"L": c + 1, "U": U, "sel": sel, "out": out, "lse": lse})
+    return res
+
+
+# ------------------------------------ branch-and-bound exact top-R (§3.2) ---
+
+def branch_and_bound(bounds, page_logits, R):
+    """[Quest] §3.2 (stopping rules beyond a fixed top-K): read pages in
+    descending bound order (ties to the lower page index), keep tau_R, the
+    R-th largest true logit among the tokens read so far, and stop when the
+    next unread page's bound is below tau_R: no token of the remaining pages
+    can enter the top R.  With fewer than R tokens read the search goes on.
+
+    bounds: [P]; page_logits: list of P arrays, the true logits of each
+    page's tokens, paired with token ids as (logit, token) tuples.  Returns
+    (pages read in order, top R (logit, token) pairs ordered by logit
+    descending then token ascending, tau_R at the stop)."""
+    P = len(bounds)
+    order = sorted(range(P), key=lambda j: (-bounds[j], j))
+    seen = []
+    read = []
+    for p in order:
+        if len(seen) >= R:
+            tau = sorted(seen, key=lambda x: (-x[0], x[1]))[R - 1][0]
+            if bounds[p] < tau:
+                break
+        read.append(p)
+        seen.extend(page_logits[p])
+    top = sorted(seen, key=lambda x: (-x[0], x[1]))[:R]
+    tau = top[-1][0] if len(top) >= R else -np.inf
+    return read, top, tau
+
+
+def exact_top_r(q_head, keys_h, L, S, R, m_h, M_h):
+    """Exact token top-R of one query head by branch-and-bound over its page
+    bounds ([Quest] §1.1 eq. (2)-(3) for this head alone, §3.2): true logits
+    are the unscaled dot products q . k_t (the bound's units; a positive
+    softmax scale does not reorder them) over tokens t < L.
+
+    q_head: [d]; keys_h: [>= L][d]; m_h, M_h: [P][d] this KV head's
+    summaries.  Returns (pages read, top-R (logit, token) pairs, tau_R)."""
+    P = num_pages(L, S)
+    bounds = np.maximum(q_head[None, :] * m_h[:P], q_head[None, :] * M_h[:P]).sum(axis=1)
+    page_logits = []
+    for p in range(P):
+        toks = range(p * S, min((p + 1) * S, L))
+        page_logits.append([(float(keys_h[t] @ q_head), t) for t in toks])
+    return branch_and_bound(bounds, page_logits, R)
+
+
+def brute_top_r(q_head, keys_h, L, R):
+    """The R largest logits q . k_t over all tokens t < L, ordered by logit
+    descending then token ascending (what the certificate must reproduce)."""
+    z = [(float(keys_h[t] @ q_head), t) for t in range(L)]
+    return sorted(z, key=lambda x: (-x[0], x[1]))[:R]
+
+
 # ----------------------------------------------------------- query union ---
 
 def union_with_membership(page_sets):

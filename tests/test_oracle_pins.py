@@ -507,3 +507,137 @@ def test_workload_cases_are_well_formed():
     assert all(k.shape[0] == L + 3 for k, L in zip(c3.keys, c3.seq_lens))
     flat = np.concatenate(c3.pages)
     assert len(set(flat.tolist())) == len(flat) and flat.max() < c3.num_pool_pages
+
+
+# ----------------------------------------------------------- NEXT-4 pins ----
+
+@pytest.mark.parametrize("L_old,L_new", [(37, 33), (37, 32), (40, 17), (17, 16), (5, 1),
+                                         (64, 63), (30, 29)])
+def test_rollback_rescan_equals_summaries_of_the_kept_tokens(L_old, L_new):
+    """Cutting the cache back and rescanning the tail page gives the summaries
+    the kept tokens define ([Quest] §1.1 eq. (1) over t < L_new)."""
+    S = 8
+    keys = _rng(70 + L_old + L_new).standard_normal((L_old, 3, 5))
+    m, M = quest.page_summaries(keys, L_old, S)
+    m2, M2 = quest.rollback_summaries(m, M, keys, L_new, S)
+    me, Me = quest.page_summaries(keys, L_new, S)
+    assert np.array_equal(m2, me) and np.array_equal(M2, Me)
+
+
+def test_rollback_without_rescan_keeps_a_revoked_extreme():
+    """The case [Quest] §3 warns of: the revoked token held the page's extreme,
+    so the old min/max would keep covering a point that no longer exists."""
+    keys = np.array([[1.0, 0.0], [2.0, 1.0], [9.0, -5.0]])[:, None, :]
+    m, M = quest.page_summaries(keys, 3, S=4)
+    assert M[0, 0].tolist() == [9.0, 1.0] and m[0, 0].tolist() == [1.0, -5.0]
+    m2, M2 = quest.rollback_summaries(m, M, keys, 2, S=4)
+    assert M2[0, 0].tolist() == [2.0, 1.0] and m2[0, 0].tolist() == [1.0, 0.0]
+
+
+def _spec_case(seed, L, gamma, S=4, H_q=4, H_kv=2, d=8):
+    r = _rng(seed)
+    keys = r.standard_normal((L, H_kv, d))
+    values = r.standard_normal((L, H_kv, d))
+    qb = r.standard_normal((gamma, H_q, d))
+    return keys, values, qb
+
+
+def test_speculative_single_position_is_a_decode_step():
+    keys, values, qb = _spec_case(80, L=37, gamma=1)
+    res = quest.speculative_positions(qb, keys, values, 37, 4, K=3)
+    ref = quest.decode_request(qb[0], keys, values, 37, 4, 3)
+    assert res[0]["sel"] == ref["sel"]
+    assert np.allclose(res[0]["out"], ref["out"], rtol=0, atol=1e-12)
+
+
+def test_speculative_position_closing_a_page_is_a_decode_step_on_the_cut_cache():
+    """Draft positions 12..16 with S = 4: position 3 (c = 15) closes page 3, so
+    the pages it scores hold exactly the tokens it sees and its result is the
+    decode step of the cache cut after token 15; position 0 (c = 12) scores
+    page 3 with the later drafts inside its bound and may not see them."""
+    L, gamma, S, K = 17, 5, 4, 2
+    keys, values, qb = _spec_case(81, L, gamma, S=S)
+    res = quest.speculative_positions(qb, keys, values, L, S, K)
+    assert [r["L"] for r in res] == [13, 14, 15, 16, 17]
+    ref = quest.decode_request(qb[3], keys[:16], values[:16], 16, S, K)
+    assert res[3]["sel"] == ref["sel"]
+    assert np.allclose(res[3]["out"], ref["out"], rtol=0, atol=1e-12)
+    assert res[0]["U"].shape[1] == 4
+    for r in res:
+        c = r["L"] - 1
+        for h, lst in enumerate(r["sel"]):
+            assert all(p * S <= c for p in lst)       # only pages it may see
+
+
+def test_speculative_positions_do_not_share_one_set():
+    """Each position ranks with its own query: with distinct queries the sets
+    differ from the first position's, and every position equals attention
+    over its own top-K support."""
+    L, gamma, S, K = 64, 4, 4, 3
+    keys, values, qb = _spec_case(82, L, gamma, S=S)
+    res = quest.speculative_positions(qb, keys, values, L, S, K)
+    assert any(r["sel"] != res[0]["sel"] for r in res[1:])
+    m, M = quest.page_summaries(keys, L, S)
+    for i, r in enumerate(res):
+        c = L - gamma + i
+        U = quest.kv_head_scores(quest.head_bounds(qb[i], m, M), 2)[:, :quest.num_pages(c + 1, S)]
+        assert np.array_equal(U, r["U"])
+        for qi in range(qb.shape[1]):
+            A = quest.support(r["sel"][qi // 2], L, c, S)
+            o, _ = quest.attend(qb[i][qi], keys[:, qi // 2], values[:, qi // 2], A,
+                                1 / math.sqrt(qb.shape[2]))
+            assert np.allclose(o, r["out"][qi], rtol=0, atol=1e-12)
+
+
+def test_branch_and_bound_four_page_example():
+    g = load_golden("quest_four_pages_bnb.json")
+    names = g["pages"]
+    page_logits = [[(float(v), j)] for j, v in enumerate(g["true_max"])]
+    read, top, tau = quest.branch_and_bound(g["bound"], page_logits, g["R"])
+    assert [names[p] for p in read] == g["read_order"]
+    assert [names[t] for _, t in top] == g["top"]
+    assert tau == g["tau_final"]
+
+
+def test_branch_and_bound_keeps_reading_at_an_equal_bound():
+    """A page whose bound equals tau_R may hold a token tied with it at a lower
+    token index, so only a bound strictly below tau_R stops the search."""
+    page_logits = [[(5.0, 0)], [(5.0, 1)]]
+    read, top, _ = quest.branch_and_bound([5.0, 6.0], page_logits, 1)
+    assert read == [1, 0] and top == [(5.0, 0)]
+
+
+@pytest.mark.parametrize("seed,R,spread", [(90, 1, 1.0), (91, 8, 1.0), (92, 50, 1.0),
+                                           (93, 8, 6.0), (94, 200, 1.0)])
+def test_branch_and_bound_is_the_exact_top_r(seed, R, spread):
+    """The certificate's claim: the tokens found equal the brute-force top R
+    over all tokens, and the first unread page's bound is below tau_R."""
+    r = _rng(seed)
+    L, S, d = 203, 8, 16
+    keys = r.standard_normal((L, 1, d))
+    q = r.standard_normal(d)
+    # a few aligned tokens make the bounds tight for the top pages
+    hot = r.choice(L, size=5, replace=False)
+    keys[hot, 0] += spread * q / np.linalg.norm(q) * math.sqrt(d)
+    m, M = quest.page_summaries(keys, L, S)
+    read, top, tau = quest.exact_top_r(q, keys[:, 0], L, S, R, m[:, 0], M[:, 0])
+    assert top == quest.brute_top_r(q, keys[:, 0], L, R)
+    P = quest.num_pages(L, S)
+    bounds = np.maximum(q * m[:, 0], q * M[:, 0]).sum(axis=1)
+    unread = [p for p in range(P) if p not in read]
+    if unread:
+        assert max(bounds[p] for p in unread) < tau
+    assert len(set(read)) == len(read) <= P
+    if spread > 1.0 and R == 8:
+        assert len(read) < P                          # tight bounds stop early
+
+
+def test_branch_and_bound_with_r_at_least_the_tokens_reads_everything():
+    r = _rng(95)
+    L, S = 21, 4
+    keys = r.standard_normal((L, 1, 4))
+    q = r.standard_normal(4)
+    m, M = quest.page_summaries(keys, L, S)
+    read, top, _ = quest.exact_top_r(q, keys[:, 0], L, S, 30, m[:, 0], M[:, 0])
+    assert sorted(read) == list(range(quest.num_pages(L, S)))
+    assert [t for _, t in top] == [t for _, t in quest.brute_top_r(q, keys[:, 0], L, L)]
