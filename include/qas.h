@@ -132,6 +132,22 @@ qas_status qas_append(const qas_cache* cache, const qas_batch* batch,
                       void* stream);
 
 /*
+ * qas_rollback - restore the summaries after the cache is cut back
+ * ([Quest] §3, cache lifecycle: rollback).  batch->seq_lens are the lengths
+ * AFTER the cut.  Pages wholly past a request's new length are the caller's
+ * to drop from its page table (their records are no longer read).  If the
+ * new length ends inside a page, the revoked tokens cannot be taken out of
+ * that page's min/max, so its record is rebuilt from the surviving keys in
+ * the pool (tokens [p*S, L) of tail page p = (L-1)/S), starting from
+ * -inf/+inf, and the e4m3 copy, if the cache has one, is re-quantised.  The
+ * pool's K/V rows are not touched; later appends at the cut overwrite the
+ * revoked rows.  Requests with L = 0, L a multiple of S, or a tail page
+ * outside their page-table row are left alone.  One launch, asynchronous on
+ * `stream`; argument errors return before anything is enqueued.
+ */
+qas_status qas_rollback(const qas_cache* cache, const qas_batch* batch, void* stream);
+
+/*
  * qas_score_pages - page bounds of the current queries ([Quest] §1.1
  * eq. (2)-(3)): U_{h,j} = max over the query heads i of KV head h of
  * sum_d max(q_{i,d} m_{j,d}, q_{i,d} M_{j,d}), unscaled, fp32 accumulate

@@ -51,6 +51,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SIGNATURES = {
     "qas_append": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
+    "qas_rollback": (_I, [_P, _P, _P]),
     "qas_score_pages": (_I, [_P, _P, _P, _I, _I, _P, _P]),
     "qas_topk_pages": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "qas_selection_capacity": (_I, [_I, _I, _I, _I]),
@@ -149,6 +150,12 @@ def qas_append(cache, batch, new_indptr, total_new, max_new, k_new, v_new, strea
     _check(_load().qas_append(ctypes.byref(cache), ctypes.byref(batch), _ptr(new_indptr),
                           int(total_new), int(max_new), _ptr(k_new), _ptr(v_new),
                           _stream(stream)))
+
+
+def qas_rollback(cache, batch, stream=None):
+    """Rebuild the tail-page summaries after the cache is cut back to
+    batch's seq_lens (see qas.h)."""
+    _check(_load().qas_rollback(ctypes.byref(cache), ctypes.byref(batch), _stream(stream)))
 
 
 def qas_score_pages(cache, batch, q, scores, stream=None):
@@ -254,7 +261,7 @@ def version():
     return _load().qas_version().decode()
 
 
-__all__ = ["qas_append", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
+__all__ = ["qas_append", "qas_rollback", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
            "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

@@ -15,6 +15,12 @@
 // into the pool, reduce min/max over their tokens, then the workgroup
 // reduces over token slots in LDS and writes the page's record.  The same
 // kernel serves prefill (many tokens per request) and decode (one token).
+//
+// Rescan mode (rollback, the Quest page's §3 on the cache lifecycle): after
+// the cache is cut back, a cut inside a page cannot be undone on the min/max
+// (a revoked token may hold an extreme), so the tail page's record is rebuilt
+// from the surviving keys in the pool, starting from -inf/+inf, and its e4m3
+// copy re-quantised; nothing is written to the pool.
 #include "qas_device.h"
 #include "qas_internal.h"
 
@@ -37,7 +43,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int u = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int H = a.H_kv, S = a.S;
   int L0, n, src0;
-  if (a.new_indptr) {
+  if (a.rescan) {            // tokens [p*S, L) of the tail page p, from the pool
+    const int L = a.seq_lens[r];
+    const int P_r = a.page_indptr[r + 1] - a.page_indptr[r];
+    if (u != 0 || L <= 0 || L % S == 0 || (L - 1) / S >= P_r) return;
+    L0 = (L - 1) / S * S;
+    n = L - L0;
+    src0 = 0;
+  } else if (a.new_indptr) {
     L0 = a.seq_lens[r];
     src0 = a.new_indptr[r];
     n = a.new_indptr[r + 1] - src0;
@@ -66,12 +79,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   char* kdst = reinterpret_cast<char*>(a.k_pool);
   char* vdst = reinterpret_cast<char*>(a.v_pool);
   for (int t = t0 + slot; t < t1; t += TS) {
-    const size_t src = (((size_t)(src0 + t - L0) * H + h) * D) * BYTES + c * 16;
     const size_t dst = (((phys * H + h) * S + (t - p * S)) * D) * BYTES + c * 16;
-    const uint4 kr = load16(ksrc + src);
-    const uint4 vr = load16(vsrc + src);
-    *reinterpret_cast<uint4*>(kdst + dst) = kr;
-    *reinterpret_cast<uint4*>(vdst + dst) = vr;
+    uint4 kr;
+    if (a.rescan) {
+      kr = load16(kdst + dst);
+    } else {
+      const size_t src = (((size_t)(src0 + t - L0) * H + h) * D) * BYTES + c * 16;
+      kr = load16(ksrc + src);
+      const uint4 vr = load16(vsrc + src);
+      *reinterpret_cast<uint4*>(kdst + dst) = kr;
+      *reinterpret_cast<uint4*>(vdst + dst) = vr;
+    }
     float kf[EPL];
     unpack16<DT>(kr, kf);
 #pragma unroll
@@ -121,7 +139,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 
 template <int DT, int D>
 hipError_t launch_t(const AppendArgs& a, hipStream_t s) {
-  const int pages = a.new_indptr ? (a.max_new + a.S - 1) / a.S + 1 : 1;
+  const int pages = a.new_indptr && !a.rescan ? (a.max_new + a.S - 1) / a.S + 1 : 1;
   dim3 grid(pages, a.H_kv, a.B);
   hipLaunchKernelGGL((append_kernel<DT, D>), grid, dim3(kAppendThreads), 0, s, a);
   return hipGetLastError();

@@ -223,6 +223,7 @@ qas::AppendArgs append_args(const qas_cache* c, const qas_batch* b, const int32_
   a.max_new = max_new;
   a.summary_fp8 = c->summary_fp8;
   a.summary_fp8_scale = c->summary_fp8_scale;
+  a.rescan = 0;
   return a;
 }
 
@@ -277,6 +278,21 @@ qas_status qas_append(const qas_cache* cache, const qas_batch* batch, const int3
   qas::AppendArgs a = append_args(cache, batch, new_indptr, max_new, k_new, v_new);
   hipError_t e = qas::launch_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+qas_status qas_rollback(const qas_cache* cache, const qas_batch* batch, void* stream) {
+  qas_status st = check_cache(cache, true, true);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  if (!qas::append_supported(cache->kv_dtype, cache->head_dim))
+    return fail(QAS_ERR_UNSUPPORTED, "rollback: dtype %d / head_dim %d", cache->kv_dtype,
+                cache->head_dim);
+  if (batch->batch == 0) return ok();
+  qas::AppendArgs a = append_args(cache, batch, nullptr, 0, nullptr, nullptr);
+  a.rescan = 1;
+  hipError_t e = qas::launch_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rollback launch");
   return ok();
 }
 

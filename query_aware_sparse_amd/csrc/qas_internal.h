@@ -67,6 +67,8 @@ struct AppendArgs {
   float* summary_fp8_scale;  //   and its scale [pool][H_kv]
   int B, H_kv, d, S, kv_dtype;
   int max_new;
+  int rescan;                // 1: rebuild each request's tail record from the pool's
+                             //    keys (seq_lens = lengths after a rollback); no K/V written
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 bool append_supported(int kv_dtype, int d);
