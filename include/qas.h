@@ -340,6 +340,37 @@ qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
                                int32_t group, const int32_t* ids, float sm_scale,
                                void* out, float* lse, void* stream);
 
+/*
+ * qas_decode_positions - the decode layer for a speculative verification
+ * block ([Quest] §1.2, speculative decoding): each request carries gamma
+ * draft tokens, already appended (seq_lens count them), whose queries
+ * depend on the earlier drafts, so each draft position selects its own
+ * pages instead of sharing one set.  Position i of request r has causal
+ * limit c = seq_lens[r] - gamma + i: its query is scored over the pages
+ * holding a token t <= c (on the summaries as they stand, a bound for every
+ * token it sees), the top-k pages per (position, KV head) are selected
+ * (ties to the lower page index), and attention runs over its support with
+ * that causal limit.  A position with c < 0 has an empty support: out = 0,
+ * lse = -inf.  Requests of more than 4096 pages (the in-kernel top-k)
+ * return QAS_ERR_UNSUPPORTED.
+ *
+ *   q        device [B][gamma][H_q][d], kv_dtype
+ *   sel_out  device [B][gamma][H_kv][k] int32 or NULL (lists, -1 padded)
+ *   out      device [B][gamma][H_q][d], kv_dtype
+ *   lse      device [B][gamma][H_q] float, may be NULL
+ *   workspace >= qas_positions_workspace_bytes(cache, batch, H_q, gamma, k),
+ *            16-byte aligned
+ */
+qas_status qas_decode_positions(const qas_cache* cache, const qas_batch* batch,
+                                const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                int32_t gamma, int32_t k, float sm_scale,
+                                int32_t* sel_out, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of qas_decode_positions; 0 for invalid arguments. */
+size_t qas_positions_workspace_bytes(const qas_cache* cache, const qas_batch* batch,
+                                     int32_t num_q_heads, int32_t gamma, int32_t k);
+
 enum { QAS_OP_SPARSE_DECODE = 1, QAS_OP_DECODE_LAYER = 2 };
 
 /*

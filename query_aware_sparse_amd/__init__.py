@@ -63,6 +63,9 @@ _SIGNATURES = {
     "qas_decode_layer_mixed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
                                     _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "qas_workspace_bytes": (ctypes.c_size_t, [_I, _P, _P, _I, _I]),
+    "qas_decode_positions": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
+    "qas_positions_workspace_bytes": (ctypes.c_size_t, [_P, _P, _I, _I, _I]),
     "qas_chunk_groups": (_I, [_I, _I, _I]),
     "qas_regroup_queries": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     "qas_union_pages": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
@@ -224,6 +227,24 @@ def qas_decode_layer_mixed(cache, batch, q, k, sink_tokens, local_tokens, sm_sca
                                           _stream(stream)))
 
 
+def qas_positions_workspace_bytes(cache, batch, num_q_heads, gamma, k):
+    return int(_load().qas_positions_workspace_bytes(ctypes.byref(cache), ctypes.byref(batch),
+                                                     int(num_q_heads), int(gamma), int(k)))
+
+
+def qas_decode_positions(cache, batch, q, k, sm_scale, out, lse, workspace, sel_out=None,
+                         stream=None):
+    """q: [B][gamma][H_q][d] draft-position queries (the drafts already
+    appended); out like q; lse [B][gamma][H_q] or None; sel_out
+    [B][gamma][H_kv][k] or None."""
+    _check(_load().qas_decode_positions(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+                                        dtype_code(q), q.shape[2], q.shape[1], int(k),
+                                        float(sm_scale), _ptr(sel_out), _ptr(out), _ptr(lse),
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
+
+
 def qas_chunk_groups(num_queries, batch, group):
     return int(_load().qas_chunk_groups(int(num_queries), int(batch), int(group)))
 
@@ -262,6 +283,7 @@ def version():
 
 
 __all__ = ["qas_append", "qas_rollback", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
-           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
+           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_decode_positions",
+           "qas_positions_workspace_bytes", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

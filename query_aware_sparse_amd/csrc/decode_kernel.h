@@ -124,9 +124,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   if constexpr (TPT > 0)
     t.issue_x4(a.scores + ((size_t)r * H + h) * a.score_stride,
                a.phys_rows + (size_t)r * a.score_stride, cap);
-  const int L = a.seq_lens[r];
-  const int pbeg = a.page_indptr[r];
-  const int P_r = a.page_indptr[r + 1] - pbeg;
+  // row r: a request, or draft position r % gamma of request r / gamma whose
+  // causal limit is its own position (length seq_lens - (gamma - 1 - i))
+  const int req = r / a.gamma;
+  const int L = a.seq_lens[req] - (a.gamma - 1 - r % a.gamma);
+  const int pbeg = a.page_indptr[req];
+  const int P_r = a.page_indptr[req + 1] - pbeg;
   const int n_pages = L > 0 ? min((L + S - 1) / S, P_r) : 0;
   const int per = (a.sel_len + a.n_split - 1) / a.n_split;
   const int e0 = min(a.sel_len, split * per);

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 
@@ -159,6 +160,7 @@ qas::ScoreArgs score_args(const qas_cache* c, const qas_batch* b, const void* q,
   a.tickets = nullptr;
   a.row_stride = 0;
   a.phys_out = nullptr;
+  a.gamma = 1;
   return a;
 }
 
@@ -194,6 +196,7 @@ qas::DecodeArgs decode_args(const qas_cache* c, const qas_batch* b, const void* 
   a.scores = nullptr;
   a.score_stride = 0;
   a.phys_rows = nullptr;
+  a.gamma = 1;
   a.sel_out = nullptr;
   a.max_pages = b->max_pages;
   a.clear_tickets = 0;
@@ -505,6 +508,77 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return qas_decode_layer_mixed(cache, batch, q, q_dtype, num_q_heads, k, 0, 0, sm_scale, k_new,
                                 v_new, sel_out, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t qas_positions_workspace_bytes(const qas_cache* cache, const qas_batch* batch,
+                                     int32_t num_q_heads, int32_t gamma, int32_t k) {
+  if (!batch || gamma < 1 || batch->batch < 1 || batch->batch > INT32_MAX / gamma) return 0;
+  qas_batch rows = *batch;             // one row per (request, draft position)
+  rows.batch = batch->batch * gamma;
+  return qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, &rows, num_q_heads, k);
+}
+
+qas_status qas_decode_positions(const qas_cache* cache, const qas_batch* batch, const void* q,
+                                int32_t q_dtype, int32_t num_q_heads, int32_t gamma, int32_t k,
+                                float sm_scale, int32_t* sel_out, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  qas_status st = check_cache(cache, true, true);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  int g;
+  if ((st = check_heads(cache, num_q_heads, &g))) return st;
+  if (!q || !out) return fail(QAS_ERR_NULL, "q / out is NULL");
+  if (q_dtype != cache->kv_dtype)
+    return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
+  if (k < 1) return fail(QAS_ERR_SHAPE, "k %d < 1", k);
+  if (gamma < 1 || batch->batch > INT32_MAX / gamma)
+    return fail(QAS_ERR_SHAPE, "gamma %d out of range", gamma);
+  if (!layer_fused_topk(batch))
+    return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed the in-kernel top-k (%d)",
+                batch->max_pages, qas::decode_fused_topk_max_pages());
+  qas_batch rows = *batch;             // one row per (request, draft position)
+  rows.batch = batch->batch * gamma;
+  const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, &rows, num_q_heads, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(QAS_ERR_WORKSPACE, "workspace %p is not 16-byte aligned", workspace);
+  if (!qas::score_supported(cache->kv_dtype, cache->head_dim, g, cache->num_kv_heads))
+    return fail(QAS_ERR_UNSUPPORTED, "score: %d KV heads of d=%d", cache->num_kv_heads,
+                cache->head_dim);
+  hipStream_t s = (hipStream_t)stream;
+  const DecodePlan p = plan_decode(cache, &rows, num_q_heads, k);
+  char* ws = (char*)workspace;
+  float* scores = (float*)ws;
+  ws += layer_scores_bytes(cache, &rows);
+  int32_t* phys_rows = (int32_t*)ws;
+  ws += layer_phys_bytes(&rows);
+  float* partials = (float*)ws;
+  ws += p.partial_bytes;
+  unsigned int* tickets = (unsigned int*)ws;
+
+  // 1. page bounds of every position's query over the pages it may see
+  hipError_t e;
+  qas::ScoreArgs sa = score_args(cache, &rows, q, num_q_heads, g, scores);
+  sa.tickets = tickets;
+  sa.row_stride = layer_score_stride(&rows);
+  sa.phys_out = phys_rows;
+  sa.gamma = gamma;
+  if ((e = qas::launch_score(sa, s)) != hipSuccess) return hip_fail(e, "score launch");
+  // 2. + 3. top-k per (position, KV head) and attention inside one kernel
+  qas::DecodeArgs da = decode_args(cache, &rows, q, num_q_heads, g, nullptr, k, k, sm_scale, out,
+                                   lse, partials, p.n_split, 0);
+  da.tickets = tickets;
+  da.k = k;
+  da.sink_tokens = 0;
+  da.local_tokens = 0;
+  da.scores = scores;
+  da.score_stride = layer_score_stride(&rows);
+  da.phys_rows = phys_rows;
+  da.sel_out = sel_out;
+  da.gamma = gamma;
+  if ((e = qas::launch_decode(da, s)) != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
 }
 
 int32_t qas_chunk_groups(int32_t num_queries, int32_t batch, int32_t group) {

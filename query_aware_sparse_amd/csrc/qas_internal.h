@@ -17,6 +17,8 @@ struct ScoreArgs {
   float* scores;             // row_stride 0: [pbeg*H_kv + h*P_r + j], else [(r*H_kv + h)*row_stride + j]
   int row_stride;
   int32_t* phys_out;         // optional (row_stride > 0): [r*row_stride + j] physical page of page j
+  int gamma;                 // rows per request: row r is draft position r % gamma of request
+                             // r / gamma, of length seq_lens - (gamma - 1 - r % gamma)
   // optional decode append of the token at seq_lens[r] - 1 (k_new != NULL)
   const void* k_new;         // [B][H_kv][d]
   const void* v_new;
@@ -91,6 +93,7 @@ struct DecodeArgs {
   const float* scores;
   int score_stride;          // row stride of scores (>= max_pages, a multiple of 4)
   const int32_t* phys_rows;  // [B][score_stride] physical page of each scored page
+  int gamma;                 // rows per request (draft positions), as in ScoreArgs
   int32_t* sel_out;          // optional [B][H_kv][sel_len] copy of the selection
   int max_pages;
   int k;                     // in-kernel top-K: pages Quest selects per row

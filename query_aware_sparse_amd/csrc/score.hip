@@ -59,9 +59,10 @@ __global__ __launch_bounds__(1024) void score_kernel(ScoreArgs a) {
   const int j0 = blockIdx.x * PPI * kScoreUnroll;
 
   // level 1: request bounds, query slices, the appended token
-  const int pbeg = a.page_indptr[r];
-  const int P_r = a.page_indptr[r + 1] - pbeg;
-  const int L = a.seq_lens[r];
+  const int req = r / a.gamma;                // request of the row (draft positions)
+  const int pbeg = a.page_indptr[req];
+  const int P_r = a.page_indptr[req + 1] - pbeg;
+  const int L = a.seq_lens[req] - (a.gamma - 1 - r % a.gamma);
   float qf[G][EPL];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
@@ -185,9 +186,10 @@ __global__ __launch_bounds__(512) void score8_kernel(ScoreArgs a) {
   const int d0 = c * 16;                      // this lane's 16 dims
 
   // level 1: request bounds, query slices, the appended token
-  const int pbeg = a.page_indptr[r];
-  const int P_r = a.page_indptr[r + 1] - pbeg;
-  const int L = a.seq_lens[r];
+  const int req = r / a.gamma;                // request of the row (draft positions)
+  const int pbeg = a.page_indptr[req];
+  const int P_r = a.page_indptr[req + 1] - pbeg;
+  const int L = a.seq_lens[req] - (a.gamma - 1 - r % a.gamma);
   constexpr int EPL = epl<DT>();
   float qf[G][16];
 #pragma unroll
