@@ -367,6 +367,30 @@ qas_status qas_decode_positions(const qas_cache* cache, const qas_batch* batch,
                                 int32_t* sel_out, void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * qas_exact_top_r - exact token top-R per (request, query head) with a
+ * branch-and-bound certificate ([Quest] §3.2, stopping rules beyond a fixed
+ * top-K): pages are read in descending order of this head's bound (eq.
+ * (2)-(3) with its own query; ties to the lower page index), and the search
+ * stops when the next page's bound is below tau_R, the R-th largest logit
+ * read so far; no token of an unread page can then enter the top R.  The
+ * bound is raised by 2^-15 * sum_j |q_j| max(|m_j|, |M_j|) so that fp32
+ * rounding of bounds and logits cannot end the search early.  Logits are the
+ * unscaled dot products q . k_t (fp32) over tokens t < seq_lens[r]; the
+ * number of pages read is data dependent (up to all of them).
+ *
+ *   q           device [B][H_q][d], kv_dtype (fp32, fp16 or bf16 caches)
+ *   R           1 .. 512; requests of up to 4096 pages (else QAS_ERR_UNSUPPORTED)
+ *   top_tokens  device [B][H_q][R] int32: token positions ordered by logit
+ *               descending, then position ascending; -1 past the tokens held
+ *   top_logits  device [B][H_q][R] float: their logits, -inf past the end
+ *   pages_read  device [B][H_q] int32 or NULL: pages opened before the stop
+ */
+qas_status qas_exact_top_r(const qas_cache* cache, const qas_batch* batch, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, int32_t R,
+                           int32_t* top_tokens, float* top_logits, int32_t* pages_read,
+                           void* stream);
+
 /* Workspace of qas_decode_positions; 0 for invalid arguments. */
 size_t qas_positions_workspace_bytes(const qas_cache* cache, const qas_batch* batch,
                                      int32_t num_q_heads, int32_t gamma, int32_t k);

@@ -29,7 +29,7 @@ FLAGS = [
 ]
 
 SOURCES = ["qas_api.cpp", "append.hip", "score.hip", "topk.hip", "decode.hip", "decode_f32.hip",
-           "decode_f16.hip", "decode_bf16.hip", "union.hip", "regroup.hip"]
+           "decode_f16.hip", "decode_bf16.hip", "union.hip", "regroup.hip", "topr.hip"]
 
 
 def _compile(src, verbose):

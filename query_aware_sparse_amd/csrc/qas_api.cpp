@@ -510,6 +510,47 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
                                 v_new, sel_out, out, lse, workspace, workspace_bytes, stream);
 }
 
+qas_status qas_exact_top_r(const qas_cache* cache, const qas_batch* batch, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, int32_t R, int32_t* top_tokens,
+                           float* top_logits, int32_t* pages_read, void* stream) {
+  qas_status st = check_cache(cache, true, true);
+  if (st) return st;
+  if ((st = check_batch(batch))) return st;
+  int g;
+  if ((st = check_heads(cache, num_q_heads, &g))) return st;
+  if (!q || !top_tokens || !top_logits) return fail(QAS_ERR_NULL, "q / top_tokens / top_logits is NULL");
+  if (q_dtype != cache->kv_dtype)
+    return fail(QAS_ERR_DTYPE, "q_dtype %d must equal kv_dtype %d", q_dtype, cache->kv_dtype);
+  if (R < 1) return fail(QAS_ERR_SHAPE, "R %d < 1", R);
+  if (R > qas::topr_max_r())
+    return fail(QAS_ERR_UNSUPPORTED, "R %d > %d", R, qas::topr_max_r());
+  if (batch->max_pages > qas::topr_max_pages())
+    return fail(QAS_ERR_UNSUPPORTED, "rows of %d pages exceed %d", batch->max_pages,
+                qas::topr_max_pages());
+  if (cache->kv_dtype == QAS_FP8_E4M3)
+    return fail(QAS_ERR_UNSUPPORTED, "exact top-R reads fp32/fp16/bf16 keys");
+  qas::ToprArgs a;
+  a.k_pool = cache->k_pool;
+  a.summary = cache->summary;
+  a.q = q;
+  a.seq_lens = batch->seq_lens;
+  a.page_indptr = batch->page_indptr;
+  a.page_indices = batch->page_indices;
+  a.top_tokens = top_tokens;
+  a.top_logits = top_logits;
+  a.pages_read = pages_read;
+  a.B = batch->batch;
+  a.H_kv = cache->num_kv_heads;
+  a.H_q = num_q_heads;
+  a.d = cache->head_dim;
+  a.S = cache->page_size;
+  a.kv_dtype = cache->kv_dtype;
+  a.R = R;
+  hipError_t e = qas::launch_topr(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-R launch");
+  return ok();
+}
+
 size_t qas_positions_workspace_bytes(const qas_cache* cache, const qas_batch* batch,
                                      int32_t num_q_heads, int32_t gamma, int32_t k) {
   if (!batch || gamma < 1 || batch->batch < 1 || batch->batch > INT32_MAX / gamma) return 0;

@@ -75,6 +75,22 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 bool append_supported(int kv_dtype, int d);
 
+struct ToprArgs {
+  const void* k_pool;
+  const void* summary;
+  const void* q;             // [B][H_q][d]
+  const int32_t* seq_lens;
+  const int32_t* page_indptr;
+  const int32_t* page_indices;
+  int32_t* top_tokens;       // [B][H_q][R]
+  float* top_logits;         // [B][H_q][R]
+  int32_t* pages_read;       // optional [B][H_q]
+  int B, H_kv, H_q, d, S, kv_dtype, R;
+};
+hipError_t launch_topr(const ToprArgs& a, hipStream_t s);
+int topr_max_pages();
+int topr_max_r();
+
 struct DecodeArgs {
   const void* k_pool;
   const void* v_pool;
