@@ -359,6 +359,54 @@ def time_decode_calls(torch, args, NL, call, out):
     return wall * 1e3 / steps, call_us, steps
 
 
+def bench_next_rows(torch, qas, args, case, exact, db, qs, NL):
+    """Timings of the NEXT-4 entry points on the same layer caches, replayed
+    from a HIP graph like the decode-layer call: a 4-token speculative
+    verification block (qas_decode_positions, the last 4 tokens taken as the
+    drafts), the exact top-64 tokens by branch-and-bound (qas_exact_top_r),
+    and the tail rescan of a rollback (qas_rollback to a cut 5 tokens back,
+    run last since it rewrites the tail record)."""
+    from query_aware_sparse_amd.staging import DeviceBatch, to_device
+    from workloads.cases import cast
+    gamma, R = 4, 64
+    dev = qs.device
+    rng = np.random.default_rng(4)
+    qpos = to_device(cast(rng.standard_normal((NL, 1, gamma, case.H_q, case.d)), case.q_dtype),
+                     case.q_dtype)
+    out_pos = torch.empty((NL, 1, gamma, case.H_q, case.d), dtype=qpos.dtype, device=dev)
+    ws_pos = torch.zeros(qas.qas_positions_workspace_bytes(exact[0], db.batch, case.H_q, gamma,
+                                                           case.K), dtype=torch.uint8, device=dev)
+
+    def call_pos(i):
+        qas.qas_decode_positions(exact[i], db.batch, qpos[i], case.K, case.sm_scale, out_pos[i],
+                                 None, ws_pos)
+
+    tok = torch.empty((NL, 1, case.H_q, R), dtype=torch.int32, device=dev)
+    lg = torch.empty((NL, 1, case.H_q, R), dtype=torch.float32, device=dev)
+    pr = torch.zeros((NL, 1, case.H_q), dtype=torch.int32, device=dev)
+
+    def call_topr(i):
+        qas.qas_exact_top_r(exact[i], db.batch, qs[i], R, tok[i], lg[i], pr[i])
+
+    L = int(case.seq_lens[0])
+    cut = DeviceBatch(np.array([L - 5], np.int32), case.pages, case.S, device=dev)
+
+    def call_rb(i):
+        qas.qas_rollback(exact[i], cut.batch)
+
+    res = {}
+    for name, fn, o in (("speculative_positions_gamma4", call_pos, out_pos),
+                        ("exact_top_r_64", call_topr, tok), ("rollback_rescan", call_rb, pr)):
+        _, us, _ = time_decode_calls(torch, args, NL, fn, o)
+        res[name] = {"us_per_call": round(us, 3)}
+        log(f"[bench] {name}: {us:.2f} us/call")
+    prh = pr.cpu().numpy()
+    res["exact_top_r_64"]["pages_read_per_head"] = {
+        "mean": round(float(prh.mean()), 1), "min": int(prh.min()), "max": int(prh.max()),
+        "of": L // case.S}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -435,6 +483,7 @@ def main():
 
     ms_per_step, call_us, steps = time_decode_calls(torch, args, NL, call, out)
     ms_fp8, us_fp8, _ = time_decode_calls(torch, args, NL, call_fp8, out)
+    next_rows = bench_next_rows(torch, qas, args, case, exact, db, qs, NL)
     bytes_fp8 = traffic.decode_layer_bytes(
         B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
         pages_scanned=L // case.S, page_heads_selected=case.H_kv * case.K,
@@ -468,7 +517,8 @@ def main():
                        "us_per_call": round(us_fp8, 3), "bytes_per_call": bytes_fp8,
                        "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
                        "ms_per_step_wall": round(ms_fp8, 6),
-                       "traffic": pmc_traffic_bytes(fp8=True)}},
+                       "traffic": pmc_traffic_bytes(fp8=True)},
+                   "next_rows": next_rows},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic_bytes(),
