@@ -31,7 +31,8 @@
  *
  * Layouts (row-major, innermost last)
  * -----------------------------------
- *   K / V pool  [num_pool_pages][H_kv][S][d]          kv_dtype
+ *   K / V pool  [num_pool_pages][H_kv][S][d]          kv_dtype (an FP8 V pool:
+ *                                                     see qas_chunk_attention)
  *   summary     [num_pool_pages][H_kv][2][d]          kv_dtype, [..][0] = min m,
  *                                                     [..][1] = max M ([Quest] eq. (1))
  *   q, out      [B][H_q][d]                           q_dtype (out has q's dtype)
@@ -323,7 +324,11 @@ qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr,
 /*
  * qas_chunk_attention - attention of every query of the chunk over its own
  * support, executed over group unions with MFMA tiles.  The cache must be
- * FP8 E4M3 with k_scale/v_scale (k = k_scale[h] * code); q is bf16
+ * FP8 E4M3 with k_scale/v_scale (k = k_scale[h] * code).  Its V pool is laid
+ * out for the MFMA operand: each (page, KV head) is [d][S] (dimension-major)
+ * and token t of the page (w = t % 32, tau = t / 32) sits at position
+ * (S/2)*((w/4) % 2) + 16*tau + 4*(w/8) + w % 4 of each dim row; K keeps
+ * [S][d].  q is bf16
  * [N][H_q][128]; out is bf16 [N][H_q][128], lse float [N][H_q] (may be
  * NULL).  Page size 32 or 64.  QK^T runs with the query row quantised to
  * e4m3 (per-row scale) and PV with probabilities scaled by 256 and

@@ -17,9 +17,11 @@
 //      e4m3 as B (v_mfma 32x32x64 f8f6f4); each lane then owns one row's
 //      logits, so the mask (membership, t <= c_i, t < L) and the online
 //      softmax are lane-local; P is scaled by 256 and quantised to e4m3 and
-//      feeds O^T += V^T P^T from registers, V^T being gathered from the
-//      page staged in LDS (rows padded to 136 bytes: conflict-free byte
-//      reads);
+//      feeds O^T += V^T P^T from registers.  The fp8 V pool stores each
+//      (page, head) dimension-major, [d][S], with the tokens of a dim row in
+//      the order of the MFMA's k slots (those of the P bytes a lane holds),
+//      so every lane loads its V^T operand as S/2 contiguous bytes: no LDS
+//      staging or byte gathers;
 //   3. the four waves' states are merged in LDS and written at the queries'
 //      own output rows.
 #include "qas_device.h"
@@ -39,7 +41,6 @@ constexpr int kUMaxGroup = 8;               // queries per group (membership byt
 constexpr int kUMaxWords = 512;             // bitmap words: pages < 16384
 constexpr int kUMaxUnion = 1024;            // union pages per group
 constexpr int kUD = 128;                    // head dim
-constexpr int kUVStride = 136;              // LDS row stride of a staged V page
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct UnionShared {
@@ -159,13 +160,6 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   return total;
 }
 
-// order this wave's LDS accesses (a staged page is written and read by the
-// same wave only)
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 __device__ __forceinline__ float lane_rowsum(float v) { return v + __shfl_xor(v, 32, kWave); }
 __device__ __forceinline__ float lane_rowmax(float v) { return fmaxf(v, __shfl_xor(v, 32, kWave)); }
 
@@ -179,7 +173,7 @@ template <int G, int NT>
 __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   constexpr int S = 32 * NT;                  // page size
   __shared__ UnionShared sh;
-  __shared__ __align__(16) unsigned char vstage[kUWaves][64 * kUVStride];
+  __shared__ __align__(16) float red_buf[2][32][kUD + 2];   // wave merge
 
   const int H = a.H_kv;
   const int h = blockIdx.x % H;
@@ -239,14 +233,10 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
 
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
-  unsigned char* vs = vstage[wave];
 
-  for (int u = wave; u < U; u += kUWaves) {
-    const int id = sh.ulist[u];
-    const unsigned char mk = sh.umask[u];
+  // K operand of union page u: token 32*tau + lane%32, dims 64*ks + 32*hf + [0, 32)
+  auto load_k = [&](int u, v8i_t (&kk)[NT][2]) {
     const size_t tile = ((size_t)sh.uphys[u] * H + h) * S * kUD;   // bytes (fp8)
-    // K operand: token 32*tau + lane%32, dims 64*ks + 32*hf + [0, 32)
-    v8i_t kop[NT][2];
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
@@ -254,23 +244,39 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
         const char* p = kbase + tile + (size_t)(32 * tau + row) * kUD + 64 * ks + 32 * hf;
         const uint4 x0 = load16(p), x1 = load16(p + 16);
         const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        kop[tau][ks] = *reinterpret_cast<const v8i_t*>(w);
+        kk[tau][ks] = *reinterpret_cast<const v8i_t*>(w);
       }
-    // V page -> LDS, rows of kUVStride bytes (8-byte stores)
-    wave_lds_sync();                          // previous page's reads are done
-    uint4 vv[S * kUD / 16 / kWave];
+  };
+  // V^T operand of union page u: the fp8 V pool holds each (page, head) as
+  // [d][S] with the tokens of a dim row in the order the PV MFMA's k slots
+  // take them, so lane (dim 32 dt + row, hf) reads its S/2 bytes in one go
+  auto load_v = [&](int u, v8i_t (&vv)[4]) {
+    const size_t tile = ((size_t)sh.uphys[u] * H + h) * S * kUD;
 #pragma unroll
-    for (int c = 0; c < S * kUD / 16 / kWave; ++c)
-      vv[c] = load16(vbase + tile + (size_t)(c * kWave + lane) * 16);
-#pragma unroll
-    for (int c = 0; c < S * kUD / 16 / kWave; ++c) {
-      const int chunk = c * kWave + lane;
-      const int t = chunk / (kUD / 16), off = (chunk % (kUD / 16)) * 16;
-      uint2* dst = reinterpret_cast<uint2*>(vs + t * kUVStride + off);
-      dst[0] = make_uint2(vv[c].x, vv[c].y);
-      dst[1] = make_uint2(vv[c].z, vv[c].w);
+    for (int dt = 0; dt < 4; ++dt) {
+      const char* vr = vbase + tile + (size_t)(32 * dt + row) * S + (S / 2) * hf;
+      uint32_t vw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const uint4 y0 = load16(vr);
+      vw[0] = y0.x;
+      vw[1] = y0.y;
+      vw[2] = y0.z;
+      vw[3] = y0.w;
+      if constexpr (NT == 2) {
+        const uint4 y1 = load16(vr + 16);
+        vw[4] = y1.x;
+        vw[5] = y1.y;
+        vw[6] = y1.z;
+        vw[7] = y1.w;
+      }
+      vv[dt] = *reinterpret_cast<const v8i_t*>(vw);
     }
-    wave_lds_sync();                          // staged page visible to the wave
+  };
+  for (int u = wave; u < U; u += kUWaves) {
+    const int id = sh.ulist[u];
+    const unsigned char mk = sh.umask[u];
+    v8i_t kop[NT][2], vop[4];
+    load_k(u, kop);
+    load_v(u, vop);
     // S^T = K Q^T: lane holds row `row`, tokens 32 tau + 8 (e/4) + 4 hf + e%4
     v16f_t st[NT];
 #pragma unroll
@@ -322,26 +328,16 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
       m_run = m_new;
     }
     const v8i_t pop = *reinterpret_cast<const v8i_t*>(pw);
-    // O^T += V^T P^T: A lane (dim 32 dt + lane%32, hf) gathers the same 32
-    // tokens, in the same order, as the lane's P bytes
+    // O^T += V^T P^T: lane (dim 32 dt + lane%32, hf) holds the same k slots
+    // (tokens 32 tau + 8 (e/4) + 4 hf + e%4) as its P bytes
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      uint32_t vw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const int dim = 32 * dt + row;
-#pragma unroll
-      for (int k = 0; k < 16 * NT; ++k) {
-        const int tau = k / 16, e = k % 16;
-        const int t = 32 * tau + 8 * (e / 4) + 4 * hf + (e % 4);
-        vw[k / 4] |= (uint32_t)vs[t * kUVStride + dim] << (8 * (k % 4));
-      }
-      const v8i_t vop = *reinterpret_cast<const v8i_t*>(vw);
-      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[dt], 0, 0, 0, 0, 0,
-                                                                0);
-    }
+    for (int dt = 0; dt < 4; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[dt], pop, acc[dt], 0, 0, 0, 0,
+                                                                0, 0);
   }
 
-  // ---- merge the waves: 2,3 -> 0,1 then 1 -> 0 (V staging area reused) -----
-  float* red = reinterpret_cast<float*>(&vstage[0][0]);   // [2][32 rows][130]
+  // ---- merge the waves: 2,3 -> 0,1 then 1 -> 0 ------------------------------
+  float* red = &red_buf[0][0][0];            // [2][32 rows][130]
   constexpr int RS = kUD + 2;
   __syncthreads();
 #pragma unroll

@@ -106,10 +106,23 @@ def prefill(pc, case, lengths=None, device="cuda"):
     return full
 
 
+def mfma_token_order(S):
+    """Token held at each position of a dim row of an fp8 V page ([d][S] per
+    (page, KV head)): the order of the k slots of the union kernel's PV MFMA.
+    Token t (w = t % 32, tau = t // 32) sits at (S/2) * ((w // 4) % 2) +
+    16 * tau + 4 * (w // 8) + w % 4."""
+    order = np.empty(S, np.int64)
+    for t in range(S):
+        w, tau = t % 32, t // 32
+        order[(S // 2) * ((w // 4) % 2) + 16 * tau + 4 * (w // 8) + w % 4] = t
+    return order
+
+
 class ChunkBatch:
     """Device state of one or more multi-query chunks (one per request) sharing
     an fp8 pool: pages of request r are placed after those of r - 1.  K/V
-    tokens go to their pages by plain copies (this path reads no summaries)."""
+    tokens go to their pages by plain copies (this path reads no summaries):
+    K as [page][H][S][d], V as [page][H][d][S] in mfma_token_order(S)."""
 
     def __init__(self, cases, device="cuda"):
         c0 = cases[0]
@@ -118,7 +131,8 @@ class ChunkBatch:
         pool = sum(c.num_pool_pages for c in cases)
         shape = (pool, H, S, d)
         self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)   # e4m3 NaN
-        self.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
+        self.v_pool = torch.full((pool, H, d, S), 0x7F, dtype=torch.uint8, device=device)
+        order = torch.from_numpy(mfma_token_order(S)).to(device)
         lengths, pages, off = [], [], 0
         for c in cases:
             P = ceil_div(c.L, S)
@@ -127,6 +141,8 @@ class ChunkBatch:
                 t = np.zeros((P * S, H, d), np.uint8)
                 t[:c.L] = raw[:c.L]
                 tt = torch.from_numpy(t).to(device).view(P, S, H, d).permute(0, 2, 1, 3)
+                if pool_t is self.v_pool:           # [P][H][d][S], tokens in MFMA order
+                    tt = tt.permute(0, 1, 3, 2)[..., order]
                 pool_t[phys] = tt.contiguous()
             lengths.append(c.L)
             pages.append(np.asarray(c.pages[:P], np.int32) + off)
