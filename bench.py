@@ -384,9 +384,11 @@ def bench_next_rows(torch, qas, args, case, exact, db, qs, NL):
     tok = torch.empty((NL, 1, case.H_q, R), dtype=torch.int32, device=dev)
     lg = torch.empty((NL, 1, case.H_q, R), dtype=torch.float32, device=dev)
     pr = torch.zeros((NL, 1, case.H_q), dtype=torch.int32, device=dev)
+    ws_topr = torch.zeros(qas.qas_exact_top_r_workspace_bytes(exact[0], db.batch, case.H_q, R),
+                          dtype=torch.uint8, device=dev)
 
     def call_topr(i):
-        qas.qas_exact_top_r(exact[i], db.batch, qs[i], R, tok[i], lg[i], pr[i])
+        qas.qas_exact_top_r(exact[i], db.batch, qs[i], R, tok[i], lg[i], ws_topr, pages_read=pr[i])
 
     L = int(case.seq_lens[0])
     cut = DeviceBatch(np.array([L - 5], np.int32), case.pages, case.S, device=dev)

@@ -382,7 +382,12 @@ qas_status qas_decode_positions(const qas_cache* cache, const qas_batch* batch,
  * bound is raised by 2^-15 * sum_j |q_j| max(|m_j|, |M_j|) so that fp32
  * rounding of bounds and logits cannot end the search early.  Logits are the
  * unscaled dot products q . k_t (fp32) over tokens t < seq_lens[r]; the
- * number of pages read is data dependent (up to all of them).
+ * number of pages read is data dependent (up to all of them).  Three
+ * launches: per row a pilot reads pages in bound order (up to 64 pages) and
+ * finishes the row if the stop rule fires; otherwise every page whose bound
+ * is not below the pilot's tau_R (which can only rise) is read by many
+ * workgroups at once, and a merge keeps the best R.  pages_read counts the
+ * pilot's pages and the pages read after it.
  *
  *   q           device [B][H_q][d], kv_dtype (fp32, fp16 or bf16 caches)
  *   R           1 .. 512; requests of up to 4096 pages (else QAS_ERR_UNSUPPORTED)
@@ -394,7 +399,11 @@ qas_status qas_decode_positions(const qas_cache* cache, const qas_batch* batch,
 qas_status qas_exact_top_r(const qas_cache* cache, const qas_batch* batch, const void* q,
                            int32_t q_dtype, int32_t num_q_heads, int32_t R,
                            int32_t* top_tokens, float* top_logits, int32_t* pages_read,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of qas_exact_top_r (16-byte aligned); 0 for invalid arguments. */
+size_t qas_exact_top_r_workspace_bytes(const qas_cache* cache, const qas_batch* batch,
+                                       int32_t num_q_heads, int32_t R);
 
 /* Workspace of qas_decode_positions; 0 for invalid arguments. */
 size_t qas_positions_workspace_bytes(const qas_cache* cache, const qas_batch* batch,

@@ -66,7 +66,8 @@ _SIGNATURES = {
     "qas_decode_positions": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
     "qas_positions_workspace_bytes": (ctypes.c_size_t, [_P, _P, _I, _I, _I]),
-    "qas_exact_top_r": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "qas_exact_top_r": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "qas_exact_top_r_workspace_bytes": (ctypes.c_size_t, [_P, _P, _I, _I]),
     "qas_chunk_groups": (_I, [_I, _I, _I]),
     "qas_regroup_queries": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     "qas_union_pages": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
@@ -246,12 +247,21 @@ def qas_decode_positions(cache, batch, q, k, sm_scale, out, lse, workspace, sel_
                                         _stream(stream)))
 
 
-def qas_exact_top_r(cache, batch, q, R, top_tokens, top_logits, pages_read=None, stream=None):
+def qas_exact_top_r_workspace_bytes(cache, batch, num_q_heads, R):
+    return int(_load().qas_exact_top_r_workspace_bytes(ctypes.byref(cache), ctypes.byref(batch),
+                                                       int(num_q_heads), int(R)))
+
+
+def qas_exact_top_r(cache, batch, q, R, top_tokens, top_logits, workspace, pages_read=None,
+                    stream=None):
     """Exact token top-R per (request, query head) by branch-and-bound over
-    the page bounds; q [B][H_q][d], outputs [B][H_q][R] (see qas.h)."""
+    the page bounds; q [B][H_q][d], outputs [B][H_q][R], workspace of
+    qas_exact_top_r_workspace_bytes (see qas.h)."""
     _check(_load().qas_exact_top_r(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
                                    dtype_code(q), q.shape[1], int(R), _ptr(top_tokens),
-                                   _ptr(top_logits), _ptr(pages_read), _stream(stream)))
+                                   _ptr(top_logits), _ptr(pages_read), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
 
 
 def qas_chunk_groups(num_queries, batch, group):
@@ -293,6 +303,7 @@ def version():
 
 __all__ = ["qas_append", "qas_rollback", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
            "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_decode_positions",
-           "qas_positions_workspace_bytes", "qas_exact_top_r", "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
+           "qas_positions_workspace_bytes", "qas_exact_top_r", "qas_exact_top_r_workspace_bytes",
+           "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",
            "qas_cache", "qas_batch", "QasError", "version", "lib", "LIB_PATH"]

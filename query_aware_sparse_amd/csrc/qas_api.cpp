@@ -510,9 +510,38 @@ qas_status qas_decode_layer(const qas_cache* cache, const qas_batch* batch, cons
                                 v_new, sel_out, out, lse, workspace, workspace_bytes, stream);
 }
 
+// Workspace of qas_exact_top_r, carved in this order (each part 256-aligned).
+struct ToprPlan {
+  size_t state, pages, pilot, chunks, counts;
+  int page_stride, scan_chunks;
+  size_t total() const { return state + pages + pilot + chunks + counts; }
+};
+ToprPlan plan_topr(const qas_cache* c, const qas_batch* b, int num_q_heads, int R) {
+  ToprPlan p;
+  const size_t rows = (size_t)b->batch * num_q_heads;
+  p.page_stride = b->max_pages > 0 ? b->max_pages : 1;
+  const int per_chunk = qas::topr_threads() / c->page_size;   // pages a scan workgroup reads
+  p.scan_chunks = (p.page_stride + per_chunk - 1) / per_chunk;
+  p.state = align256(rows * 4 * sizeof(int));
+  p.pages = align256(rows * p.page_stride * sizeof(uint64_t));
+  p.pilot = align256(rows * R * sizeof(uint64_t));
+  p.chunks = align256(rows * p.scan_chunks * R * sizeof(uint64_t));
+  p.counts = align256(rows * p.scan_chunks * sizeof(int));
+  return p;
+}
+
+size_t qas_exact_top_r_workspace_bytes(const qas_cache* cache, const qas_batch* batch,
+                                       int32_t num_q_heads, int32_t R) {
+  if (!cache || !batch || batch->batch < 1 || num_q_heads < 1 || R < 1 ||
+      !pow2_in(cache->page_size, 1, 256))
+    return 0;
+  return plan_topr(cache, batch, num_q_heads, R).total();
+}
+
 qas_status qas_exact_top_r(const qas_cache* cache, const qas_batch* batch, const void* q,
                            int32_t q_dtype, int32_t num_q_heads, int32_t R, int32_t* top_tokens,
-                           float* top_logits, int32_t* pages_read, void* stream) {
+                           float* top_logits, int32_t* pages_read, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   qas_status st = check_cache(cache, true, true);
   if (st) return st;
   if ((st = check_batch(batch))) return st;
@@ -529,7 +558,25 @@ qas_status qas_exact_top_r(const qas_cache* cache, const qas_batch* batch, const
                 qas::topr_max_pages());
   if (cache->kv_dtype == QAS_FP8_E4M3)
     return fail(QAS_ERR_UNSUPPORTED, "exact top-R reads fp32/fp16/bf16 keys");
+  const ToprPlan tp = plan_topr(cache, batch, num_q_heads, R);
+  if (!workspace || workspace_bytes < tp.total())
+    return fail(QAS_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, tp.total());
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(QAS_ERR_WORKSPACE, "workspace %p is not 16-byte aligned", workspace);
   qas::ToprArgs a;
+  char* ws = (char*)workspace;
+  a.ws_state = (int*)ws;
+  ws += tp.state;
+  a.ws_pages = (uint64_t*)ws;
+  ws += tp.pages;
+  a.ws_pilot = (uint64_t*)ws;
+  ws += tp.pilot;
+  a.ws_chunks = (uint64_t*)ws;
+  ws += tp.chunks;
+  a.ws_counts = (int*)ws;
+  a.page_stride = tp.page_stride;
+  a.scan_chunks = tp.scan_chunks;
+  a.pilot_pages = 64;
   a.k_pool = cache->k_pool;
   a.summary = cache->summary;
   a.q = q;

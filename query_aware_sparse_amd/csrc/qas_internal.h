@@ -86,10 +86,18 @@ struct ToprArgs {
   float* top_logits;         // [B][H_q][R]
   int32_t* pages_read;       // optional [B][H_q]
   int B, H_kv, H_q, d, S, kv_dtype, R;
+  // workspace, per row (request, query head)
+  int* ws_state;             // [rows][4]: finished, pilot pages, pages left to scan, pilot kept
+  uint64_t* ws_pages;        // [rows][page_stride] page sort keys
+  uint64_t* ws_pilot;        // [rows][R] the pilot's best keys
+  uint64_t* ws_chunks;       // [rows][scan_chunks][R] each chunk's best keys
+  int* ws_counts;            // [rows][scan_chunks]
+  int page_stride, scan_chunks, pilot_pages;
 };
 hipError_t launch_topr(const ToprArgs& a, hipStream_t s);
 int topr_max_pages();
 int topr_max_r();
+int topr_threads();
 
 struct DecodeArgs {
   const void* k_pool;

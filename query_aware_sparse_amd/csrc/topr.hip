@@ -21,6 +21,7 @@
 // ascending) are unique, so ties between logits go to the lower token).
 #include "qas_device.h"
 #include "qas_internal.h"
+#include "topk_block.h"
 
 namespace qas {
 
@@ -31,6 +32,7 @@ constexpr int kTrWaves = kTrThreads / kWave;
 constexpr int kTrMaxPages = 4096;
 constexpr int kTrMaxR = 512;
 constexpr int kTrBuf = kTrMaxR + kTrThreads;     // kept + new candidates of a round
+constexpr int kTrMaxPilot = 64;                  // pages of the pilot
 
 // 64-bit key, ascending = value descending then index ascending
 __device__ __forceinline__ uint64_t desc_key(float v, uint32_t idx) {
@@ -79,129 +81,374 @@ __device__ void bitonic_sort(uint64_t* s, int n) {
     }
 }
 
+// Rank merge of the sorted best `kept` keys of buf[cur] with `total` unsorted
+// keys appended after them (keys unique); the best min(kept + total, R) go
+// to buf[cur ^ 1] in order.  Every thread calls it; ends with a barrier.
+__device__ void rank_merge(uint64_t (*buf)[kTrBuf], int& cur, int& kept, int total, int R) {
+  const int n = kept + total;
+  for (int i = threadIdx.x; i < n; i += kTrThreads) {
+    const uint64_t x = buf[cur][i];
+    int rank = 0;
+    if (i < kept) {
+      rank = i;
+    } else {
+      int lo = 0, hi = kept;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (buf[cur][mid] < x) lo = mid + 1; else hi = mid;
+      }
+      rank = lo;
+    }
+    for (int q = kept; q < n; ++q) rank += buf[cur][q] < x ? 1 : 0;
+    if (rank < R) buf[cur ^ 1][rank] = x;
+  }
+  kept = min(n, R);
+  cur ^= 1;
+  __syncthreads();
+}
+
+// key of token `off` of physical page `phys` for this head (logit q . k in fp32)
 template <int DT, int D>
-__global__ __launch_bounds__(kTrThreads) void topr_kernel(ToprArgs a) {
+__device__ __forceinline__ uint64_t token_key(const ToprArgs& a, const float* s_q, int phys, int h,
+                                              int off, int t) {
   constexpr int EPL = epl<DT>();
   constexpr int BYTES = DType<DT>::bytes;
-  __shared__ uint64_t s_pages[kTrMaxPages];
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const size_t row = (((size_t)phys * a.H_kv + h) * a.S + off) * D;
+  float z = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < D / EPL; ++c) {
+    float k[EPL];
+    unpack16<DT>(load16(kpool + (row + c * EPL) * BYTES), k);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) z += s_q[c * EPL + e] * k[e];
+  }
+  return desc_key(z, (uint32_t)t);
+}
+
+// the row's query head in LDS; returns P (pages of the row)
+template <int DT, int D>
+__device__ __forceinline__ int row_setup(const ToprArgs& a, float* s_q, int r, int qh, int& L,
+                                         int& pbeg) {
+  L = a.seq_lens[r];
+  pbeg = a.page_indptr[r];
+  const int P_r = a.page_indptr[r + 1] - pbeg;
+  const size_t orow = (size_t)r * a.H_q + qh;
+  for (int d = threadIdx.x; d < D; d += kTrThreads) s_q[d] = load_scalar<DT>(a.q, orow * D + d);
+  __syncthreads();
+  // the host keeps rows within kTrMaxPages; the clamp keeps LDS in bounds regardless
+  return L > 0 ? min(min((L + a.S - 1) / a.S, P_r), kTrMaxPages) : 0;
+}
+
+__device__ __forceinline__ void write_result(const ToprArgs& a, size_t orow, const uint64_t* best,
+                                             int kept, int pages) {
+  for (int i = threadIdx.x; i < a.R; i += kTrThreads) {
+    const bool ok = i < kept;
+    a.top_tokens[orow * a.R + i] = ok ? (int)(uint32_t)best[i] : -1;
+    a.top_logits[orow * a.R + i] = ok ? key_value(best[i]) : -INFINITY;
+  }
+  if (threadIdx.x == 0 && a.pages_read) a.pages_read[orow] = pages;
+}
+
+// 0. bounds: this head's page bounds ([Quest] eq. (2)-(3) with its own
+//    query), raised by the rounding margin, as sort keys in the workspace.
+//    RL lanes share a record (16-byte chunks of min and of max), so the
+//    summary reads coalesce; kTbPages pages per workgroup.
+constexpr int kTbThreads = 256;
+constexpr int kTbPages = 64;
+template <int DT, int D>
+__global__ __launch_bounds__(kTbThreads) void topr_bounds_kernel(ToprArgs a) {
+  constexpr int EPL = epl<DT>();
+  constexpr int RL = D / EPL;                 // lanes per record half
+  constexpr int PPS = kTbThreads / RL;        // pages per step of the workgroup
+  constexpr int BYTES = DType<DT>::bytes;
+  const int qh = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
+  const int H = a.H_kv, S = a.S, h = qh / (a.H_q / a.H_kv);
+  const int L = a.seq_lens[r];
+  const int pbeg = a.page_indptr[r];
+  const int P_r = a.page_indptr[r + 1] - pbeg;
+  const int P = L > 0 ? min(min((L + S - 1) / S, P_r), kTrMaxPages) : 0;
+  const int p_end = min(P, (blockIdx.x + 1) * kTbPages);
+  const size_t orow = (size_t)r * a.H_q + qh;
+  const int c = tid % RL;
+  float qf[EPL];
+  unpack16<DT>(load16(reinterpret_cast<const char*>(a.q) + (orow * D + c * EPL) * BYTES), qf);
+  const char* summ = reinterpret_cast<const char*>(a.summary);
+  uint64_t* wk = a.ws_pages + orow * a.page_stride;
+  for (int p = blockIdx.x * kTbPages + tid / RL; p < p_end; p += PPS) {
+    const size_t rec = ((size_t)a.page_indices[pbeg + p] * H + h) * 2 * D + c * EPL;
+    float m[EPL], M[EPL];
+    unpack16<DT>(load16(summ + rec * BYTES), m);
+    unpack16<DT>(load16(summ + (rec + D) * BYTES), M);
+    float u = 0.f, mag = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      u += fmaxf(qf[e] * m[e], qf[e] * M[e]);
+      mag += fabsf(qf[e]) * fmaxf(fabsf(m[e]), fabsf(M[e]));
+    }
+    u = group_sum<RL>(u);
+    mag = group_sum<RL>(mag);
+    if (c == 0) wk[p] = desc_key(u + ldexpf(mag, -15), (uint32_t)p);
+  }
+}
+
+// 1. plan: the branch-and-bound pilot.  The a.pilot_pages pages of largest
+//    bound (ties to the lower index: the page keys' order) are picked by the
+//    workgroup top-K select and ranked; the pilot reads them in that order.
+//    A row whose stop rule fires in the pilot, or whose next bound outside
+//    it is below tau_R, or that has no other page, is finished here;
+//    otherwise the pilot's best R go to the workspace with the list of the
+//    other pages whose bound is not below the pilot's tau_R (all other pages
+//    while fewer than R tokens are known), left to the scan.
+template <int DT, int D>
+__global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
+  constexpr int PT = kTrMaxPages / kTrThreads;        // bounds per thread
+  __shared__ TopkShared tsh;
+  __shared__ uint64_t s_sel[kTrMaxPilot];
   __shared__ uint64_t s_buf[2][kTrBuf];
   __shared__ float s_q[D];
   __shared__ int s_cnt[kTrWaves];
 
   const int qh = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-  const int H = a.H_kv, S = a.S, h = qh / (a.H_q / a.H_kv);
-  const int L = a.seq_lens[r];
-  const int pbeg = a.page_indptr[r];
-  const int P_r = a.page_indptr[r + 1] - pbeg;
-  // the host keeps rows within kTrMaxPages; the clamp keeps LDS in bounds regardless
-  const int P = L > 0 ? min(min((L + S - 1) / S, P_r), kTrMaxPages) : 0;
+  const int S = a.S, h = qh / (a.H_q / a.H_kv);
   const size_t orow = (size_t)r * a.H_q + qh;
-  for (int d = tid; d < D; d += kTrThreads) s_q[d] = load_scalar<DT>(a.q, orow * D + d);
-  __syncthreads();
+  int L, pbeg;
+  const int P = row_setup<DT, D>(a, s_q, r, qh, L, pbeg);
+  const uint64_t* wk = a.ws_pages + orow * a.page_stride;
 
-  // 1. this head's bounds, raised by the rounding margin, as sort keys
-  int Pp = 1;
-  while (Pp < P) Pp <<= 1;
-  const char* summ = reinterpret_cast<const char*>(a.summary);
-  for (int p = tid; p < Pp; p += kTrThreads) {
-    uint64_t key = ~0ull;
-    if (p < P) {
-      const size_t rec = ((size_t)a.page_indices[pbeg + p] * H + h) * 2 * D;
-      float u = 0.f, mag = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < D / EPL; ++c) {
-        float m[EPL], M[EPL];
-        unpack16<DT>(load16(summ + (rec + c * EPL) * BYTES), m);
-        unpack16<DT>(load16(summ + (rec + D + c * EPL) * BYTES), M);
+  // the pilot pages: the npil largest bounds, ordered by (bound desc, index asc)
+  TopkRow<PT, kTrThreads> t;
+  t.j0 = tid * PT;
+  t.n = P;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float qd = s_q[c * EPL + e];
-          u += fmaxf(qd * m[e], qd * M[e]);
-          mag += fabsf(qd) * fmaxf(fabsf(m[e]), fabsf(M[e]));
-        }
-      }
-      key = desc_key(u + ldexpf(mag, -15), (uint32_t)p);
-    }
-    s_pages[p] = key;
+  for (int k = 0; k < PT; ++k) t.v[k] = t.j0 + k < P ? key_value(wk[t.j0 + k]) : 0.f;
+  const int npil = min(P, a.pilot_pages);
+  t.select(npil, tsh);
+  int count;
+  int pos = t.first_position(tsh, &count);
+  float out_max = -INFINITY;                          // largest bound outside the pilot
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    if (t.selected(k)) s_sel[pos++] = desc_key(t.v[k], (uint32_t)(t.j0 + k));
+    else if (t.valid(k)) out_max = fmaxf(out_max, t.v[k]);
   }
-  __syncthreads();
-  bitonic_sort(s_pages, Pp);
+  float lo_dummy = FLT_MAX;
+  tk::block_minmax<kTrWaves>(lo_dummy, out_max, tsh.mm);   // barrier: s_sel complete
+  {
+    uint64_t x = 0;
+    int rank = 0;
+    if (tid < npil) {
+      x = s_sel[tid];
+      for (int q = 0; q < npil; ++q) rank += s_sel[q] < x ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid < npil) s_sel[rank] = x;
+    __syncthreads();
+  }
 
-  // 2. rounds of kTrThreads tokens in bound order until the next bound is below tau_R
+  // pilot rounds over the pilot pages in order (first enough for R tokens,
+  // then doubling up to one token per thread)
   const int R = a.R;
-  // pages per round: first enough for R tokens, then doubling up to one
-  // token per thread, so that tight bounds stop after few pages and loose
-  // ones read 512 tokens a round (S <= 256)
   const int cp = kTrThreads / S;
   int np_round = max(1, min(cp, (R + S - 1) / S));
-  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   int kept = 0, cur = 0, next = 0;
-  while (next < P) {
-    if (kept >= R && key_value(s_pages[next]) < key_value(s_buf[cur][R - 1])) break;
-    const int np = min(np_round, P - next);
+  bool stopped = false;
+  while (next < npil) {
+    if (kept >= R && key_value(s_sel[next]) < key_value(s_buf[cur][R - 1])) {
+      stopped = true;
+      break;
+    }
+    const int np = min(np_round, npil - next);
     np_round = min(cp, 2 * np_round);
     bool cand = false;
     uint64_t ck = 0;
     if (tid < np * S) {
-      const int j = (int)(uint32_t)s_pages[next + tid / S];
-      const int off = tid % S;
-      const int t = j * S + off;
-      if (t < L) {
-        const size_t row = (((size_t)a.page_indices[pbeg + j] * H + h) * S + off) * D;
-        float z = 0.f;
-#pragma unroll 4
-        for (int c = 0; c < D / EPL; ++c) {
-          float k[EPL];
-          unpack16<DT>(load16(kpool + (row + c * EPL) * BYTES), k);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) z += s_q[c * EPL + e] * k[e];
-        }
-        ck = desc_key(z, (uint32_t)t);
+      const int j = (int)(uint32_t)s_sel[next + tid / S];
+      const int tt = j * S + tid % S;
+      if (tt < L) {
+        ck = token_key<DT, D>(a, s_q, a.page_indices[pbeg + j], h, tid % S, tt);
         cand = kept < R || ck < s_buf[cur][R - 1];
       }
     }
     int total;
-    const int pos = tr_excl_count(cand, s_cnt, &total);
-    if (cand) s_buf[cur][kept + pos] = ck;
+    const int p2 = tr_excl_count(cand, s_cnt, &total);
+    if (cand) s_buf[cur][kept + p2] = ck;
     __syncthreads();
-    if (total > 0) {
-      // rank of every entry among old (sorted) + new (unsorted), unique keys
-      const int n = kept + total;
-      for (int i = tid; i < n; i += kTrThreads) {
-        const uint64_t x = s_buf[cur][i];
-        int rank = 0;
-        if (i < kept) {
-          rank = i;
-        } else {
-          int lo = 0, hi = kept;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s_buf[cur][mid] < x) lo = mid + 1; else hi = mid;
-          }
-          rank = lo;
-        }
-        for (int q = kept; q < n; ++q) rank += s_buf[cur][q] < x ? 1 : 0;
-        if (rank < R) s_buf[cur ^ 1][rank] = x;
-      }
-      kept = min(n, R);
-      cur ^= 1;
-      __syncthreads();
-    }
+    if (total > 0) rank_merge(s_buf, cur, kept, total, R);
     next += np;
   }
-
-  // 3. the best R by (logit descending, token ascending), padded
-  for (int i = tid; i < R; i += kTrThreads) {
-    const bool ok = i < kept;
-    a.top_tokens[orow * R + i] = ok ? (int)(uint32_t)s_buf[cur][i] : -1;
-    a.top_logits[orow * R + i] = ok ? key_value(s_buf[cur][i]) : -INFINITY;
+  const float tau = kept >= R ? key_value(s_buf[cur][R - 1]) : -INFINITY;
+  int* st = a.ws_state + orow * 4;
+  if (stopped || npil == P || (kept >= R && out_max < tau)) {
+    write_result(a, orow, s_buf[cur], kept, next);
+    if (tid == 0) st[0] = 1;
+    return;
   }
-  if (tid == 0 && a.pages_read) a.pages_read[orow] = next;
+  // the other pages the pilot cannot exclude, in page order
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < PT; ++k)
+    mine += (t.valid(k) && !t.selected(k) && (kept < R || !(t.v[k] < tau))) ? 1 : 0;
+  int n_scan;
+  int at = tk::block_excl_scan<kTrWaves>(mine, tsh.scan[0], &n_scan);
+  uint64_t* wp = a.ws_pages + orow * a.page_stride;
+  __syncthreads();                                    // every wk read above is done
+#pragma unroll
+  for (int k = 0; k < PT; ++k)
+    if (t.valid(k) && !t.selected(k) && (kept < R || !(t.v[k] < tau)))
+      wp[at++] = desc_key(t.v[k], (uint32_t)(t.j0 + k));
+  uint64_t* wb = a.ws_pilot + orow * R;
+  for (int i = tid; i < kept; i += kTrThreads) wb[i] = s_buf[cur][i];
+  if (tid == 0) {
+    st[0] = 0;
+    st[1] = npil;          // pages read by the pilot
+    st[2] = n_scan;        // pages left to the scan
+    st[3] = kept;
+  }
+}
+
+// 2. scan: one workgroup per (chunk of kTrThreads tokens of the pages left,
+//    query head, request) computes their exact logits and keeps the best R
+//    of those beating the pilot's R-th (all of them if the pilot holds fewer
+//    than R), in order.
+template <int DT, int D>
+__global__ __launch_bounds__(kTrThreads) void topr_scan_kernel(ToprArgs a) {
+  __shared__ uint64_t s_cand[kTrThreads];
+  __shared__ float s_q[D];
+  __shared__ int s_cnt[kTrWaves];
+  const int c = blockIdx.x, qh = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
+  const size_t orow = (size_t)r * a.H_q + qh;
+  const int* st = a.ws_state + orow * 4;
+  const int nchunks = a.scan_chunks;
+  uint64_t* out = a.ws_chunks + (orow * nchunks + c) * a.R;
+  int* cnt = a.ws_counts + orow * nchunks + c;
+  if (st[0] != 0) return;                              // finished by the pilot
+  const int S = a.S, cp = kTrThreads / S;
+  const int p0 = c * cp, p1 = min(st[2], p0 + cp);
+  if (p0 >= p1) {
+    if (tid == 0) *cnt = 0;
+    return;
+  }
+  const int R = a.R;
+  const int pilot_kept = st[3];
+  const uint64_t bar = pilot_kept >= R ? a.ws_pilot[orow * R + R - 1] : ~0ull;
+  int L, pbeg;
+  (void)row_setup<DT, D>(a, s_q, r, qh, L, pbeg);
+  const int h = qh / (a.H_q / a.H_kv);
+  const uint64_t* wp = a.ws_pages + orow * a.page_stride;
+  bool cand = false;
+  uint64_t ck = 0;
+  if (tid < (p1 - p0) * S) {
+    const int j = (int)(uint32_t)wp[p0 + tid / S];
+    const int t = j * S + tid % S;
+    if (t < L) {
+      ck = token_key<DT, D>(a, s_q, a.page_indices[pbeg + j], h, tid % S, t);
+      cand = ck < bar;
+    }
+  }
+  int total;
+  const int pos = tr_excl_count(cand, s_cnt, &total);
+  if (cand) s_cand[pos] = ck;
+  __syncthreads();
+  // the best min(total, R) of the candidates, ranked (keys unique)
+  if (tid < total) {
+    const uint64_t x = s_cand[tid];
+    int rank = 0;
+    for (int q = 0; q < total; ++q) rank += s_cand[q] < x ? 1 : 0;
+    if (rank < R) out[rank] = x;
+  }
+  if (tid == 0) *cnt = min(total, R);
+}
+
+// 3. merge: the pilot's best R with every chunk's list, 512 new keys at a
+//    time, then the result.
+constexpr int kTrMaxChunks = kTrMaxPages / 2;   // page size >= 1, 512 tokens a chunk
+template <int DT, int D>
+__global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
+  __shared__ uint64_t s_buf[2][kTrBuf];
+  __shared__ uint64_t s_all[kTrMaxPages];
+  __shared__ int s_off[kTrMaxChunks + 1];
+  const int qh = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const size_t orow = (size_t)r * a.H_q + qh;
+  const int* st = a.ws_state + orow * 4;
+  if (st[0] != 0) return;
+  const int R = a.R, S = a.S, cp = kTrThreads / S;
+  const int nch = (st[2] + cp - 1) / cp;               // chunks the scan used
+  const int* cnts = a.ws_counts + orow * a.scan_chunks;
+  const int pilot = st[3];
+  // list offsets (one pass over the counts; at most kTrMaxPages / 2 lists)
+  for (int i = tid; i < nch; i += kTrThreads) s_off[i] = cnts[i];
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nch; ++i) {
+      const int n = s_off[i];
+      s_off[i] = run;
+      run += n;
+    }
+    s_off[nch] = run;
+  }
+  __syncthreads();
+  const int total = s_off[nch];
+  if (pilot + total <= kTrMaxPages) {
+    // everything fits: gather the pilot's and every chunk's keys, sort once
+    int n2 = 1;
+    while (n2 < pilot + total) n2 <<= 1;
+    for (int i = tid; i < n2; i += kTrThreads) {
+      uint64_t x = ~0ull;
+      if (i < pilot) {
+        x = a.ws_pilot[orow * R + i];
+      } else if (i < pilot + total) {
+        const int e = i - pilot;
+        int lo = 0, hi = nch;                 // last list with offset <= e
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_off[mid] <= e) lo = mid; else hi = mid;
+        }
+        x = a.ws_chunks[(orow * a.scan_chunks + lo) * R + (e - s_off[lo])];
+      }
+      s_all[i] = x;
+    }
+    __syncthreads();
+    bitonic_sort(s_all, n2);
+    write_result(a, orow, s_all, min(R, pilot + total), st[1] + st[2]);
+    return;
+  }
+  // else merge 512 new keys at a time
+  int kept = pilot, cur = 0;
+  for (int i = tid; i < kept; i += kTrThreads) s_buf[0][i] = a.ws_pilot[orow * R + i];
+  __syncthreads();
+  int c = 0;
+  while (c < nch) {
+    // gather whole chunk lists while they fit in kTrThreads new slots (a list
+    // holds at most R <= kTrThreads keys)
+    int got = 0;
+    while (c < nch && got + cnts[c] <= kTrThreads) {
+      const int n = cnts[c];
+      const uint64_t* src = a.ws_chunks + (orow * a.scan_chunks + c) * R;
+      for (int i = tid; i < n; i += kTrThreads) s_buf[cur][kept + got + i] = src[i];
+      got += n;
+      ++c;
+    }
+    __syncthreads();
+    if (got > 0) rank_merge(s_buf, cur, kept, got, R);
+  }
+  write_result(a, orow, s_buf[cur], kept, st[1] + st[2]);
 }
 
 template <int DT, int D>
 hipError_t launch_t(const ToprArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((topr_kernel<DT, D>), dim3(a.H_q, a.B), dim3(kTrThreads), 0, s, a);
+  hipLaunchKernelGGL((topr_bounds_kernel<DT, D>),
+                     dim3((a.page_stride + kTbPages - 1) / kTbPages, a.H_q, a.B), dim3(kTbThreads),
+                     0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((topr_plan_kernel<DT, D>), dim3(a.H_q, a.B), dim3(kTrThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((topr_scan_kernel<DT, D>), dim3(a.scan_chunks, a.H_q, a.B), dim3(kTrThreads),
+                     0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((topr_merge_kernel<DT, D>), dim3(a.H_q, a.B), dim3(kTrThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -218,6 +465,7 @@ hipError_t by_d(const ToprArgs& a, hipStream_t s) {
 }  // namespace
 
 int topr_max_pages() { return kTrMaxPages; }
+int topr_threads() { return kTrThreads; }
 int topr_max_r() { return kTrMaxR; }
 
 hipError_t launch_topr(const ToprArgs& a, hipStream_t s) {

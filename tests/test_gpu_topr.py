@@ -29,7 +29,9 @@ def _run(qas, pc, db, case, R, q_raw=None):
     tok = torch.full((case.B, case.H_q, R), 12345, dtype=torch.int32, device="cuda")
     lg = torch.full((case.B, case.H_q, R), 7.0, device="cuda")
     pr = torch.full((case.B, case.H_q), -3, dtype=torch.int32, device="cuda")
-    qas.qas_exact_top_r(pc.cache, db.batch, q, R, tok, lg, pr)
+    n = qas.qas_exact_top_r_workspace_bytes(pc.cache, db.batch, case.H_q, R)
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")   # no zero-fill needed
+    qas.qas_exact_top_r(pc.cache, db.batch, q, R, tok, lg, ws, pages_read=pr)
     torch.cuda.synchronize()
     return tok.cpu().numpy(), lg.cpu().numpy(), pr.cpu().numpy()
 
@@ -131,4 +133,6 @@ def test_exact_top_r_full_size_layer(qas):
 
 
 def test_exact_top_r_validation_without_launch(qas):
-    assert qas.lib.qas_exact_top_r(None, None, None, 0, 1, 1, None, None, None, None) == 1
+    assert qas.lib.qas_exact_top_r(None, None, None, 0, 1, 1, None, None, None, None, 0,
+                                   None) == 1
+    assert qas.lib.qas_exact_top_r_workspace_bytes(None, None, 8, 4) == 0
