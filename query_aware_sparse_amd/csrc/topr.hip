@@ -63,22 +63,31 @@ __device__ __forceinline__ int tr_excl_count(bool flag, int* scratch, int* total
   return before + in_wave;
 }
 
-// ascending bitonic sort of n (a power of two) keys in LDS
-__device__ void bitonic_sort(uint64_t* s, int n) {
-  for (int k = 2; k <= n; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += kTrThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = s[i], y = s[ixj];
-          if ((x > y) == ((i & k) == 0)) {
-            s[i] = y;
-            s[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+// Keys of s[lo, hi) below x, for an LDS array s that is 16-byte aligned;
+// every lane reads the same words.  Two keys per 16-byte read and eight
+// reads in flight, so the count does not wait one LDS round trip per key.
+__device__ __forceinline__ int count_below(const uint64_t* s, int lo, int hi, uint64_t x) {
+  int c = 0;
+  if ((lo & 1) && lo < hi) {
+    c += s[lo] < x ? 1 : 0;
+    ++lo;
+  }
+  const ulonglong2* p = reinterpret_cast<const ulonglong2*>(s + lo);
+  const int pairs = (hi - lo) >> 1;
+  int i = 0;
+  for (; i + 8 <= pairs; i += 8) {
+    ulonglong2 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = p[i + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += (w[u].x < x ? 1 : 0) + (w[u].y < x ? 1 : 0);
+  }
+  for (; i < pairs; ++i) {
+    const ulonglong2 w = p[i];
+    c += (w.x < x ? 1 : 0) + (w.y < x ? 1 : 0);
+  }
+  if (lo < hi && ((hi - lo) & 1)) c += s[hi - 1] < x ? 1 : 0;
+  return c;
 }
 
 // Rank merge of the sorted best `kept` keys of buf[cur] with `total` unsorted
@@ -99,7 +108,7 @@ __device__ void rank_merge(uint64_t (*buf)[kTrBuf], int& cur, int& kept, int tot
       }
       rank = lo;
     }
-    for (int q = kept; q < n; ++q) rank += buf[cur][q] < x ? 1 : 0;
+    rank += count_below(buf[cur], kept, n, x);
     if (rank < R) buf[cur ^ 1][rank] = x;
   }
   kept = min(n, R);
@@ -136,8 +145,9 @@ __device__ __forceinline__ int row_setup(const ToprArgs& a, float* s_q, int r, i
   const size_t orow = (size_t)r * a.H_q + qh;
   for (int d = threadIdx.x; d < D; d += kTrThreads) s_q[d] = load_scalar<DT>(a.q, orow * D + d);
   __syncthreads();
-  // the host keeps rows within kTrMaxPages; the clamp keeps LDS in bounds regardless
-  return L > 0 ? min(min((L + a.S - 1) / a.S, P_r), kTrMaxPages) : 0;
+  // the host keeps rows within kTrMaxPages and the batch's max_pages (the
+  // workspace row stride); the clamp keeps LDS and the workspace in bounds regardless
+  return L > 0 ? min(min((L + a.S - 1) / a.S, P_r), min(kTrMaxPages, a.page_stride)) : 0;
 }
 
 __device__ __forceinline__ void write_result(const ToprArgs& a, size_t orow, const uint64_t* best,
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kTbThreads) void topr_bounds_kernel(ToprArgs a) {
   const int L = a.seq_lens[r];
   const int pbeg = a.page_indptr[r];
   const int P_r = a.page_indptr[r + 1] - pbeg;
-  const int P = L > 0 ? min(min((L + S - 1) / S, P_r), kTrMaxPages) : 0;
+  const int P = L > 0 ? min(min((L + S - 1) / S, P_r), min(kTrMaxPages, a.page_stride)) : 0;
   const int p_end = min(P, (blockIdx.x + 1) * kTbPages);
   const size_t orow = (size_t)r * a.H_q + qh;
   const int c = tid % RL;
@@ -200,12 +210,13 @@ __global__ __launch_bounds__(kTbThreads) void topr_bounds_kernel(ToprArgs a) {
 //    otherwise the pilot's best R go to the workspace with the list of the
 //    other pages whose bound is not below the pilot's tau_R (all other pages
 //    while fewer than R tokens are known), left to the scan.
-template <int DT, int D>
+template <int DT, int D, int PT>
 __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
-  constexpr int PT = kTrMaxPages / kTrThreads;        // bounds per thread
+  // PT bounds per thread: rows of up to kTrThreads * PT pages
   __shared__ TopkShared tsh;
-  __shared__ uint64_t s_sel[kTrMaxPilot];
-  __shared__ uint64_t s_buf[2][kTrBuf];
+  __shared__ __align__(16) uint64_t s_sel[kTrMaxPilot];
+  __shared__ int s_phys[kTrMaxPilot];
+  __shared__ __align__(16) uint64_t s_buf[2][kTrBuf];
   __shared__ float s_q[D];
   __shared__ int s_cnt[kTrWaves];
 
@@ -216,13 +227,22 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   const int P = row_setup<DT, D>(a, s_q, r, qh, L, pbeg);
   const uint64_t* wk = a.ws_pages + orow * a.page_stride;
 
+  // rounds read whole pages: first enough for R tokens, then twice as many
+  // each round up to one token per thread; the pilot is the rounds that fit
+  // in a.pilot_pages pages
+  const int R = a.R;
+  const int cp = kTrThreads / S;
+  const int s0 = max(1, min(cp, (R + S - 1) / S));
+  int cap = 0;
+  for (int np = s0; cap + np <= a.pilot_pages; np = min(cp, 2 * np)) cap += np;
+  const int npil = min(P, cap > 0 ? cap : a.pilot_pages);
+
   // the pilot pages: the npil largest bounds, ordered by (bound desc, index asc)
   TopkRow<PT, kTrThreads> t;
   t.j0 = tid * PT;
   t.n = P;
 #pragma unroll
   for (int k = 0; k < PT; ++k) t.v[k] = t.j0 + k < P ? key_value(wk[t.j0 + k]) : 0.f;
-  const int npil = min(P, a.pilot_pages);
   t.select(npil, tsh);
   int count;
   int pos = t.first_position(tsh, &count);
@@ -235,22 +255,24 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   float lo_dummy = FLT_MAX;
   tk::block_minmax<kTrWaves>(lo_dummy, out_max, tsh.mm);   // barrier: s_sel complete
   {
+    // rank the pilot pages and fetch their physical pages once
     uint64_t x = 0;
-    int rank = 0;
+    int rank = 0, phys = 0;
     if (tid < npil) {
       x = s_sel[tid];
-      for (int q = 0; q < npil; ++q) rank += s_sel[q] < x ? 1 : 0;
+      phys = a.page_indices[pbeg + (int)(uint32_t)x];
+      rank = count_below(s_sel, 0, npil, x);
     }
     __syncthreads();
-    if (tid < npil) s_sel[rank] = x;
+    if (tid < npil) {
+      s_sel[rank] = x;
+      s_phys[rank] = phys;
+    }
     __syncthreads();
   }
 
-  // pilot rounds over the pilot pages in order (first enough for R tokens,
-  // then doubling up to one token per thread)
-  const int R = a.R;
-  const int cp = kTrThreads / S;
-  int np_round = max(1, min(cp, (R + S - 1) / S));
+  // pilot rounds over the pilot pages in order
+  int np_round = s0;
   int kept = 0, cur = 0, next = 0;
   bool stopped = false;
   while (next < npil) {
@@ -266,7 +288,7 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
       const int j = (int)(uint32_t)s_sel[next + tid / S];
       const int tt = j * S + tid % S;
       if (tt < L) {
-        ck = token_key<DT, D>(a, s_q, a.page_indices[pbeg + j], h, tid % S, tt);
+        ck = token_key<DT, D>(a, s_q, s_phys[next + tid / S], h, tid % S, tt);
         cand = kept < R || ck < s_buf[cur][R - 1];
       }
     }
@@ -313,7 +335,7 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
 //    than R), in order.
 template <int DT, int D>
 __global__ __launch_bounds__(kTrThreads) void topr_scan_kernel(ToprArgs a) {
-  __shared__ uint64_t s_cand[kTrThreads];
+  __shared__ __align__(16) uint64_t s_cand[kTrThreads];
   __shared__ float s_q[D];
   __shared__ int s_cnt[kTrWaves];
   const int c = blockIdx.x, qh = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
@@ -353,21 +375,69 @@ __global__ __launch_bounds__(kTrThreads) void topr_scan_kernel(ToprArgs a) {
   // the best min(total, R) of the candidates, ranked (keys unique)
   if (tid < total) {
     const uint64_t x = s_cand[tid];
-    int rank = 0;
-    for (int q = 0; q < total; ++q) rank += s_cand[q] < x ? 1 : 0;
+    const int rank = count_below(s_cand, 0, total, x);
     if (rank < R) out[rank] = x;
   }
   if (tid == 0) *cnt = min(total, R);
 }
 
-// 3. merge: the pilot's best R with every chunk's list, 512 new keys at a
-//    time, then the result.
+// 3. merge: the pilot's list and the chunks' lists, each sorted, merged
+//    pairwise in a tree in LDS.  A list sits in a slot of W keys (R rounded
+//    up to a power of two), padded with ~0, which is above every key.  Two
+//    slots merge into the best W of their union: a key moves to its index
+//    plus the number of keys of the other list below it (keys are unique,
+//    so the best W land on distinct places, and the padding fills the rest).
+//    The search for that number runs on all of a thread's keys in step, one
+//    LDS read each per step.  Lists beyond one batch of slots are merged a
+//    batch at a time, the running result in the first slot.
+// One level of the merge tree: slots 2s and 2s + 1 of `in` (W = 2^lw keys
+// each, n slots) into slot s of `out`, KK keys per thread (keys e = tid +
+// k * kTrThreads, k < KK, cover the n * W keys in use).
+template <int KK>
+__device__ __forceinline__ void merge_level(const uint64_t* in, uint64_t* out, int n, int lw) {
+  const int W = 1 << lw, tid = threadIdx.x;
+  uint64_t x[KK];
+  int base[KK], pos[KK];
+  bool pair[KK];
+#pragma unroll
+  for (int k = 0; k < KK; ++k) {
+    const int e = tid + k * kTrThreads;
+    const int slot = e >> lw;
+    const bool live = e < n * W;
+    pair[k] = live && (slot ^ 1) < n;
+    x[k] = in[live ? e : 0];
+    base[k] = pair[k] ? (slot ^ 1) << lw : 0;
+    pos[k] = 0;
+  }
+  for (int step = W >> 1; step > 0; step >>= 1) {
+    uint64_t y[KK];
+#pragma unroll
+    for (int k = 0; k < KK; ++k) y[k] = in[base[k] + pos[k] + step - 1];
+#pragma unroll
+    for (int k = 0; k < KK; ++k) pos[k] += y[k] < x[k] ? step : 0;
+  }
+  uint64_t y[KK];
+#pragma unroll
+  for (int k = 0; k < KK; ++k) y[k] = in[base[k] + pos[k]];
+#pragma unroll
+  for (int k = 0; k < KK; ++k) {
+    pos[k] += y[k] < x[k] ? 1 : 0;
+    const int e = tid + k * kTrThreads;
+    const int slot = e >> lw, i = e & (W - 1);
+    const int at = pair[k] ? i + pos[k] : i;           // an unpaired last slot passes through
+    if (e < n * W && at < W) out[((slot >> 1) << lw) + at] = x[k];
+  }
+}
+
 constexpr int kTrMaxChunks = kTrMaxPages / 2;   // page size >= 1, 512 tokens a chunk
+constexpr int kTrMergeKeys = kTrMaxPages;       // keys in a batch of slots
 template <int DT, int D>
 __global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
-  __shared__ uint64_t s_buf[2][kTrBuf];
-  __shared__ uint64_t s_all[kTrMaxPages];
+  constexpr int KPT = kTrMergeKeys / kTrThreads;      // keys per thread
+  constexpr int CPT = kTrMaxChunks / kTrThreads;      // chunk counts per thread
+  __shared__ __align__(16) uint64_t s_m[2][kTrMergeKeys];
   __shared__ int s_off[kTrMaxChunks + 1];
+  __shared__ int s_scan[kTrWaves];
   const int qh = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const size_t orow = (size_t)r * a.H_q + qh;
   const int* st = a.ws_state + orow * 4;
@@ -376,64 +446,74 @@ __global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
   const int nch = (st[2] + cp - 1) / cp;               // chunks the scan used
   const int* cnts = a.ws_counts + orow * a.scan_chunks;
   const int pilot = st[3];
-  // list offsets (one pass over the counts; at most kTrMaxPages / 2 lists)
-  for (int i = tid; i < nch; i += kTrThreads) s_off[i] = cnts[i];
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < nch; ++i) {
-      const int n = s_off[i];
-      s_off[i] = run;
-      run += n;
-    }
-    s_off[nch] = run;
+  // list offsets: CPT consecutive counts per thread, one block scan
+  int cn[CPT], mine = 0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int i = tid * CPT + k;
+    cn[k] = i < nch ? cnts[i] : 0;
+    mine += cn[k];
   }
+  int total;
+  int run = tk::block_excl_scan<kTrWaves>(mine, s_scan, &total);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int i = tid * CPT + k;
+    if (i < nch) s_off[i] = run;
+    run += cn[k];
+  }
+  if (tid == 0) s_off[nch] = total;
   __syncthreads();
-  const int total = s_off[nch];
-  if (pilot + total <= kTrMaxPages) {
-    // everything fits: gather the pilot's and every chunk's keys, sort once
-    int n2 = 1;
-    while (n2 < pilot + total) n2 <<= 1;
-    for (int i = tid; i < n2; i += kTrThreads) {
-      uint64_t x = ~0ull;
-      if (i < pilot) {
-        x = a.ws_pilot[orow * R + i];
-      } else if (i < pilot + total) {
-        const int e = i - pilot;
-        int lo = 0, hi = nch;                 // last list with offset <= e
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_off[mid] <= e) lo = mid; else hi = mid;
-        }
-        x = a.ws_chunks[(orow * a.scan_chunks + lo) * R + (e - s_off[lo])];
+
+  const int lw = 32 - __clz(R - 1);                    // W = 2^lw >= R
+  const int W = 1 << lw;
+  const int NS = kTrMergeKeys / W;                     // slots of a batch
+  const int nl = 1 + nch;                              // the pilot's list, then the chunks'
+  int cur = 0, done = 0, first = 0;
+  while (done < nl) {
+    const int fresh = min(NS - first, nl - done);      // lists loaded in this batch
+    int n = first + fresh;                             // slots in use
+    {
+      // every load issued before any LDS store (a key outside the lists
+      // reads the pilot list's first entry and is dropped)
+      const uint64_t* pil = a.ws_pilot + orow * R;
+      uint64_t v[KPT];
+      bool ok[KPT];
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const int e = tid + k * kTrThreads;
+        const int slot = e >> lw, i = e & (W - 1);
+        const bool act = slot >= first && slot < n;
+        const int list = act ? done + slot - first : 0;
+        const int cnt = list == 0 ? pilot : s_off[list] - s_off[list - 1];
+        ok[k] = act && i < cnt;
+        const uint64_t* src =
+            !ok[k] ? pil : list == 0 ? pil + i : a.ws_chunks + (orow * a.scan_chunks + list - 1) * R + i;
+        v[k] = *src;
       }
-      s_all[i] = x;
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const int e = tid + k * kTrThreads;
+        const int slot = e >> lw;
+        if (slot >= first && slot < n) s_m[cur][e] = ok[k] ? v[k] : ~0ull;
+      }
     }
     __syncthreads();
-    bitonic_sort(s_all, n2);
-    write_result(a, orow, s_all, min(R, pilot + total), st[1] + st[2]);
-    return;
-  }
-  // else merge 512 new keys at a time
-  int kept = pilot, cur = 0;
-  for (int i = tid; i < kept; i += kTrThreads) s_buf[0][i] = a.ws_pilot[orow * R + i];
-  __syncthreads();
-  int c = 0;
-  while (c < nch) {
-    // gather whole chunk lists while they fit in kTrThreads new slots (a list
-    // holds at most R <= kTrThreads keys)
-    int got = 0;
-    while (c < nch && got + cnts[c] <= kTrThreads) {
-      const int n = cnts[c];
-      const uint64_t* src = a.ws_chunks + (orow * a.scan_chunks + c) * R;
-      for (int i = tid; i < n; i += kTrThreads) s_buf[cur][kept + got + i] = src[i];
-      got += n;
-      ++c;
+    while (n > 1) {
+      // keys per thread at this level: n * W halves with every level
+      const int live = (n * W + kTrThreads - 1) / kTrThreads;
+      if (live > 4) merge_level<KPT>(s_m[cur], s_m[cur ^ 1], n, lw);
+      else if (live > 2) merge_level<4>(s_m[cur], s_m[cur ^ 1], n, lw);
+      else if (live > 1) merge_level<2>(s_m[cur], s_m[cur ^ 1], n, lw);
+      else merge_level<1>(s_m[cur], s_m[cur ^ 1], n, lw);
+      __syncthreads();
+      cur ^= 1;
+      n = (n + 1) >> 1;
     }
-    __syncthreads();
-    if (got > 0) rank_merge(s_buf, cur, kept, got, R);
+    done += fresh;
+    first = 1;
   }
-  write_result(a, orow, s_buf[cur], kept, st[1] + st[2]);
+  write_result(a, orow, s_m[cur], min(R, pilot + total), st[1] + st[2]);
 }
 
 template <int DT, int D>
@@ -443,7 +523,11 @@ hipError_t launch_t(const ToprArgs& a, hipStream_t s) {
                      0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topr_plan_kernel<DT, D>), dim3(a.H_q, a.B), dim3(kTrThreads), 0, s, a);
+  if (a.page_stride <= kTrThreads * 4)
+    hipLaunchKernelGGL((topr_plan_kernel<DT, D, 4>), dim3(a.H_q, a.B), dim3(kTrThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((topr_plan_kernel<DT, D, kTrMaxPages / kTrThreads>), dim3(a.H_q, a.B),
+                       dim3(kTrThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((topr_scan_kernel<DT, D>), dim3(a.scan_chunks, a.H_q, a.B), dim3(kTrThreads),
                      0, s, a);
