@@ -116,35 +116,58 @@ __device__ void rank_merge(uint64_t (*buf)[kTrBuf], int& cur, int& kept, int tot
   __syncthreads();
 }
 
-// key of token `off` of physical page `phys` for this head (logit q . k in fp32)
+// Logits q . k (fp32, unscaled: the bound's units) of the nt = np * S
+// tokens of np pages, token u being row u % S of physical page pp[u / S],
+// into z[u] (LDS).  RL = D / EPL lanes share a row, each loading 16 bytes
+// of it with the matching slice qf of the query, and a DPP sum joins them:
+// one wave load covers 64 / RL whole rows.  Rows of the tail page past the
+// sequence are read too (they lie inside the page) and left to the caller
+// to drop.  Ends without a barrier.
 template <int DT, int D>
-__device__ __forceinline__ uint64_t token_key(const ToprArgs& a, const float* s_q, int phys, int h,
-                                              int off, int t) {
+__device__ __forceinline__ void page_logits(const ToprArgs& a, const float* qf, int h,
+                                            const int* pp, int np, float* z) {
   constexpr int EPL = epl<DT>();
+  constexpr int RL = D / EPL;
+  constexpr int TPP = kTrThreads / RL;                 // rows per pass of the workgroup
+  constexpr int UNR = 8;                               // passes in flight
   constexpr int BYTES = DType<DT>::bytes;
+  const int ls = __ffs(a.S) - 1;                       // S is a power of two
+  const int nt = np << ls, g = threadIdx.x / RL, c = threadIdx.x % RL;
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
-  const size_t row = (((size_t)phys * a.H_kv + h) * a.S + off) * D;
-  float z = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < D / EPL; ++c) {
-    float k[EPL];
-    unpack16<DT>(load16(kpool + (row + c * EPL) * BYTES), k);
+  for (int b = 0; b < nt; b += TPP * UNR) {
+    uint4 raw[UNR];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) z += s_q[c * EPL + e] * k[e];
+    for (int u = 0; u < UNR; ++u) {
+      const int t = min(b + u * TPP + g, nt - 1);
+      const size_t row = (((size_t)pp[t >> ls] * a.H_kv + h) << ls) + (t & (a.S - 1));
+      raw[u] = load16(kpool + (row * D + c * EPL) * BYTES);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float k[EPL];
+      unpack16<DT>(raw[u], k);
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v += qf[e] * k[e];
+      v = group_sum<RL>(v);
+      const int t = b + u * TPP + g;
+      if (c == 0 && t < nt) z[t] = v;
+    }
   }
-  return desc_key(z, (uint32_t)t);
 }
 
-// the row's query head in LDS; returns P (pages of the row)
+// This lane's slice of the row's query head for page_logits; returns P (pages of the row)
 template <int DT, int D>
-__device__ __forceinline__ int row_setup(const ToprArgs& a, float* s_q, int r, int qh, int& L,
+__device__ __forceinline__ int row_setup(const ToprArgs& a, float* qf, int r, int qh, int& L,
                                          int& pbeg) {
+  constexpr int EPL = epl<DT>();
+  constexpr int RL = D / EPL;
   L = a.seq_lens[r];
   pbeg = a.page_indptr[r];
   const int P_r = a.page_indptr[r + 1] - pbeg;
   const size_t orow = (size_t)r * a.H_q + qh;
-  for (int d = threadIdx.x; d < D; d += kTrThreads) s_q[d] = load_scalar<DT>(a.q, orow * D + d);
-  __syncthreads();
+  unpack16<DT>(load16(reinterpret_cast<const char*>(a.q) +
+                      (orow * D + (threadIdx.x % RL) * EPL) * DType<DT>::bytes), qf);
   // the host keeps rows within kTrMaxPages and the batch's max_pages (the
   // workspace row stride); the clamp keeps LDS and the workspace in bounds regardless
   return L > 0 ? min(min((L + a.S - 1) / a.S, P_r), min(kTrMaxPages, a.page_stride)) : 0;
@@ -217,14 +240,15 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   __shared__ __align__(16) uint64_t s_sel[kTrMaxPilot];
   __shared__ int s_phys[kTrMaxPilot];
   __shared__ __align__(16) uint64_t s_buf[2][kTrBuf];
-  __shared__ float s_q[D];
+  __shared__ float s_z[kTrThreads];
   __shared__ int s_cnt[kTrWaves];
 
   const int qh = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int S = a.S, h = qh / (a.H_q / a.H_kv);
   const size_t orow = (size_t)r * a.H_q + qh;
   int L, pbeg;
-  const int P = row_setup<DT, D>(a, s_q, r, qh, L, pbeg);
+  float qf[epl<DT>()];
+  const int P = row_setup<DT, D>(a, qf, r, qh, L, pbeg);
   const uint64_t* wk = a.ws_pages + orow * a.page_stride;
 
   // rounds read whole pages: first enough for R tokens, then twice as many
@@ -282,13 +306,15 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
     }
     const int np = min(np_round, npil - next);
     np_round = min(cp, 2 * np_round);
+    page_logits<DT, D>(a, qf, h, s_phys + next, np, s_z);
+    __syncthreads();
     bool cand = false;
     uint64_t ck = 0;
     if (tid < np * S) {
       const int j = (int)(uint32_t)s_sel[next + tid / S];
       const int tt = j * S + tid % S;
       if (tt < L) {
-        ck = token_key<DT, D>(a, s_q, s_phys[next + tid / S], h, tid % S, tt);
+        ck = desc_key(s_z[tid], (uint32_t)tt);
         cand = kept < R || ck < s_buf[cur][R - 1];
       }
     }
@@ -336,7 +362,8 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
 template <int DT, int D>
 __global__ __launch_bounds__(kTrThreads) void topr_scan_kernel(ToprArgs a) {
   __shared__ __align__(16) uint64_t s_cand[kTrThreads];
-  __shared__ float s_q[D];
+  __shared__ float s_z[kTrThreads];
+  __shared__ int s_pp[kTrThreads], s_j[kTrThreads];
   __shared__ int s_cnt[kTrWaves];
   const int c = blockIdx.x, qh = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
   const size_t orow = (size_t)r * a.H_q + qh;
@@ -355,16 +382,25 @@ __global__ __launch_bounds__(kTrThreads) void topr_scan_kernel(ToprArgs a) {
   const int pilot_kept = st[3];
   const uint64_t bar = pilot_kept >= R ? a.ws_pilot[orow * R + R - 1] : ~0ull;
   int L, pbeg;
-  (void)row_setup<DT, D>(a, s_q, r, qh, L, pbeg);
+  float qf[epl<DT>()];
+  (void)row_setup<DT, D>(a, qf, r, qh, L, pbeg);
   const int h = qh / (a.H_q / a.H_kv);
   const uint64_t* wp = a.ws_pages + orow * a.page_stride;
+  const int np = p1 - p0;
+  if (tid < np) {
+    const int j = (int)(uint32_t)wp[p0 + tid];
+    s_j[tid] = j;
+    s_pp[tid] = a.page_indices[pbeg + j];
+  }
+  __syncthreads();
+  page_logits<DT, D>(a, qf, h, s_pp, np, s_z);
+  __syncthreads();
   bool cand = false;
   uint64_t ck = 0;
-  if (tid < (p1 - p0) * S) {
-    const int j = (int)(uint32_t)wp[p0 + tid / S];
-    const int t = j * S + tid % S;
+  if (tid < np * S) {
+    const int t = s_j[tid / S] * S + tid % S;
     if (t < L) {
-      ck = token_key<DT, D>(a, s_q, a.page_indices[pbeg + j], h, tid % S, t);
+      ck = desc_key(s_z[tid], (uint32_t)t);
       cand = ck < bar;
     }
   }
