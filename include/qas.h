@@ -324,11 +324,14 @@ qas_status qas_union_pages(const qas_batch* batch, const int32_t* q_indptr,
 /*
  * qas_chunk_attention - attention of every query of the chunk over its own
  * support, executed over group unions with MFMA tiles.  The cache must be
- * FP8 E4M3 with k_scale/v_scale (k = k_scale[h] * code).  Its V pool is laid
- * out for the MFMA operand: each (page, KV head) is [d][S] (dimension-major)
- * and token t of the page (w = t % 32, tau = t / 32) sits at position
- * (S/2)*((w/4) % 2) + 16*tau + 4*(w/8) + w % 4 of each dim row; K keeps
- * [S][d].  q is bf16
+ * FP8 E4M3 with k_scale/v_scale (k = k_scale[h] * code).  Its pools are
+ * laid out for the MFMA operands: each (page, KV head) tile of S * 128 bytes
+ * is a sequence of blocks of 64 lanes x 16 bytes (lane l: row = l % 32,
+ * hf = l / 32).  K: blocks (tau < S/32, ks < 2, c < 2) in that order, lane
+ * l holding token 32*tau + row, dims 64*ks + 32*hf + 16*c + [0, 16).  V:
+ * blocks (dt < 4, c < S/32), lane l holding dim 32*dt + row at k slots
+ * (S/2)*hf + 16*c + [0, 16), where token t (w = t % 32, tau = t / 32) is k
+ * slot (S/2)*((w/4) % 2) + 16*tau + 4*(w/8) + w % 4.  q is bf16
  * [N][H_q][128]; out is bf16 [N][H_q][128], lse float [N][H_q] (may be
  * NULL).  Page size 32 or 64.  QK^T runs with the query row quantised to
  * e4m3 (per-row scale) and PV with probabilities scaled by 256 and

@@ -17,11 +17,11 @@
 //      e4m3 as B (v_mfma 32x32x64 f8f6f4); each lane then owns one row's
 //      logits, so the mask (membership, t <= c_i, t < L) and the online
 //      softmax are lane-local; P is scaled by 256 and quantised to e4m3 and
-//      feeds O^T += V^T P^T from registers.  The fp8 V pool stores each
-//      (page, head) dimension-major, [d][S], with the tokens of a dim row in
-//      the order of the MFMA's k slots (those of the P bytes a lane holds),
-//      so every lane loads its V^T operand as S/2 contiguous bytes: no LDS
-//      staging or byte gathers;
+//      feeds O^T += V^T P^T from registers.  The fp8 pools store each
+//      (page, head) tile in operand order: blocks of 64 lanes x 16 bytes,
+//      each block holding one 16-byte piece of every lane's A (K) or B (V^T,
+//      tokens in the order of the MFMA's k slots) operand, so a wave load
+//      reads 1 KiB of consecutive bytes: no LDS staging or byte gathers;
 //   3. the four waves' states are merged in LDS and written at the queries'
 //      own output rows.
 #include "qas_device.h"
@@ -120,11 +120,21 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
     sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[qid] : -1;
   }
   __syncthreads();
+  // entries <= kUMaxUnion: every set entry's load is issued before any is used
+  constexpr int EPT = kUMaxUnion / kUThreads;
   const int entries = gr.nq * a.kq;
-  for (int e = tid; e < entries; e += kUThreads) {
+  int ids[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = min(tid + k * kUThreads, entries - 1);
     const int i = e / a.kq;
-    const int id = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
-    if (id >= 0 && id < n_pages) atomicOr(&sh.bm[i][id >> 5], 1u << (id & 31));
+    ids[k] = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * kUThreads;
+    const int id = ids[k];
+    if (e < entries && id >= 0 && id < n_pages) atomicOr(&sh.bm[e / a.kq][id >> 5], 1u << (id & 31));
   }
   __syncthreads();
   // each thread owns a contiguous run of bitmap words
@@ -154,7 +164,15 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   }
   __syncthreads();
   // physical pages of the union: independent loads, all in flight together
-  for (int u = tid; u < total; u += kUThreads) sh.uphys[u] = a.page_indices[pbeg + sh.ulist[u]];
+  // (total <= kUMaxUnion; an index past the union rereads its last page)
+  if (total > 0) {
+    int ph[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) ph[k] = a.page_indices[pbeg + sh.ulist[min(tid + k * kUThreads, total - 1)]];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (tid + k * kUThreads < total) sh.uphys[tid + k * kUThreads] = ph[k];
+  }
   if (tid == 0) sh.count = total;
   __syncthreads();
   return total;
@@ -194,14 +212,22 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   const bool row_ok = qi < gr.nq;
   const int cq = row_ok ? sh.cpos[qi] : -1;
   // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row
+  // (16-byte loads issued together; a row past the group reads the first
+  // query's row and is zeroed)
   float qf[64];
   {
     const size_t qbase = ((size_t)sh.qid[row_ok ? qi : 0] * a.H_q + h * G + hq) * kUD;
+    const char* qp = reinterpret_cast<const char*>(a.q) + qbase * 2;
+    uint4 raw[8];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 32; ++e)
-        qf[ks * 32 + e] = row_ok ? load_scalar<kBF16>(a.q, qbase + 64 * ks + 32 * hf + e) : 0.f;
+      for (int c = 0; c < 4; ++c) raw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) unpack16<kBF16>(raw[i], qf + 8 * i);
+    if (!row_ok)
+#pragma unroll
+      for (int e = 0; e < 64; ++e) qf[e] = 0.f;
   }
   float amax = 0.f;
 #pragma unroll
@@ -234,27 +260,29 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
 
-  // K operand of union page u: token 32*tau + lane%32, dims 64*ks + 32*hf + [0, 32)
+  // K operand of union page u: token 32*tau + lane%32, dims 64*ks + 32*hf + [0, 32).
+  // The tile is stored in operand order, blocks (tau, ks, c) of 64 lanes x
+  // 16 bytes, so each load reads 1 KiB of consecutive bytes.
   auto load_k = [&](int u, v8i_t (&kk)[NT][2]) {
     const size_t tile = ((size_t)sh.uphys[u] * H + h) * S * kUD;   // bytes (fp8)
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const char* p = kbase + tile + (size_t)(32 * tau + row) * kUD + 64 * ks + 32 * hf;
-        const uint4 x0 = load16(p), x1 = load16(p + 16);
+        const char* p = kbase + tile + (size_t)(2 * tau + ks) * 2048 + lane * 16;
+        const uint4 x0 = load16(p), x1 = load16(p + 1024);
         const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         kk[tau][ks] = *reinterpret_cast<const v8i_t*>(w);
       }
   };
-  // V^T operand of union page u: the fp8 V pool holds each (page, head) as
-  // [d][S] with the tokens of a dim row in the order the PV MFMA's k slots
-  // take them, so lane (dim 32 dt + row, hf) reads its S/2 bytes in one go
+  // V^T operand of union page u: lane (dim 32 dt + row, hf) holds k slots
+  // (S/2) hf + [0, S/2) of that dim row, in the order the PV MFMA takes the
+  // tokens; the tile is stored as blocks (dt, c) of 64 lanes x 16 bytes
   auto load_v = [&](int u, v8i_t (&vv)[4]) {
     const size_t tile = ((size_t)sh.uphys[u] * H + h) * S * kUD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const char* vr = vbase + tile + (size_t)(32 * dt + row) * S + (S / 2) * hf;
+      const char* vr = vbase + tile + (size_t)(dt * NT) * 1024 + lane * 16;
       uint32_t vw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       const uint4 y0 = load16(vr);
       vw[0] = y0.x;
@@ -262,7 +290,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
       vw[2] = y0.z;
       vw[3] = y0.w;
       if constexpr (NT == 2) {
-        const uint4 y1 = load16(vr + 16);
+        const uint4 y1 = load16(vr + 1024);
         vw[4] = y1.x;
         vw[5] = y1.y;
         vw[6] = y1.z;
@@ -288,44 +316,75 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
         st[tau] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[tau][ks], qop[ks], st[tau],
                                                                   0, 0, 0, 0, 0, 0);
     }
-    // mask + online softmax, lane-local per row
+    // mask + online softmax, lane-local per row.  Pages that every row of
+    // the wave sees whole (all but those at a causal limit or the sequence
+    // end) skip the per-token mask; element k = 16 tau + e of a lane is
+    // token 32 tau + 8 (e/4) + 4 hf + e%4 of the page.
     const bool member = row_ok && ((mk >> qi) & 1);
-    float zmax = -INFINITY;
+    const int pend = id * S + S - 1;
+    const bool full = __ballot(member && !(pend <= cq && pend < L)) == 0;
+    uint32_t okb = 0xffffffffu;                 // bit k: the row sees element k
+    float zr = -INFINITY;                       // unscaled row max
+    if (full) {
 #pragma unroll
-    for (int tau = 0; tau < NT; ++tau)
+      for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = id * S + 32 * tau + 8 * (e / 4) + 4 * hf + (e % 4);
-        const bool ok = member && t <= cq && t < L;
-        st[tau][e] = ok ? st[tau][e] * zscale : -INFINITY;
-        zmax = fmaxf(zmax, st[tau][e]);
-      }
-    zmax = lane_rowmax(zmax);
-    const float m_new = fmaxf(m_run, zmax);
-    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T operand: 32 e4m3 bytes
-    const bool live = m_new != -INFINITY;       // same for both lanes of a row
-    float lsum = 0.f;
-    if (live) {
+        for (int e = 0; e < 16; ++e) zr = fmaxf(zr, st[tau][e]);
+    } else {
+      okb = 0;
 #pragma unroll
       for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(st[tau][e] - m_new);       // 0 for masked
-          const uint32_t b = to_e4m3(p * 256.f);
-          lsum += __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
-          const int k = 16 * tau + e;
-          pw[k / 4] |= b << (8 * (k % 4));
+          const int t = id * S + 32 * tau + 8 * (e / 4) + 4 * hf + (e % 4);
+          const bool ok = t <= cq && t < L;
+          okb |= (ok ? 1u : 0u) << (16 * tau + e);
+          zr = fmaxf(zr, ok ? st[tau][e] : -INFINITY);
         }
     }
+    zr = member ? zr : -INFINITY;
+    // zscale >= 0 (products of scales); -inf stays -inf
+    const float zmax = lane_rowmax(zr == -INFINITY ? -INFINITY : zr * zscale);
+    const float m_new = fmaxf(m_run, zmax);
+    const bool live = m_new != -INFINITY;       // same for both lanes of a row
+    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T operand: 32 e4m3 bytes
+    float lsum = 0.f;
+    if (member && live) {
+      // p = 2^8 exp2(z - m_new) <= 256, quantised two bytes per conversion
+      const float off = 8.f - m_new;
+#pragma unroll
+      for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+          const int k = 16 * tau + e;
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(fmaf(st[tau][e + i], zscale, off));
+            if (!full) p[i] = ((okb >> (k + i)) & 1u) ? p[i] : 0.f;
+          }
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pw[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+        }
+      // the row sum over the quantised values (the ones the PV product uses)
+#pragma unroll
+      for (int w = 0; w < 4 * NT; ++w) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
+        lsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+      }
+    }
     lsum = lane_rowsum(lsum);
+    const float alpha = live ? fast_exp2(m_run - m_new) : 1.f;
     if (live) {
-      const float alpha = fast_exp2(m_run - m_new);
       l_run = l_run * alpha + lsum * (1.f / 256.f);
+      m_run = m_new;
+    }
+    if (__ballot(alpha != 1.f) != 0) {          // a row's max moved: rescale
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-      m_run = m_new;
     }
     const v8i_t pop = *reinterpret_cast<const v8i_t*>(pw);
     // O^T += V^T P^T: lane (dim 32 dt + lane%32, hf) holds the same k slots

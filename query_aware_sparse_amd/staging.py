@@ -107,10 +107,10 @@ def prefill(pc, case, lengths=None, device="cuda"):
 
 
 def mfma_token_order(S):
-    """Token held at each position of a dim row of an fp8 V page ([d][S] per
-    (page, KV head)): the order of the k slots of the union kernel's PV MFMA.
-    Token t (w = t % 32, tau = t // 32) sits at (S/2) * ((w // 4) % 2) +
-    16 * tau + 4 * (w // 8) + w % 4."""
+    """Token at each k slot of a dim row of V^T, the B operand of the union
+    kernel's PV MFMA: the slots a lane (row, hf) holds are (S/2) * hf + [0,
+    S/2), and token t (w = t % 32, tau = t // 32) sits at slot (S/2) *
+    ((w // 4) % 2) + 16 * tau + 4 * (w // 8) + w % 4."""
     order = np.empty(S, np.int64)
     for t in range(S):
         w, tau = t % 32, t // 32
@@ -118,32 +118,72 @@ def mfma_token_order(S):
     return order
 
 
+def union_k_order(S, d=128):
+    """Byte order of an fp8 K tile (one page, one KV head) for the union
+    kernel: entry j of the stored tile is byte order[j] of the token-major
+    [S][d] tile.  The tile is (S/32) * 2 * 2 blocks of 64 lanes x 16 bytes,
+    block (tau, ks, c) giving lane (row = l % 32, hf = l // 32) bytes 16c +
+    [0, 16) of its QK A operand: token 32 tau + row, dims 64 ks + 32 hf +
+    16 c + [0, 16).  Each wave load is then 1 KiB of consecutive bytes."""
+    assert d == 128 and S % 32 == 0
+    order = np.empty(S * d, np.int64)
+    j = 0
+    for tau in range(S // 32):
+        for ks in range(2):
+            for c in range(2):
+                for lane in range(64):
+                    tok = 32 * tau + lane % 32
+                    dim = 64 * ks + 32 * (lane // 32) + 16 * c
+                    order[j:j + 16] = tok * d + dim + np.arange(16)
+                    j += 16
+    return order
+
+
+def union_v_order(S, d=128):
+    """Byte order of an fp8 V tile for the union kernel, from the
+    token-major [S][d] tile: 4 * (S/32) blocks of 64 lanes x 16 bytes, block
+    (dt, c) giving lane (row = l % 32, hf = l // 32) k slots (S/2) hf + 16 c
+    + [0, 16) of dim row 32 dt + row of V^T (tokens in mfma_token_order)."""
+    assert d == 128 and S % 32 == 0
+    tok_at = mfma_token_order(S)
+    order = np.empty(S * d, np.int64)
+    j = 0
+    for dt in range(4):
+        for c in range(S // 32):
+            for lane in range(64):
+                dim = 32 * dt + lane % 32
+                slots = (S // 2) * (lane // 32) + 16 * c + np.arange(16)
+                order[j:j + 16] = tok_at[slots] * d + dim
+                j += 16
+    return order
+
+
 class ChunkBatch:
     """Device state of one or more multi-query chunks (one per request) sharing
     an fp8 pool: pages of request r are placed after those of r - 1.  K/V
-    tokens go to their pages by plain copies (this path reads no summaries):
-    K as [page][H][S][d], V as [page][H][d][S] in mfma_token_order(S)."""
+    tokens go to their pages by plain copies (this path reads no summaries),
+    each (page, KV head) tile of S * d bytes in the union kernel's operand
+    order (union_k_order, union_v_order)."""
 
     def __init__(self, cases, device="cuda"):
         c0 = cases[0]
         H, S, d = c0.H_kv, c0.S, c0.d
         self.S = S
         pool = sum(c.num_pool_pages for c in cases)
-        shape = (pool, H, S, d)
+        shape = (pool, H, S, d)                     # sizes only: tiles are in operand order
         self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)   # e4m3 NaN
-        self.v_pool = torch.full((pool, H, d, S), 0x7F, dtype=torch.uint8, device=device)
-        order = torch.from_numpy(mfma_token_order(S)).to(device)
+        self.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
+        korder = torch.from_numpy(union_k_order(S, d)).to(device)
+        vorder = torch.from_numpy(union_v_order(S, d)).to(device)
         lengths, pages, off = [], [], 0
         for c in cases:
             P = ceil_div(c.L, S)
             phys = torch.from_numpy(np.asarray(c.pages[:P], np.int64) + off).to(device)
-            for pool_t, raw in ((self.k_pool, c.keys), (self.v_pool, c.values)):
+            for pool_t, raw, order in ((self.k_pool, c.keys, korder), (self.v_pool, c.values, vorder)):
                 t = np.zeros((P * S, H, d), np.uint8)
                 t[:c.L] = raw[:c.L]
                 tt = torch.from_numpy(t).to(device).view(P, S, H, d).permute(0, 2, 1, 3)
-                if pool_t is self.v_pool:           # [P][H][d][S], tokens in MFMA order
-                    tt = tt.permute(0, 1, 3, 2)[..., order]
-                pool_t[phys] = tt.contiguous()
+                pool_t.view(pool, H, S * d)[phys] = tt.reshape(P, H, S * d)[..., order].contiguous()
             lengths.append(c.L)
             pages.append(np.asarray(c.pages[:P], np.int32) + off)
             off += c.num_pool_pages
