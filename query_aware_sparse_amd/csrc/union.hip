@@ -42,6 +42,7 @@ constexpr int kUMaxWords = 512;             // bitmap words: pages < 16384
 constexpr int kUMaxUnion = 1024;            // union pages per group
 constexpr int kUD = 128;                    // head dim
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kULazy = 0.75f;             // running-max slack, log2 units
 
 struct UnionShared {
   uint32_t bm[kUMaxGroup][kUMaxWords];
@@ -247,8 +248,9 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
     }
     qop[ks] = *reinterpret_cast<v8i_t*>(w);
   }
-  // logit scale (log2 units) of this row
-  const float zscale = qs * a.k_scale[h] * a.sm_scale * kLog2e;
+  // logit scale (log2 units) of this row, floored at a tiny positive value
+  // so that a masked logit (-inf) times it stays -inf
+  const float zscale = fmaxf(qs * a.k_scale[h] * a.sm_scale * kLog2e, 1e-30f);
 
   float m_run = -INFINITY, l_run = 0.f;
   v16f_t acc[4];
@@ -299,12 +301,19 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
       vv[dt] = *reinterpret_cast<const v8i_t*>(vw);
     }
   };
+  // The operands of a wave's next page are loaded into the registers of the
+  // current one as soon as its MFMAs have read them (K after QK, V after PV),
+  // so the loads fly during the softmax and the MFMAs; the last page's
+  // loads repeat it and are not used.
+  v8i_t kop[NT][2], vop[4];
+  if (wave < U) {
+    load_k(wave, kop);
+    load_v(wave, vop);
+  }
   for (int u = wave; u < U; u += kUWaves) {
     const int id = sh.ulist[u];
     const unsigned char mk = sh.umask[u];
-    v8i_t kop[NT][2], vop[4];
-    load_k(u, kop);
-    load_v(u, vop);
+    const int un = min(u + kUWaves, U - 1);
     // S^T = K Q^T: lane holds row `row`, tokens 32 tau + 8 (e/4) + 4 hf + e%4
     v16f_t st[NT];
 #pragma unroll
@@ -316,42 +325,39 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
         st[tau] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[tau][ks], qop[ks], st[tau],
                                                                   0, 0, 0, 0, 0, 0);
     }
+    load_k(un, kop);
     // mask + online softmax, lane-local per row.  Pages that every row of
     // the wave sees whole (all but those at a causal limit or the sequence
     // end) skip the per-token mask; element k = 16 tau + e of a lane is
     // token 32 tau + 8 (e/4) + 4 hf + e%4 of the page.
     const bool member = row_ok && ((mk >> qi) & 1);
     const int pend = id * S + S - 1;
-    const bool full = __ballot(member && !(pend <= cq && pend < L)) == 0;
-    uint32_t okb = 0xffffffffu;                 // bit k: the row sees element k
-    float zr = -INFINITY;                       // unscaled row max
-    if (full) {
-#pragma unroll
-      for (int tau = 0; tau < NT; ++tau)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) zr = fmaxf(zr, st[tau][e]);
-    } else {
-      okb = 0;
+    if (__ballot(member && !(pend <= cq && pend < L)) != 0) {
 #pragma unroll
       for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int t = id * S + 32 * tau + 8 * (e / 4) + 4 * hf + (e % 4);
-          const bool ok = t <= cq && t < L;
-          okb |= (ok ? 1u : 0u) << (16 * tau + e);
-          zr = fmaxf(zr, ok ? st[tau][e] : -INFINITY);
+          st[tau][e] = (t <= cq && t < L) ? st[tau][e] : -INFINITY;
         }
     }
+    float zr = -INFINITY;                       // unscaled row max
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zr = fmaxf(zr, st[tau][e]);
     zr = member ? zr : -INFINITY;
-    // zscale >= 0 (products of scales); -inf stays -inf
     const float zmax = lane_rowmax(zr == -INFINITY ? -INFINITY : zr * zscale);
-    const float m_new = fmaxf(m_run, zmax);
-    const bool live = m_new != -INFINITY;       // same for both lanes of a row
+    // The running max moves only when a row's max passes it by more than
+    // kULazy (log2 units): p = 2^8 exp2(z - m) then stays below
+    // 2^(8 + kULazy) < 448, inside e4m3, and most pages skip the rescale.
+    const bool grow = zmax > m_run + kULazy;    // same for both lanes of a row
+    const float m_use = grow ? zmax : m_run;
+    const bool live = m_use != -INFINITY;
     uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T operand: 32 e4m3 bytes
     float lsum = 0.f;
     if (member && live) {
-      // p = 2^8 exp2(z - m_new) <= 256, quantised two bytes per conversion
-      const float off = 8.f - m_new;
+      const float off = 8.f - m_use;
 #pragma unroll
       for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
@@ -359,10 +365,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
           const int k = 16 * tau + e;
           float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(fmaf(st[tau][e + i], zscale, off));
-            if (!full) p[i] = ((okb >> (k + i)) & 1u) ? p[i] : 0.f;
-          }
+          for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(st[tau][e + i], zscale, off));
           const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           pw[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
         }
@@ -375,12 +378,12 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
       }
     }
     lsum = lane_rowsum(lsum);
-    const float alpha = live ? fast_exp2(m_run - m_new) : 1.f;
+    const float alpha = grow ? fast_exp2(m_run - m_use) : 1.f;   // 0 on a row's first page
     if (live) {
       l_run = l_run * alpha + lsum * (1.f / 256.f);
-      m_run = m_new;
+      m_run = m_use;
     }
-    if (__ballot(alpha != 1.f) != 0) {          // a row's max moved: rescale
+    if (__ballot(grow) != 0) {                  // a row's max moved: rescale
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -393,6 +396,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
     for (int dt = 0; dt < 4; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[dt], pop, acc[dt], 0, 0, 0, 0,
                                                                 0, 0);
+    load_v(un, vop);
   }
 
   // ---- merge the waves: 2,3 -> 0,1 then 1 -> 0 ------------------------------
