@@ -5,20 +5,22 @@
 // bound is below tau_R, since no token of the remaining pages can then enter
 // the top R.  The reads are data dependent: tight bounds stop early, loose
 // ones open nearly every page.  Rounds read whole pages (first enough for R
-// tokens, then twice as many each round), so the pages opened are at most
-// about twice the pages the page-by-page rule would read.
+// tokens, then twice as many each round), so a search that stops in the
+// pilot opens at most about twice the pages the page-by-page rule would
+// read; one that does not reads the remaining candidate pages in parallel.
 //
-// One workgroup of 512 threads per (request, query head).  Bounds are this
-// head's own ([Quest] §1.1 eq. (2)-(3) with its query, not the group max),
-// each raised by 2^-15 * sum_j |q_j| max(|m_j|, |M_j|): that covers the fp32
-// rounding of the bound and of a logit (sums of at most 128 products), so a
-// page whose raised bound is below tau_R holds no token whose computed logit
-// could reach tau_R.  Pages are sorted by 64-bit keys (bound descending,
-// index ascending) with a bitonic sort in LDS; then each round reads 512
-// tokens (one per thread, logit = q . k in fp32, unscaled: the bound's
-// units), keeps the tokens that beat the current R-th, and merges them into
-// the sorted list of the best R by rank (keys (logit descending, token
-// ascending) are unique, so ties between logits go to the lower token).
+// Four launches: page bounds for every (request, query head); the pilot,
+// one 512-thread workgroup per (request, query head); the scan of the pages
+// the pilot leaves, one workgroup per 512 tokens; the merge of the lists.
+// Bounds are the head's own ([Quest] §1.1 eq. (2)-(3) with its query, not
+// the group max), each raised by 2^-15 * sum_j |q_j| max(|m_j|, |M_j|):
+// that covers the fp32 rounding of the bound and of a logit (sums of at
+// most 128 products, in any order), so a page whose raised bound is below
+// tau_R holds no token whose computed logit could reach tau_R.  Pages and
+// tokens are ordered by 64-bit keys: (bound descending, page ascending) and
+// (logit q . k in fp32, unscaled: the bound's units, descending; token
+// ascending).  Keys are unique, so ties between logits go to the lower
+// token.
 #include "qas_device.h"
 #include "qas_internal.h"
 #include "topk_block.h"
@@ -33,6 +35,7 @@ constexpr int kTrMaxPages = 4096;
 constexpr int kTrMaxR = 512;
 constexpr int kTrBuf = kTrMaxR + kTrThreads;     // kept + new candidates of a round
 constexpr int kTrMaxPilot = 64;                  // pages of the pilot
+constexpr int kTrBail = 4;                       // pilot rounds worth of pages before the scan
 
 // 64-bit key, ascending = value descending then index ascending
 __device__ __forceinline__ uint64_t desc_key(float v, uint32_t idx) {
@@ -225,14 +228,16 @@ __global__ __launch_bounds__(kTbThreads) void topr_bounds_kernel(ToprArgs a) {
   }
 }
 
-// 1. plan: the branch-and-bound pilot.  The a.pilot_pages pages of largest
-//    bound (ties to the lower index: the page keys' order) are picked by the
-//    workgroup top-K select and ranked; the pilot reads them in that order.
-//    A row whose stop rule fires in the pilot, or whose next bound outside
-//    it is below tau_R, or that has no other page, is finished here;
-//    otherwise the pilot's best R go to the workspace with the list of the
-//    other pages whose bound is not below the pilot's tau_R (all other pages
-//    while fewer than R tokens are known), left to the scan.
+// 1. plan: the branch-and-bound pilot.  The pages of largest bound that
+//    whole rounds can read within a.pilot_pages (ties to the lower index:
+//    the page keys' order) are picked by the workgroup top-K select and
+//    ranked; the pilot reads them in that order, and gives up early when
+//    too many unread pages still reach tau_R.  A row whose stop rule fires,
+//    or whose largest unread bound is below tau_R, or that has no page left,
+//    is finished here; otherwise the pilot's best R go to the workspace with
+//    the list of the unread pages whose bound is not below the pilot's
+//    tau_R (every unread page while fewer than R tokens are known), left to
+//    the scan.
 template <int DT, int D, int PT>
 __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   // PT bounds per thread: rows of up to kTrThreads * PT pages
@@ -295,10 +300,21 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
     __syncthreads();
   }
 
-  // pilot rounds over the pilot pages in order
+  // pilot rounds over the pilot pages in order.  After a round, a pilot
+  // whose bounds are loose against the logits it has read (even the largest
+  // one is below the bound of its last page) and that still has more than
+  // kTrBail rounds' worth of unread pages with bounds not below tau_R would
+  // not end soon: it hands them to the scan (the result is the same; only
+  // the schedule changes).
   int np_round = s0;
   int kept = 0, cur = 0, next = 0;
   bool stopped = false;
+  // unread: a page outside the pilot, or a pilot page ranked at or after `next`
+  auto unread = [&](int k, int nxt) {
+    return t.valid(k) &&
+           (!t.selected(k) ||
+            (nxt < npil && !(desc_key(t.v[k], (uint32_t)(t.j0 + k)) < s_sel[nxt])));
+  };
   while (next < npil) {
     if (kept >= R && key_value(s_sel[next]) < key_value(s_buf[cur][R - 1])) {
       stopped = true;
@@ -324,32 +340,45 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
     __syncthreads();
     if (total > 0) rank_merge(s_buf, cur, kept, total, R);
     next += np;
+    // (not before two rounds: tau_R from the first alone leaves the scan
+    // most tokens as candidates)
+    if (kept >= R && next >= 3 * s0 && next < npil &&
+        key_value(s_buf[cur][0]) < key_value(s_sel[npil - 1])) {
+      const float tr = key_value(s_buf[cur][R - 1]);
+      int above = 0;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) above += (unread(k, next) && !(t.v[k] < tr)) ? 1 : 0;
+      int n_above;
+      (void)tk::block_excl_scan<kTrWaves>(above, tsh.scan[1], &n_above);
+      if (n_above > kTrBail * np_round) break;
+    }
   }
   const float tau = kept >= R ? key_value(s_buf[cur][R - 1]) : -INFINITY;
+  // largest bound not read: the next pilot page's or the best outside the pilot
+  const float rest_max = fmaxf(out_max, next < npil ? key_value(s_sel[next]) : -INFINITY);
   int* st = a.ws_state + orow * 4;
-  if (stopped || npil == P || (kept >= R && out_max < tau)) {
+  if (stopped || (next == npil && npil == P) || (kept >= R && rest_max < tau)) {
     write_result(a, orow, s_buf[cur], kept, next);
     if (tid == 0) st[0] = 1;
     return;
   }
-  // the other pages the pilot cannot exclude, in page order
+  // the unread pages the pilot cannot exclude, in page order
   int mine = 0;
 #pragma unroll
-  for (int k = 0; k < PT; ++k)
-    mine += (t.valid(k) && !t.selected(k) && (kept < R || !(t.v[k] < tau))) ? 1 : 0;
+  for (int k = 0; k < PT; ++k) mine += (unread(k, next) && (kept < R || !(t.v[k] < tau))) ? 1 : 0;
   int n_scan;
   int at = tk::block_excl_scan<kTrWaves>(mine, tsh.scan[0], &n_scan);
   uint64_t* wp = a.ws_pages + orow * a.page_stride;
   __syncthreads();                                    // every wk read above is done
 #pragma unroll
   for (int k = 0; k < PT; ++k)
-    if (t.valid(k) && !t.selected(k) && (kept < R || !(t.v[k] < tau)))
+    if (unread(k, next) && (kept < R || !(t.v[k] < tau)))
       wp[at++] = desc_key(t.v[k], (uint32_t)(t.j0 + k));
   uint64_t* wb = a.ws_pilot + orow * R;
   for (int i = tid; i < kept; i += kTrThreads) wb[i] = s_buf[cur][i];
   if (tid == 0) {
     st[0] = 0;
-    st[1] = npil;          // pages read by the pilot
+    st[1] = next;          // pages read by the pilot
     st[2] = n_scan;        // pages left to the scan
     st[3] = kept;
   }
