@@ -42,32 +42,35 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 CHUNK_METRIC = "µs per multi-query chunk call + fp8 MFMA TFLOP/s, 64K ctx, 512 queries, union-8"
 
 # HBM traffic of one decode-layer call from two rocprofv3 --pmc passes of this
-# bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the timed
-# dispatches), scaled by what the same counters read for a plain 1 GiB copy
-# (`bench.py --copy-calibration`): FETCH_SIZE read 524303 KiB and WRITE_SIZE
-# 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write x1.0.  Valid only
-# for the kernel sources they were taken on (sha256 of csrc/).
+# bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the pass's
+# dispatches, `--no-next-rows`), scaled by what the same counters read for a
+# plain 1 GiB copy (`bench.py --copy-calibration`): FETCH_SIZE read 524301.6
+# KiB and WRITE_SIZE 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write
+# x1.0.  Valid only for the sources the decode-layer call is built from
+# (DECODE_SOURCES).
+DECODE_SOURCES = ("score.hip", "decode.hip", "decode_f32.hip", "decode_f16.hip",
+                  "decode_bf16.hip", "decode_kernel.h", "topk_block.h", "qas_device.h",
+                  "qas_internal.h", "qas_api.cpp")
 PMC_TRAFFIC = {
-    "csrc_sha256": "24aa17043df6fac23bec6b8f7695ad1b21a590bd52e6ec94aa553289a6ec58d5",
-    "fetch_kib": {"score_kernel": 16557.8, "decode_kernel": 34082.0},
-    "write_kib": {"score_kernel": 614.8, "decode_kernel": 173.3},
+    "sources_sha256": "f07b734a36620307d82937554ae5626d314ab3651228fdb6ba208c99dc681fce",
+    "fetch_kib": {"score_kernel": 16561.3, "decode_kernel": 34084.4},
+    "write_kib": {"score_kernel": 617.0, "decode_kernel": 173.3},
     # the same passes, call on the e4m3 summary copy
-    "fetch_kib_fp8": {"score8_kernel": 8495.9, "decode_kernel": 34082.0},
+    "fetch_kib_fp8": {"score8_kernel": 8498.4, "decode_kernel": 34084.4},
     "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.3},
     "fetch_factor": 2.0,
     "write_factor": 1.0,
 }
 
 
-def csrc_sha256():
+def decode_sources_sha256():
     import hashlib
     d = os.path.join(ROOT, "query_aware_sparse_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -76,7 +79,7 @@ def pmc_traffic_bytes(fp8=False):
     the e4m3 summary copy if fp8), or None if the kernels changed since they
     were taken."""
     t = PMC_TRAFFIC
-    if t["csrc_sha256"] is None or t["csrc_sha256"] != csrc_sha256():
+    if t["sources_sha256"] is None or t["sources_sha256"] != decode_sources_sha256():
         return None
     sfx = "_fp8" if fp8 else ""
     kib = (sum(t["fetch_kib" + sfx].values()) * t["fetch_factor"] +
@@ -421,6 +424,8 @@ def main():
     ap.add_argument("--workload", choices=("decode", "chunk"), default="decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the NEXT-4 timings (counter passes of the decode-layer call)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures the "
@@ -485,7 +490,8 @@ def main():
 
     ms_per_step, call_us, steps = time_decode_calls(torch, args, NL, call, out)
     ms_fp8, us_fp8, _ = time_decode_calls(torch, args, NL, call_fp8, out)
-    next_rows = bench_next_rows(torch, qas, args, case, exact, db, qs, NL)
+    next_rows = None if args.no_next_rows else bench_next_rows(torch, qas, args, case, exact, db,
+                                                               qs, NL)
     bytes_fp8 = traffic.decode_layer_bytes(
         B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
         pages_scanned=L // case.S, page_heads_selected=case.H_kv * case.K,
