@@ -385,19 +385,21 @@ qas_status qas_decode_positions(const qas_cache* cache, const qas_batch* batch,
  * bound is raised by 2^-15 * sum_j |q_j| max(|m_j|, |M_j|) so that fp32
  * rounding of bounds and logits cannot end the search early.  Logits are the
  * unscaled dot products q . k_t (fp32) over tokens t < seq_lens[r]; the
- * number of pages read is data dependent (up to all of them).  Three
- * launches: per row a pilot reads pages in bound order (up to 64 pages) and
- * finishes the row if the stop rule fires; otherwise every page whose bound
+ * number of pages read is data dependent (up to all of them).  Four
+ * launches: the bounds of every page; per row a pilot that reads pages in
+ * bound order, in rounds of whole pages within 64 pages, and finishes the
+ * row if the stop rule fires (it hands over early when its bounds are loose
+ * against the logits it has read); otherwise every unread page whose bound
  * is not below the pilot's tau_R (which can only rise) is read by many
- * workgroups at once, and a merge keeps the best R.  pages_read counts the
- * pilot's pages and the pages read after it.
+ * workgroups at once, and a merge keeps the best R.  The result does not
+ * depend on that schedule; pages_read counts the pages actually read.
  *
  *   q           device [B][H_q][d], kv_dtype (fp32, fp16 or bf16 caches)
  *   R           1 .. 512; requests of up to 4096 pages (else QAS_ERR_UNSUPPORTED)
  *   top_tokens  device [B][H_q][R] int32: token positions ordered by logit
  *               descending, then position ascending; -1 past the tokens held
  *   top_logits  device [B][H_q][R] float: their logits, -inf past the end
- *   pages_read  device [B][H_q] int32 or NULL: pages opened before the stop
+ *   pages_read  device [B][H_q] int32 or NULL: pages read (pilot and scan)
  */
 qas_status qas_exact_top_r(const qas_cache* cache, const qas_batch* batch, const void* q,
                            int32_t q_dtype, int32_t num_q_heads, int32_t R,

@@ -132,6 +132,30 @@ def test_exact_top_r_full_size_layer(qas):
     say(f"[top-R] 32K layer R=64: pages read per head min {pr.min()} max {pr.max()} of 2048")
 
 
+def test_exact_top_r_degenerate_rows(qas):
+    """A ragged batch with an empty request, a one-token request and one whose
+    last page is partly filled: the empty rows return -1 / -inf and no pages,
+    the others match brute force (R above and below the row's token count)."""
+    from query_aware_sparse_amd.staging import PagedCache, prefill
+    case = batched_gqa_append(B=4, L_min=200, L_max=3000, H_q=8, H_kv=2, steps=0)
+    case.seq_lens[1] = 0
+    case.seq_lens[2] = 1
+    case.seq_lens[3] = 16 * 40 + 7
+    pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype)
+    db = prefill(pc, case)
+    for R in (3, 64):
+        say(f"[top-R] degenerate rows R={R}")
+        tok, lg, pr = _run(qas, pc, db, case, R)
+        assert np.all(tok[1] == -1) and np.all(np.isneginf(lg[1])) and np.all(pr[1] == 0)
+        for r in (0, 2, 3):
+            L = int(case.seq_lens[r])
+            keys = oracle.decode(case.keys[r][:L], case.kv_dtype)
+            qh = oracle.decode(case.q[0][r], case.q_dtype)
+            for i in range(case.H_q):
+                _check_row(qh[i], keys[:, i // case.g], L, case.S, R, tok[r, i], lg[r, i],
+                           pr[r, i], f"R={R} r={r} head={i}")
+
+
 def test_exact_top_r_validation_without_launch(qas):
     assert qas.lib.qas_exact_top_r(None, None, None, 0, 1, 1, None, None, None, None, 0,
                                    None) == 1
