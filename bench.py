@@ -13,7 +13,10 @@ Infinity Cache; the 32 calls are captured once in a HIP graph and replayed.
 
 The value is the achieved rate on the bytes the method must move per call
 (summary scan + selected K/V + q/o + the append's row and summary record),
-divided by the measured time per call.
+divided by the measured time per call.  Beside it: the same call on the
+e4m3 summary copy, the call under a cold-cache protocol (a read of 1 GiB
+before each of 200 event-timed calls, p50 and p95, under
+`config.cold_flush`), and the NEXT-4 entry points.
 
     python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline]
 
@@ -362,6 +365,30 @@ def time_decode_calls(torch, args, NL, call, out):
     return wall * 1e3 / steps, call_us, steps
 
 
+def time_cold_flush(torch, call, warm=20, timed=200):
+    """The cold-cache protocol: before every call a read of a 1 GiB buffer
+    (a sum) evicts the 256 MB Infinity Cache and the L2s; each call is
+    event-timed on its own (eager launches, layer 0); 20 warm-up calls, then
+    200 timed.  The flush only reads: a read-and-write pass leaves 1 GiB of
+    dirty lines whose write-back then lands inside the timed call.  Returns
+    (p50, p95) in microseconds."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(timed)]
+    for i in range(warm + timed):
+        sink.copy_(flush.sum().view(1))
+        if i >= warm:
+            evs[i - warm][0].record()
+        call(0)
+        if i >= warm:
+            evs[i - warm][1].record()
+    torch.cuda.synchronize()
+    t = np.sort([a.elapsed_time(b) * 1e3 for a, b in evs])
+    del flush, sink
+    return float(np.percentile(t, 50)), float(np.percentile(t, 95))
+
+
 def bench_next_rows(torch, qas, args, case, exact, db, qs, NL):
     """Timings of the NEXT-4 entry points on the same layer caches, replayed
     from a HIP graph like the decode-layer call: a 4-token speculative
@@ -490,6 +517,9 @@ def main():
 
     ms_per_step, call_us, steps = time_decode_calls(torch, args, NL, call, out)
     ms_fp8, us_fp8, _ = time_decode_calls(torch, args, NL, call_fp8, out)
+    cold_p50, cold_p95 = time_cold_flush(torch, call)
+    log(f"[bench] cold caches (1 GiB read before each call): p50 {cold_p50:.2f} us, "
+        f"p95 {cold_p95:.2f} us")
     next_rows = None if args.no_next_rows else bench_next_rows(torch, qas, args, case, exact, db,
                                                                qs, NL)
     bytes_fp8 = traffic.decode_layer_bytes(
@@ -526,6 +556,11 @@ def main():
                        "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
                        "ms_per_step_wall": round(ms_fp8, 6),
                        "traffic": pmc_traffic_bytes(fp8=True)},
+                   "cold_flush": {
+                       "protocol": "1 GiB read (sum) before each call, eager launch, "
+                                   "20 warm-up + 200 timed calls, event-timed each",
+                       "p50_us": round(cold_p50, 3), "p95_us": round(cold_p95, 3),
+                       "GB/s_p50": round(total / (cold_p50 * 1e-6) / 1e9, 1)},
                    "next_rows": next_rows},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
