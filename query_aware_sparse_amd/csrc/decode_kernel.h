@@ -124,6 +124,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   if constexpr (TPT > 0)
     t.issue_x4(a.scores + ((size_t)r * H + h) * a.score_stride,
                a.phys_rows + (size_t)r * a.score_stride, cap);
+  // this lane's 16-byte slice of each query head of the group, loaded now so
+  // that it lands during the selection instead of before the K/V stream
+  uint4 qraw[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg)
+    qraw[gg] = load16(reinterpret_cast<const char*>(a.q) +
+                      (((size_t)r * a.H_q + h * G + gg) * D + (lane % RL) * EPL) * BYTES);
   // row r: a request, or draft position r % gamma of request r / gamma whose
   // causal limit is its own position (length seq_lens - (gamma - 1 - i))
   const int req = r / a.gamma;
@@ -203,15 +210,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   // ---- 2. stream K/V of the pages, online softmax per lane -----------------
   const int c = lane % RL;
   const int trow = lane / RL;
-  const int NI = S > TPI ? S / TPI : 1;       // token groups per page
+  const int NI = S > TPI ? S / TPI : 1;       // token groups per page (a power of two)
+  const int lni = __ffs(NI) - 1;
   const int units = npg * NI;
+  // byte offsets: page stride and head offset are uniform, so a load's
+  // address is one 64-bit multiply-add of its physical page
+  const size_t pstride = (size_t)H * S * D * BYTES;
+  const uint32_t hoff = (uint32_t)(h * S * D * BYTES) + c * 16;
   const float qscale = a.sm_scale * kLog2e;   // logits in log2 units
   float qf[G][EPL];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    const size_t qo = ((size_t)r * a.H_q + h * G + gg) * D + c * EPL;
+    unpack16<DT>(qraw[gg], qf[gg]);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[gg][e] = load_scalar<DT>(a.q, qo + e) * qscale;
+    for (int e = 0; e < EPL; ++e) qf[gg][e] *= qscale;
   }
   float m_run[G], l_run[G], acc[G][EPL];
 #pragma unroll
@@ -238,10 +250,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int b = 0; b < UNR; ++b) {
       const int u = min(u0 + b * kDecWaves, units - 1);
-      const int pi = u / NI, gi = u - (u / NI) * NI;
+      const int pi = u >> lni, gi = u & (NI - 1);
       const int tip = gi * TPI + trow;
       ok[b] = (u0 + b * kDecWaves < units) & (tip < s_ntok[pi]);
-      offs[b] = ((((size_t)s_phys[pi] * H + h) * S + min(tip, S - 1)) * D) * BYTES + c * 16;
+      offs[b] = (size_t)(uint32_t)s_phys[pi] * pstride +
+                (hoff + (uint32_t)(min(tip, S - 1) * D * BYTES));
     }
 #pragma unroll
     for (int b = 0; b < UNR; ++b) kr[b] = load16(kbase + offs[b]);
