@@ -46,7 +46,7 @@ CHUNK_METRIC = "µs per multi-query chunk call + fp8 MFMA TFLOP/s, 64K ctx, 512 
 
 # HBM traffic of one decode-layer call from two rocprofv3 --pmc passes of this
 # bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the pass's
-# dispatches, `--no-next-rows`), scaled by what the same counters read for a
+# dispatches, `--no-next-rows --no-cold-flush`), scaled by what the same counters read for a
 # plain 1 GiB copy (`bench.py --copy-calibration`): FETCH_SIZE read 524301.6
 # KiB and WRITE_SIZE 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write
 # x1.0.  Valid only for the sources the decode-layer call is built from
@@ -55,12 +55,12 @@ DECODE_SOURCES = ("score.hip", "decode.hip", "decode_f32.hip", "decode_f16.hip",
                   "decode_bf16.hip", "decode_kernel.h", "topk_block.h", "qas_device.h",
                   "qas_internal.h", "qas_api.cpp")
 PMC_TRAFFIC = {
-    "sources_sha256": "f07b734a36620307d82937554ae5626d314ab3651228fdb6ba208c99dc681fce",
-    "fetch_kib": {"score_kernel": 16561.3, "decode_kernel": 34084.4},
-    "write_kib": {"score_kernel": 617.0, "decode_kernel": 173.3},
+    "sources_sha256": "a352bbf5bba14f890b4944b10e75ba4e6f9b96c6701450d07f5ab02ab8f42989",
+    "fetch_kib": {"score_kernel": 16562.1, "decode_kernel": 34061.7},
+    "write_kib": {"score_kernel": 610.0, "decode_kernel": 173.2},
     # the same passes, call on the e4m3 summary copy
-    "fetch_kib_fp8": {"score8_kernel": 8498.4, "decode_kernel": 34084.4},
-    "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.3},
+    "fetch_kib_fp8": {"score8_kernel": 8498.1, "decode_kernel": 34061.7},
+    "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.2},
     "fetch_factor": 2.0,
     "write_factor": 1.0,
 }
@@ -453,6 +453,8 @@ def main():
                     help="only run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the NEXT-4 timings (counter passes of the decode-layer call)")
+    ap.add_argument("--no-cold-flush", action="store_true",
+                    help="skip the cold-cache protocol (counter passes of the decode-layer call)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures the "
@@ -517,9 +519,14 @@ def main():
 
     ms_per_step, call_us, steps = time_decode_calls(torch, args, NL, call, out)
     ms_fp8, us_fp8, _ = time_decode_calls(torch, args, NL, call_fp8, out)
-    cold_p50, cold_p95 = time_cold_flush(torch, call)
-    log(f"[bench] cold caches (1 GiB read before each call): p50 {cold_p50:.2f} us, "
-        f"p95 {cold_p95:.2f} us")
+    cold = None
+    if not args.no_cold_flush:
+        cold_p50, cold_p95 = time_cold_flush(torch, call)
+        log(f"[bench] cold caches (1 GiB read before each call): p50 {cold_p50:.2f} us, "
+            f"p95 {cold_p95:.2f} us")
+        cold = {"protocol": "1 GiB read (sum) before each call, eager launch, "
+                            "20 warm-up + 200 timed calls, event-timed each",
+                "p50_us": round(cold_p50, 3), "p95_us": round(cold_p95, 3)}
     next_rows = None if args.no_next_rows else bench_next_rows(torch, qas, args, case, exact, db,
                                                                qs, NL)
     bytes_fp8 = traffic.decode_layer_bytes(
@@ -534,6 +541,8 @@ def main():
         pages_scanned=L // case.S, page_heads_selected=case.H_kv * case.K,
         append_tokens=1)
     total = nbytes["total"]
+    if cold:
+        cold["GB/s_p50"] = round(total / (cold["p50_us"] * 1e-6) / 1e9, 1)
     value = total / (ms_per_step * 1e-3) / 1e9
     achieved = total / (call_us * 1e-6) / 1e9
     log(f"[bench] {steps} calls: {ms_per_step * 1e3:.2f} us/call (wall), "
@@ -556,11 +565,7 @@ def main():
                        "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
                        "ms_per_step_wall": round(ms_fp8, 6),
                        "traffic": pmc_traffic_bytes(fp8=True)},
-                   "cold_flush": {
-                       "protocol": "1 GiB read (sum) before each call, eager launch, "
-                                   "20 warm-up + 200 timed calls, event-timed each",
-                       "p50_us": round(cold_p50, 3), "p95_us": round(cold_p95, 3),
-                       "GB/s_p50": round(total / (cold_p50 * 1e-6) / 1e9, 1)},
+                   "cold_flush": cold,
                    "next_rows": next_rows},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
