@@ -129,3 +129,31 @@ def test_selection_capacity_and_select_validation(qas):
     assert need >= lib.qas_workspace_bytes(2, byref(c), byref(b), 32, 64)
     assert lib.qas_decode_layer_mixed(byref(c), byref(b), 8, 1, 32, 64, 4, 512, 0.1, None, None,
                                       None, 8, None, 8, need - 1, None) == 5
+
+
+def test_next_row_workspace_sizes(qas):
+    """Workspace sizes of the draft-position and exact top-R calls (no launch):
+    0 for invalid arguments, 256-byte granular, growing with the draft count
+    and with R; the position call's size is the decode layer's over
+    B * gamma rows."""
+    from ctypes import byref
+    lib = qas.lib
+    c, b = _cache(qas), _batch(qas)
+    # draft positions: gamma rows per request
+    p1 = qas.qas_positions_workspace_bytes(c, b, 32, 1, 64)
+    p4 = qas.qas_positions_workspace_bytes(c, b, 32, 4, 64)
+    rows4 = _batch(qas, batch=b.batch * 4)
+    assert p1 == lib.qas_workspace_bytes(2, byref(c), byref(b), 32, 64)
+    assert p4 == lib.qas_workspace_bytes(2, byref(c), byref(rows4), 32, 64)
+    assert 0 < p1 < p4 and p4 % 256 == 0
+    assert qas.qas_positions_workspace_bytes(c, b, 32, 0, 64) == 0
+    assert qas.qas_positions_workspace_bytes(c, _batch(qas, batch=0), 32, 4, 64) == 0
+    # exact top-R
+    t1 = qas.qas_exact_top_r_workspace_bytes(c, b, 32, 1)
+    t64 = qas.qas_exact_top_r_workspace_bytes(c, b, 32, 64)
+    assert 0 < t1 < t64 and t1 % 256 == 0 and t64 % 256 == 0
+    assert qas.qas_exact_top_r_workspace_bytes(c, b, 32, 0) == 0
+    assert qas.qas_exact_top_r_workspace_bytes(c, b, 0, 64) == 0
+    assert qas.qas_exact_top_r_workspace_bytes(_cache(qas, page_size=12), b, 32, 64) == 0
+    # more query heads, more workspace
+    assert qas.qas_exact_top_r_workspace_bytes(c, b, 64, 64) > t64
