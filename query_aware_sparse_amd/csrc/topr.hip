@@ -34,7 +34,7 @@ constexpr int kTrWaves = kTrThreads / kWave;
 constexpr int kTrMaxPages = 4096;
 constexpr int kTrMaxR = 512;
 constexpr int kTrBuf = kTrMaxR + kTrThreads;     // kept + new candidates of a round
-constexpr int kTrMaxPilot = 64;                  // pages of the pilot
+constexpr int kTrMaxPilot = 64;                  // most pages of the pilot
 constexpr int kTrBail = 4;                       // pilot rounds worth of pages before the scan
 
 // 64-bit key, ascending = value descending then index ascending
@@ -494,7 +494,7 @@ __device__ __forceinline__ void merge_level(const uint64_t* in, uint64_t* out, i
   }
 }
 
-constexpr int kTrMaxChunks = kTrMaxPages / 2;   // page size >= 1, 512 tokens a chunk
+constexpr int kTrMaxChunks = kTrMaxPages / 2;   // page size <= 256: at least 2 pages a chunk
 constexpr int kTrMergeKeys = kTrMaxPages;       // keys in a batch of slots
 template <int DT, int D>
 __global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
