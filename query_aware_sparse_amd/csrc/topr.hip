@@ -244,6 +244,7 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   __shared__ TopkShared tsh;
   __shared__ __align__(16) uint64_t s_sel[kTrMaxPilot];
   __shared__ int s_phys[kTrMaxPilot];
+  __shared__ int s_selp[kTrMaxPilot];
   __shared__ __align__(16) uint64_t s_buf[2][kTrBuf];
   __shared__ float s_z[kTrThreads];
   __shared__ int s_cnt[kTrWaves];
@@ -267,9 +268,15 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   const int npil = min(P, cap > 0 ? cap : a.pilot_pages);
 
   // the pilot pages: the npil largest bounds, ordered by (bound desc, index asc)
+  // (each thread's page-table entries are loaded with its bounds, so the
+  // pilot pages' physical pages need no further round trip)
   TopkRow<PT, kTrThreads> t;
   t.j0 = tid * PT;
   t.n = P;
+  if (P > 0) {
+#pragma unroll
+    for (int k = 0; k < PT; ++k) t.pv[k] = a.page_indices[pbeg + min(t.j0 + k, P - 1)];
+  }
 #pragma unroll
   for (int k = 0; k < PT; ++k) t.v[k] = t.j0 + k < P ? key_value(wk[t.j0 + k]) : 0.f;
   t.select(npil, tsh);
@@ -278,18 +285,22 @@ __global__ __launch_bounds__(kTrThreads) void topr_plan_kernel(ToprArgs a) {
   float out_max = -INFINITY;                          // largest bound outside the pilot
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
-    if (t.selected(k)) s_sel[pos++] = desc_key(t.v[k], (uint32_t)(t.j0 + k));
-    else if (t.valid(k)) out_max = fmaxf(out_max, t.v[k]);
+    if (t.selected(k)) {
+      s_sel[pos] = desc_key(t.v[k], (uint32_t)(t.j0 + k));
+      s_selp[pos++] = t.pv[k];
+    } else if (t.valid(k)) {
+      out_max = fmaxf(out_max, t.v[k]);
+    }
   }
   float lo_dummy = FLT_MAX;
   tk::block_minmax<kTrWaves>(lo_dummy, out_max, tsh.mm);   // barrier: s_sel complete
   {
-    // rank the pilot pages and fetch their physical pages once
+    // rank the pilot pages
     uint64_t x = 0;
     int rank = 0, phys = 0;
     if (tid < npil) {
       x = s_sel[tid];
-      phys = a.page_indices[pbeg + (int)(uint32_t)x];
+      phys = s_selp[tid];
       rank = count_below(s_sel, 0, npil, x);
     }
     __syncthreads();
