@@ -67,6 +67,35 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
+// Page bitmaps of the window's queries in LDS (rows of RS words, zeroed
+// here): every thread issues BL set-entry loads before its LDS atomics, so
+// the loads of a batch are in flight together.  Ends with a barrier.
+template <int NT, int RS>
+__device__ __forceinline__ void build_bitmaps(const RegroupArgs& a, const WindowInfo& win, int h,
+                                              int n_pages, uint32_t* bm, int rows) {
+  constexpr int BL = 8;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < rows * RS; i += NT) bm[i] = 0u;
+  __syncthreads();
+  const int entries = win.nq * a.kq;                 // >= 1
+  for (int e0 = 0; e0 < entries; e0 += NT * BL) {
+    int pg[BL];
+#pragma unroll
+    for (int b = 0; b < BL; ++b) {
+      const int e = min(e0 + b * NT + tid, entries - 1);
+      const int i = e / a.kq;
+      pg[b] = a.sets[((size_t)(win.q0 + i) * a.H_kv + h) * a.kq + (e - i * a.kq)];
+    }
+#pragma unroll
+    for (int b = 0; b < BL; ++b) {
+      const int e = e0 + b * NT + tid;
+      const int p = pg[b];
+      if (e < entries && p >= 0 && p < n_pages) atomicOr(&bm[(e / a.kq) * RS + (p >> 5)], 1u << (p & 31));
+    }
+  }
+  __syncthreads();
+}
+
 // WQ = queries per window slot range (64 or 128): 4 * WQ threads
 template <int WQ>
 __global__ __launch_bounds__(kRgLanesPerQuery * WQ) void regroup_kernel(RegroupArgs a) {
@@ -88,14 +117,7 @@ __global__ __launch_bounds__(kRgLanesPerQuery * WQ) void regroup_kernel(RegroupA
   }
 
   // ---- page bitmaps of the window's queries --------------------------------
-  for (int i = tid; i < WQ * kRgWords; i += NT) (&bm[0][0])[i] = 0u;
-  __syncthreads();
-  for (int e = tid; e < win.nq * a.kq; e += NT) {
-    const int i = e / a.kq;
-    const int p = a.sets[((size_t)(win.q0 + i) * a.H_kv + h) * a.kq + (e - i * a.kq)];
-    if (p >= 0 && p < n_pages) atomicOr(&bm[i][p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
+  build_bitmaps<NT, kRgWords>(a, win, h, n_pages, &bm[0][0], WQ);
   const int q = tid / kRgLanesPerQuery;       // this lane's query
   const int k = tid % kRgLanesPerQuery;       // and its word range
   uint32_t b[kRgWordsPerLane], U[kRgWordsPerLane];
