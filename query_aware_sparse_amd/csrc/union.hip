@@ -112,16 +112,17 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   const int words = (n_pages + 31) / 32;
   for (int i = tid; i < kUMaxGroup * words; i += kUThreads) sh.bm[i / words][i % words] = 0;
   // the original query of every slot (an execution order from the regroup,
-  // else the identity) and its causal limit (the union preparation alone has
-  // none)
+  // else the identity)
+  int my_qid = 0;
   if (tid < kUMaxGroup) {
     const int slot = gr.q0 + (tid < gr.nq ? tid : 0);
-    const int qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
-    sh.qid[tid] = qid;
-    sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[qid] : -1;
+    my_qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
+    sh.qid[tid] = my_qid;
   }
   __syncthreads();
-  // entries <= kUMaxUnion: every set entry's load is issued before any is used
+  // entries <= kUMaxUnion: every set entry's load is issued before any is
+  // used, and the slots' causal limits (the union preparation alone has
+  // none) are loaded beside them
   constexpr int EPT = kUMaxUnion / kUThreads;
   const int entries = gr.nq * a.kq;
   int ids[EPT];
@@ -131,6 +132,7 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
     const int i = e / a.kq;
     ids[k] = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
   }
+  if (tid < kUMaxGroup) sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[my_qid] : -1;
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = tid + k * kUThreads;
@@ -138,27 +140,39 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
     if (e < entries && id >= 0 && id < n_pages) atomicOr(&sh.bm[e / a.kq][id >> 5], 1u << (id & 31));
   }
   __syncthreads();
-  // each thread owns a contiguous run of bitmap words
-  const int per = (words + kUThreads - 1) / kUThreads;
-  const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+  // each thread owns up to WPT consecutive bitmap words, whose per-query
+  // words it reads once into registers (all in flight together)
+  constexpr int WPT = kUMaxWords / kUThreads;
+  const int per = (words + kUThreads - 1) / kUThreads;   // <= WPT
+  const int w0 = tid * per;
+  uint32_t qw[WPT][kUMaxGroup];
   int mine = 0;
-  for (int w = w0; w < w1; ++w) {
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = w0 + k;
+    const bool in = k < per && w < words;
+#pragma unroll
+    for (int i = 0; i < kUMaxGroup; ++i) qw[k][i] = (in && i < gr.nq) ? sh.bm[i][in ? w : 0] : 0u;
     uint32_t u = 0;
-    for (int i = 0; i < gr.nq; ++i) u |= sh.bm[i][w];
+#pragma unroll
+    for (int i = 0; i < kUMaxGroup; ++i) u |= qw[k][i];
     mine += __popc(u);
   }
   int total;
   int pos = block_excl(mine, sh.wave_tot, &total);
-  for (int w = w0; w < w1; ++w) {
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = w0 + k;
     uint32_t u = 0;
-    for (int i = 0; i < gr.nq; ++i) u |= sh.bm[i][w];
+#pragma unroll
+    for (int i = 0; i < kUMaxGroup; ++i) u |= qw[k][i];
     while (u) {
       const int b = __builtin_ctz(u);
       u &= u - 1;
-      const int id = w * 32 + b;
       unsigned char m = 0;
-      for (int i = 0; i < gr.nq; ++i) m |= ((sh.bm[i][w] >> b) & 1u) << i;
-      sh.ulist[pos] = id;
+#pragma unroll
+      for (int i = 0; i < kUMaxGroup; ++i) m |= ((qw[k][i] >> b) & 1u) << i;
+      sh.ulist[pos] = w * 32 + b;
       sh.umask[pos] = m;
       ++pos;
     }
@@ -205,31 +219,33 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   const int P_r = a.page_indptr[gr.r + 1] - pbeg;
   const int n_pages = L > 0 ? min(min((L + S - 1) / S, P_r), kUMaxWords * 32) : 0;
 
-  const int U = build_union(sh, a, gr, h, n_pages, pbeg);
-
   // ---- per-lane row: row = query * G + head (S^T / O^T column = lane % 32)
   const int row = lane % 32, hf = lane / 32;
   const int qi = row / G, hq = row % G;
   const bool row_ok = qi < gr.nq;
-  const int cq = row_ok ? sh.cpos[qi] : -1;
-  // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row
-  // (16-byte loads issued together; a row past the group reads the first
-  // query's row and is zeroed)
-  float qf[64];
+  // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row.
+  // Its 16-byte loads are issued now, so they land during the union build (a
+  // row past the group reads the first query's row and is zeroed).
+  uint4 qraw[8];
   {
-    const size_t qbase = ((size_t)sh.qid[row_ok ? qi : 0] * a.H_q + h * G + hq) * kUD;
-    const char* qp = reinterpret_cast<const char*>(a.q) + qbase * 2;
-    uint4 raw[8];
+    const int slot = gr.q0 + (row_ok ? qi : 0);
+    const int qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) raw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) unpack16<kBF16>(raw[i], qf + 8 * i);
-    if (!row_ok)
-#pragma unroll
-      for (int e = 0; e < 64; ++e) qf[e] = 0.f;
+      for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
   }
+
+  const int U = build_union(sh, a, gr, h, n_pages, pbeg);
+  const int cq = row_ok ? sh.cpos[qi] : -1;
+  float qf[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack16<kBF16>(qraw[i], qf + 8 * i);
+  if (!row_ok)
+#pragma unroll
+    for (int e = 0; e < 64; ++e) qf[e] = 0.f;
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(qf[e]));
