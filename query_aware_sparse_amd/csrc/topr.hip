@@ -467,17 +467,19 @@ __global__ __launch_bounds__(kTrThreads) void topr_scan_kernel(ToprArgs a) {
 //    LDS read each per step.  Lists beyond one batch of slots are merged a
 //    batch at a time, the running result in the first slot.
 // One level of the merge tree: slots 2s and 2s + 1 of `in` (W = 2^lw keys
-// each, n slots) into slot s of `out`, KK keys per thread (keys e = tid +
-// k * kTrThreads, k < KK, cover the n * W keys in use).
+// each, n slots) into slot s of `out`, KK keys per thread: keys e = e0 +
+// threadIdx.x + k * kTrThreads, k < KK (calls with e0 = 0, KK * kTrThreads, ...
+// cover the n * W keys in use; they read only `in` and write only `out`).
 template <int KK>
-__device__ __forceinline__ void merge_level(const uint64_t* in, uint64_t* out, int n, int lw) {
-  const int W = 1 << lw, tid = threadIdx.x;
+__device__ __forceinline__ void merge_level(const uint64_t* in, uint64_t* out, int n, int lw,
+                                            int e0 = 0) {
+  const int W = 1 << lw, eb = e0 + threadIdx.x;
   uint64_t x[KK];
   int base[KK], pos[KK];
   bool pair[KK];
 #pragma unroll
   for (int k = 0; k < KK; ++k) {
-    const int e = tid + k * kTrThreads;
+    const int e = eb + k * kTrThreads;
     const int slot = e >> lw;
     const bool live = e < n * W;
     pair[k] = live && (slot ^ 1) < n;
@@ -498,7 +500,7 @@ __device__ __forceinline__ void merge_level(const uint64_t* in, uint64_t* out, i
 #pragma unroll
   for (int k = 0; k < KK; ++k) {
     pos[k] += y[k] < x[k] ? 1 : 0;
-    const int e = tid + k * kTrThreads;
+    const int e = eb + k * kTrThreads;
     const int slot = e >> lw, i = e & (W - 1);
     const int at = pair[k] ? i + pos[k] : i;           // an unpaired last slot passes through
     if (e < n * W && at < W) out[((slot >> 1) << lw) + at] = x[k];
@@ -516,18 +518,52 @@ __global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
   __shared__ int s_scan[kTrWaves];
   const int qh = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const size_t orow = (size_t)r * a.H_q + qh;
-  const int* st = a.ws_state + orow * 4;
-  if (st[0] != 0) return;
   const int R = a.R, S = a.S, cp = kTrThreads / S;
-  const int nch = (st[2] + cp - 1) / cp;               // chunks the scan used
+  const int lw = 32 - __clz(R - 1);                    // W = 2^lw >= R
+  const int W = 1 << lw;
+  const int NS = kTrMergeKeys / W;                     // slots of a batch
+  // The global loads of the first two batches go out at entry, before the
+  // row state is known: the state, the chunk counts and the keys of both
+  // batches (batch 1: slot s holds list s, the pilot's and then chunk s - 1's;
+  // batch 2: slot s >= 1 holds list NS + s - 1, slot 0 the running result),
+  // none of whose addresses depends on the counts.  Addresses outside the
+  // rows read the pilot list's first entry; validity is applied once state
+  // and counts have landed.
+  const int* st = a.ws_state + orow * 4;
+  const int st0 = st[0], st1 = st[1], st2 = st[2], pilot = st[3];
   const int* cnts = a.ws_counts + orow * a.scan_chunks;
-  const int pilot = st[3];
-  // list offsets: CPT consecutive counts per thread, one block scan
-  int cn[CPT], mine = 0;
+  int cn[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     const int i = tid * CPT + k;
-    cn[k] = i < nch ? cnts[i] : 0;
+    cn[k] = cnts[i < a.scan_chunks ? i : 0];
+  }
+  const uint64_t* pil = a.ws_pilot + orow * R;
+  uint64_t v[KPT], v2[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int e = tid + k * kTrThreads;
+    const int slot = e >> lw, i = e & (W - 1);
+    const uint64_t* src = pil;
+    const uint64_t* src2 = pil;
+    if (i < R) {
+      if (slot == 0) src = pil + i;
+      else if (slot - 1 < a.scan_chunks)
+        src = a.ws_chunks + (orow * a.scan_chunks + slot - 1) * R + i;
+      const int c2 = NS + slot - 2;                    // chunk of list NS + slot - 1
+      if (slot >= 1 && c2 < a.scan_chunks) src2 = a.ws_chunks + (orow * a.scan_chunks + c2) * R + i;
+    }
+    v[k] = *src;
+    v2[k] = *src2;
+  }
+  // a row the plan finished has nothing to merge (no lists, no result)
+  const bool live_row = st0 == 0;
+  const int nch = live_row ? (st2 + cp - 1) / cp : 0;  // chunks the scan used
+  // list offsets: CPT consecutive counts per thread, one block scan
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    cn[k] = tid * CPT + k < nch ? cn[k] : 0;
     mine += cn[k];
   }
   int total;
@@ -541,37 +577,34 @@ __global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
   if (tid == 0) s_off[nch] = total;
   __syncthreads();
 
-  const int lw = 32 - __clz(R - 1);                    // W = 2^lw >= R
-  const int W = 1 << lw;
-  const int NS = kTrMergeKeys / W;                     // slots of a batch
   const int nl = 1 + nch;                              // the pilot's list, then the chunks'
   int cur = 0, done = 0, first = 0;
   while (done < nl) {
     const int fresh = min(NS - first, nl - done);      // lists loaded in this batch
     int n = first + fresh;                             // slots in use
-    {
-      // every load issued before any LDS store (a key outside the lists
-      // reads the pilot list's first entry and is dropped)
-      const uint64_t* pil = a.ws_pilot + orow * R;
-      uint64_t v[KPT];
-      bool ok[KPT];
+    if (done == NS) {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) v[k] = v2[k];
+    } else if (done > 0) {
+      // batches after the second: slot s >= 1 holds list done + s - 1;
+      // every load issued before any LDS store
 #pragma unroll
       for (int k = 0; k < KPT; ++k) {
         const int e = tid + k * kTrThreads;
         const int slot = e >> lw, i = e & (W - 1);
-        const bool act = slot >= first && slot < n;
-        const int list = act ? done + slot - first : 0;
-        const int cnt = list == 0 ? pilot : s_off[list] - s_off[list - 1];
-        ok[k] = act && i < cnt;
-        const uint64_t* src =
-            !ok[k] ? pil : list == 0 ? pil + i : a.ws_chunks + (orow * a.scan_chunks + list - 1) * R + i;
-        v[k] = *src;
+        const int list = done + slot - first;
+        const bool act = slot >= first && slot < n && i < R;
+        v[k] = *(act ? a.ws_chunks + (orow * a.scan_chunks + list - 1) * R + i : pil);
       }
+    }
 #pragma unroll
-      for (int k = 0; k < KPT; ++k) {
-        const int e = tid + k * kTrThreads;
-        const int slot = e >> lw;
-        if (slot >= first && slot < n) s_m[cur][e] = ok[k] ? v[k] : ~0ull;
+    for (int k = 0; k < KPT; ++k) {
+      const int e = tid + k * kTrThreads;
+      const int slot = e >> lw, i = e & (W - 1);
+      if (slot >= first && slot < n) {
+        const int list = done + slot - first;
+        const int cnt = list == 0 ? pilot : s_off[list] - s_off[list - 1];
+        s_m[cur][e] = i < cnt ? v[k] : ~0ull;
       }
     }
     __syncthreads();
@@ -589,7 +622,7 @@ __global__ __launch_bounds__(kTrThreads) void topr_merge_kernel(ToprArgs a) {
     done += fresh;
     first = 1;
   }
-  write_result(a, orow, s_m[cur], min(R, pilot + total), st[1] + st[2]);
+  if (live_row) write_result(a, orow, s_m[cur], min(R, pilot + total), st1 + st2);
 }
 
 template <int DT, int D>
