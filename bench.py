@@ -457,8 +457,8 @@ def main():
                     help="skip the cold-cache protocol (counter passes of the decode-layer call)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested, but this build measures the "
-              "single-GPU path only (one GPU per box); run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} requested, but the path runs on one GPU "
+              "(no multi-GPU mode); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         return copy_calibration()

@@ -58,7 +58,7 @@ typedef enum qas_status {
   QAS_ERR_NULL = 1,        /* a required pointer is NULL                      */
   QAS_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree        */
   QAS_ERR_DTYPE = 3,       /* dtype not accepted for this operand             */
-  QAS_ERR_UNSUPPORTED = 4, /* valid request outside this build (e.g. head_dim) */
+  QAS_ERR_UNSUPPORTED = 4, /* valid request the library does not implement (e.g. head_dim) */
   QAS_ERR_WORKSPACE = 5,   /* workspace NULL, not 16-byte aligned, too small  */
   QAS_ERR_HIP = 6          /* a HIP runtime call or launch failed             */
 } qas_status;
