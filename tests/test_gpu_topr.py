@@ -66,6 +66,9 @@ CASES = {
     "tiny-f32": (lambda: tiny_single_head(L=301, K=4), [1, 5, 40, 400]),
     "gqa-bf16": (lambda: batched_gqa_append(B=3, L_min=200, L_max=3000, H_q=8, H_kv=2, steps=0), [16]),
     "llama-f16-5k": (lambda: llama2_7b_layer(L=5000, H=4, K=40), [8, 512]),
+    # R = 512: a merge batch holds 8 lists, and ~24 lists (the pilot's and
+    # ~23 scan chunks') take four batches
+    "llama-f16-12k": (lambda: llama2_7b_layer(L=12000, H=2, K=40), [512]),
 }
 
 
