@@ -157,3 +157,42 @@ def test_next_row_workspace_sizes(qas):
     assert qas.qas_exact_top_r_workspace_bytes(_cache(qas, page_size=12), b, 32, 64) == 0
     # more query heads, more workspace
     assert qas.qas_exact_top_r_workspace_bytes(c, b, 64, 64) > t64
+
+
+def _prototypes():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    out = {}
+    for ret, name, args in re.findall(
+            r"([A-Za-z_][\w\s\*]*?)\b(qas_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        params = [] if args.strip() in ("", "void") else [p.strip() for p in args.split(",")]
+        out[name] = (ret.strip(), params)
+    return out
+
+
+def _ctype_of(decl):
+    """The ctypes type a C parameter or return type must be marshalled as."""
+    if "*" in decl or decl.split()[0] == "hipStream_t":
+        return "ptr"
+    words = decl.replace("const", "").split()
+    base = words[0]
+    return {"int32_t": "i32", "int": "i32", "qas_status": "i32", "float": "f32",
+            "size_t": "size"}[base]
+
+
+def test_binding_signatures_match_the_header(qas):
+    """Every function the header declares has a ctypes signature in the binding
+    with the same number of parameters and matching widths (a pointer passed
+    without one would be truncated to a C int)."""
+    import ctypes
+    kinds = {ctypes.c_void_p: "ptr", ctypes.c_char_p: "ptr", ctypes.c_int32: "i32",
+             ctypes.c_float: "f32", ctypes.c_size_t: "size"}
+    protos = _prototypes()
+    assert set(protos) == set(qas._SIGNATURES), set(protos) ^ set(qas._SIGNATURES)
+    for name, (ret, params) in protos.items():
+        res, args = qas._SIGNATURES[name]
+        assert len(args) == len(params), (name, len(args), len(params))
+        for i, (p, a) in enumerate(zip(params, args)):
+            assert kinds[a] == _ctype_of(p), (name, i, p, a)
+        assert kinds[res] == _ctype_of(ret), (name, ret, res)
