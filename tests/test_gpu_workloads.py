@@ -178,6 +178,31 @@ def test_batched_gqa_with_append(qas):
         assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
 
 
+@pytest.mark.parametrize("S", [1, 2, 8, 64, 128, 256])
+def test_page_sizes(qas, S):
+    """Page sizes beyond the workloads' 4, 16 and 32, up to the largest the
+    library takes: decode-layer calls with one append each (S = 1: every
+    token opens a page; S = 256: 64 KiB of K per page and head), checked
+    against the oracle, and every summary after the last append."""
+    case = batched_gqa_append(seed=60 + S, B=2, L_min=1100, L_max=2100, H_q=4, H_kv=2, d=128,
+                              S=S, K=max(2, 256 // S), steps=3)
+    say(f"[e2e] page size {S}: lengths={case.seq_lens.tolist()} K={case.K}")
+    lay = Layer(qas, case)
+    decoded = {r: oracle.decoded_kv(case, r) for r in range(case.B)}
+    reqs = list(range(case.B))
+    for step in range(-1, case.steps):
+        out, lse, sel, db = lay.call(step=step, append=step >= 0)
+        ref = oracle.run_decode(case, step=step, requests=reqs, decoded=decoded)
+        compare(case, out, lse, sel, ref, reqs, lay.scores(db, step) if step == -1 else None,
+                db, step=step)
+    summ = lay.pc.summary.float().cpu().numpy()
+    final = case.lengths(case.steps - 1)
+    for r in reqs:
+        m, M = oracle.quest.page_summaries(decoded[r][0], int(final[r]), case.S)
+        phys = case.pages[r][:len(m)]
+        assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
+
+
 def test_stress_long_context(qas):
     """16 requests at 131072 tokens, 32/8 heads, S=32, K=41, Student-t keys,
     fp16: decode-layer call checked on a seeded sample of requests; then
