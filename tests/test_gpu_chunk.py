@@ -105,6 +105,19 @@ def test_chunk_attention_page_size_32(qas):
     _check(case, got, lse, list(range(case.N)))
 
 
+@pytest.mark.parametrize("g,group,S", [(1, 8, 64), (2, 8, 32), (8, 4, 64), (4, 5, 32)])
+def test_chunk_attention_group_shapes(qas, g, group, S):
+    """Query heads per KV head 1, 2 and 8 (tiles of 8, 16 and 32 rows) and
+    groups of 5 queries, each with a ragged last group: every query against
+    the oracle."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    case = multiquery_chunk(seed=50 + g, L=5000, S=S, N=23, H_q=2 * g, H_kv=2, kq=32, keep=22,
+                            group=group)
+    say(f"[chunk] g={g} group={group} S={S}")
+    got, lse = _run(qas, ChunkBatch([case]))
+    _check(case, got, lse, list(range(case.N)))
+
+
 def test_chunk_attention_two_requests(qas):
     """Two requests in one call share the fp8 pool and scales; groups never
     cross the request boundary."""
