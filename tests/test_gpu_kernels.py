@@ -97,8 +97,10 @@ def _topk_scores(kind, total, rng):
         wide = (rng.standard_normal(total) * 5000).astype(np.float32)
         return np.where(rng.random(total) < 0.85, c, wide).astype(np.float32)
     if kind == "huge":
-        # a range beyond fp32 (and -inf entries): binning by order keys
-        x = (rng.standard_normal(total) * 1e38).astype(np.float32)
+        # a range beyond fp32 (and -inf entries): binning by order keys; the
+        # samples past the fp32 range become +-inf on purpose
+        with np.errstate(over="ignore"):
+            x = (rng.standard_normal(total) * 1e38).astype(np.float32)
         pick = rng.random(total)
         x[pick < 0.05] = -np.inf
         x[(pick >= 0.05) & (pick < 0.1)] = np.float32(3.4e38)
