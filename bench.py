@@ -66,15 +66,41 @@ PMC_TRAFFIC = {
 }
 
 
-def decode_sources_sha256():
+# Counters of the union attention kernel (the chunk line), from passes of
+# `bench.py --workload chunk --no-cpu-baseline --steps 16 --warmup 4`: medians
+# over the dispatches with the chunk's own sets (the phase the chunk line
+# times), the same scaling; valid only for CHUNK_SOURCES.
+CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
+CHUNK_PMC_TRAFFIC = {
+    "sources_sha256": "61dd3e0f23ea912b3fc18a060b7fa1717750c75b58f79554bcaf72631b6e795c",
+    "fetch_kib": 145403.2,
+    "write_kib": 4224.2,
+}
+
+
+def sources_sha256(names):
     import hashlib
     d = os.path.join(ROOT, "query_aware_sparse_amd", "csrc")
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in names:
         h.update(name.encode())
         with open(os.path.join(d, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def decode_sources_sha256():
+    return sources_sha256(DECODE_SOURCES)
+
+
+def chunk_traffic_bytes():
+    """HBM bytes per chunk call of the union kernel from the recorded
+    counters, or None if its sources changed since they were taken."""
+    t = CHUNK_PMC_TRAFFIC
+    if t["sources_sha256"] != sources_sha256(CHUNK_SOURCES):
+        return None
+    kib = t["fetch_kib"] * PMC_TRAFFIC["fetch_factor"] + t["write_kib"] * PMC_TRAFFIC["write_factor"]
+    return int(round(kib * 1024))
 
 
 def pmc_traffic_bytes(fp8=False):
@@ -319,7 +345,7 @@ def bench_chunk(args):
                                    "online_pi_us": round(shuf_online_us, 3)}}},
         "roofline": {"bound": "mfma", "achieved": round(exe, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(exe / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "union_attn_kernel",
+                     "traffic": chunk_traffic_bytes(), "kernel": "union_attn_kernel",
                      "us_per_launch": round(call_us, 3),
                      "useful_tflops": round(use, 2)},
     }
