@@ -20,14 +20,15 @@ def say(*a):
 
 
 def score_denominator(q_heads, m, M, g):
-    """max over the group of sum_d |q_d| * max(|m_d|, |M_d|): a bound on
-    sum_d |u_d| used so near-zero bounds get an absolute floor.  [H_kv][P]"""
+    """max over the group's query heads of sum_d |u_d|, u_d = max(q_d m_d,
+    q_d M_d): the scale of the fp32 rounding error of a bound, so near-zero
+    bounds get an absolute floor.  [H_kv][P]"""
     P, H_kv, _ = m.shape
-    mag = np.maximum(np.abs(m), np.abs(M))
     out = np.zeros((H_kv, P))
     for h in range(H_kv):
         for i in range(h * g, (h + 1) * g):
-            out[h] = np.maximum(out[h], mag[:, h, :] @ np.abs(q_heads[i]))
+            u = np.maximum(q_heads[i][None, :] * m[:, h, :], q_heads[i][None, :] * M[:, h, :])
+            out[h] = np.maximum(out[h], np.abs(u).sum(axis=1))
     return out
 
 

@@ -318,5 +318,9 @@ def test_longest_row(qas):
     torch.cuda.synchronize()
     ref = oracle.run_decode(case)[0]
     from tests.gpu_util import check_selection
-    if check_selection(sel.cpu().numpy()[0, 0], ref["U"][0], case.K):
-        assert_attn_close(out_to_numpy(out)[0], ref["out"], "f32", "long row")
+    got_sel = sel.cpu().numpy()
+    if not check_selection(got_sel[0, 0], ref["U"][0], case.K):
+        # near tie: the oracle's attention over the GPU's own set
+        ref = oracle.run_decode(case, page_ids=got_sel.astype(np.int64))[0]
+    assert_attn_close(out_to_numpy(out)[0], ref["out"], "f32", "long row")
+    np.testing.assert_allclose(lse.cpu().numpy()[0], ref["lse"], rtol=1e-5, atol=1e-4)

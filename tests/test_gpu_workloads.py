@@ -64,8 +64,12 @@ class Layer:
 
 
 def compare(case, got_out, got_lse, got_sel, ref, requests, got_scores=None, db=None,
-            step=-1, min_exact=0.75):
-    """Compare a decode-layer call with oracle results for `requests`."""
+            step=-1, decoded=None):
+    """Compare a decode-layer call with oracle results for `requests`: page
+    bounds (if given), page sets (exact outside near ties, valid inside
+    them), and the output and lse of every row.  A row whose set differs
+    inside the near-tie band is compared with the oracle's attention over
+    the GPU's own set, so no row goes unchecked."""
     rows = exact = 0
     q_all = oracle.decode(case.q[step + 1], case.q_dtype)
     for r, res in zip(requests, ref):
@@ -76,18 +80,21 @@ def compare(case, got_out, got_lse, got_sel, ref, requests, got_scores=None, db=
             for h in range(case.H_kv):
                 assert_scores_close(got_scores[base + h * P: base + (h + 1) * P],
                                     res["U"][h], denom[h], f"{case.name} r={r} h={h}")
+        same = [check_selection(got_sel[r, h], res["U"][h], case.K) for h in range(case.H_kv)]
+        rows += case.H_kv
+        exact += sum(same)
+        own = res
+        if not all(same):
+            own = oracle.run_decode(case, step=step, page_ids=got_sel.astype(np.int64),
+                                    requests=[r], decoded=decoded)[0]
         for h in range(case.H_kv):
-            rows += 1
-            same = check_selection(got_sel[r, h], res["U"][h], case.K)
-            if same:
-                exact += 1
-                heads = slice(h * case.g, (h + 1) * case.g)
-                assert_attn_close(got_out[r, heads], res["out"][heads], case.kv_dtype,
-                                  f"{case.name} r={r} h={h}")
-                np.testing.assert_allclose(got_lse[r, heads], res["lse"][heads],
-                                           rtol=1e-5, atol=1e-4)
-    say(f"  {case.name} step {step}: {exact}/{rows} rows with the oracle's exact set")
-    assert exact >= min_exact * rows
+            heads = slice(h * case.g, (h + 1) * case.g)
+            what = f"{case.name} r={r} h={h}" + ("" if same[h] else " (GPU's near-tie set)")
+            assert_attn_close(got_out[r, heads], own["out"][heads], case.kv_dtype, what)
+            np.testing.assert_allclose(got_lse[r, heads], own["lse"][heads],
+                                       rtol=1e-5, atol=1e-4, err_msg=what)
+    say(f"  {case.name} step {step}: {exact}/{rows} rows with the oracle's exact set, "
+        f"{rows - exact} near-tie rows checked on the GPU's set")
     return exact, rows
 
 
@@ -99,7 +106,7 @@ def test_tiny_cases(qas, make):
     lay = Layer(qas, case)
     out, lse, sel, db = lay.call()
     ref = oracle.run_decode(case)
-    compare(case, out, lse, sel, ref, range(case.B), lay.scores(db), db, min_exact=1.0)
+    compare(case, out, lse, sel, ref, range(case.B), lay.scores(db), db)
 
 
 def test_figure2_two_steps(qas):
@@ -127,8 +134,8 @@ def test_llama2_7b_layer_full(qas):
     out, lse, sel, db = lay.call()
     ref = oracle.run_decode(case)
     compare(case, out, lse, sel, ref, [0], lay.scores(db), db)
-    # repeatability: identical bits over repeated calls
-    for _ in range(3):
+    # repeatability: identical bits over 50 repeated calls
+    for _ in range(50):
         o2, l2, s2, _ = lay.call()
         assert np.array_equal(o2, out) and np.array_equal(s2, sel)
         assert np.array_equal(l2, lse)
@@ -162,14 +169,14 @@ def test_batched_gqa_with_append(qas):
     say(f"[e2e] {case.name} lengths={case.seq_lens.tolist()}")
     lay = Layer(qas, case)
     decoded = {r: oracle.decoded_kv(case, r) for r in range(case.B)}
-    check_steps = {-1, 0, 7, 15}
+    all_steps = {-1, 0, 7, 15}
     for step in range(-1, case.steps):
         out, lse, sel, db = lay.call(step=step, append=step >= 0)
-        if step in check_steps:
-            reqs = list(range(case.B)) if step == -1 else [0, 3, 6]
-            ref = oracle.run_decode(case, step=step, requests=reqs, decoded=decoded)
-            compare(case, out, lse, sel, ref, reqs,
-                    lay.scores(db, step) if step == -1 else None, db, step=step)
+        # every request at four steps; requests 0 and 5 at every step
+        reqs = list(range(case.B)) if step in all_steps else [0, 5]
+        ref = oracle.run_decode(case, step=step, requests=reqs, decoded=decoded)
+        compare(case, out, lse, sel, ref, reqs, lay.scores(db, step) if step == -1 else None,
+                db, step=step, decoded=decoded)
     summ = lay.pc.summary.float().cpu().numpy()
     final = case.lengths(case.steps - 1)
     for r in range(case.B):
@@ -194,7 +201,7 @@ def test_page_sizes(qas, S):
         out, lse, sel, db = lay.call(step=step, append=step >= 0)
         ref = oracle.run_decode(case, step=step, requests=reqs, decoded=decoded)
         compare(case, out, lse, sel, ref, reqs, lay.scores(db, step) if step == -1 else None,
-                db, step=step)
+                db, step=step, decoded=decoded)
     summ = lay.pc.summary.float().cpu().numpy()
     final = case.lengths(case.steps - 1)
     for r in reqs:
@@ -212,10 +219,10 @@ def test_stress_long_context(qas):
     say(f"[e2e] {case.name} K={case.K}")
     lay = Layer(qas, case)
     out, lse, sel, db = lay.call()
-    reqs = sorted(np.random.default_rng(55).choice(case.B, size=4, replace=False).tolist())
+    reqs = sorted(np.random.default_rng(55).choice(case.B, size=8, replace=False).tolist())
     decoded = {r: oracle.decoded_kv(case, r) for r in reqs}
     ref = oracle.run_decode(case, requests=reqs, decoded=decoded)
-    compare(case, out, lse, sel, ref, reqs, lay.scores(db), db)
+    compare(case, out, lse, sel, ref, reqs, lay.scores(db), db, decoded=decoded)
     # corrupted lists: oracle top-K on sampled requests, seeded random pages elsewhere
     P = case.seq_lens[0] // case.S
     rng = np.random.default_rng(56)

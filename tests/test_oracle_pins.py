@@ -497,6 +497,156 @@ def test_chunk_attention_per_query_matches_decode_definition():
     np.testing.assert_array_equal(out[0], res["out"])
 
 
+# ------------------------------------- chunk / GQA attention against SDPA ----
+#
+# [PageWeaver] eq. (1)-(2): query n, head i attends over the tokens t of KV
+# head i // g whose page floor(t/S) is in its own set, with t < L_n and
+# t <= c_n.  The pins below build that support as a dense boolean mask from
+# per-page membership (np.repeat over the S tokens of a page, not the
+# oracle's list-of-tokens route) and hand it to torch's float64
+# scaled_dot_product_attention with enable_gqa=True, whose head grouping is
+# the library's own (consecutive query heads share a KV head).
+
+
+def _membership_mask(sets, L, c, S, T, g):
+    """Dense mask [N][H_q][T]: page membership expanded over its S tokens,
+    then the length and causal limits; per KV head, repeated g times over
+    the query heads that read it."""
+    N, H_kv = len(sets), len(sets[0])
+    mask = np.zeros((N, H_kv, T), dtype=bool)
+    n_pages = -(-T // S)
+    t = np.arange(T)
+    for n in range(N):
+        for h in range(H_kv):
+            on = np.zeros(n_pages, dtype=bool)
+            for p in sets[n][h]:
+                if 0 <= p < n_pages and p * S < L[n]:
+                    on[p] = True
+            mask[n, h] = np.repeat(on, S)[:T] & (t < L[n]) & (t <= c[n])
+    return np.repeat(mask, g, axis=1)
+
+
+def _sdpa_masked(q, keys, values, mask, scale):
+    """torch SDPA (float64, CPU, enable_gqa) of q [N][H_q][d] over keys /
+    values [T][H_kv][d] with mask [N][H_q][T]; rows with an empty mask come
+    back as NaN and are the caller's to skip.  Also the log-sum-exp of the
+    masked logits (KV heads expanded by repeat_interleave)."""
+    qt = torch.tensor(q).permute(1, 0, 2)[None]            # [1][H_q][N][d]
+    kt = torch.tensor(keys).permute(1, 0, 2)[None]         # [1][H_kv][T][d]
+    vt = torch.tensor(values).permute(1, 0, 2)[None]
+    mt = torch.tensor(mask).permute(1, 0, 2)[None]         # [1][H_q][N][T]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt,
+                                                         scale=scale, enable_gqa=True)
+    g = q.shape[1] // keys.shape[1]
+    z = (qt @ torch.repeat_interleave(kt, g, dim=1).transpose(-1, -2)) * scale
+    z = z.masked_fill(~mt, -math.inf)
+    return o[0].permute(1, 0, 2).numpy(), torch.logsumexp(z, -1)[0].T.numpy()
+
+
+def _chunk_case(seed, g, H_kv=2, d=8, S=4, T=40):
+    """Queries with their own lengths and causal limits inside pages, sets
+    with duplicates, invalid IDs and pages past the limit, one empty set."""
+    rng = _rng(seed)
+    keys = rng.normal(size=(T, H_kv, d)) * np.arange(1, H_kv + 1)[None, :, None]
+    values = rng.normal(size=(T, H_kv, d)) + np.arange(H_kv)[None, :, None]
+    L = [40, 37, 40, 33, 29, 40]
+    c = [39, 30, 21, 13, 28, 5]          # limits inside pages (S = 4)
+    N = len(L)
+    q = rng.normal(size=(N, H_kv * g, d))
+    P = -(-T // S)
+    sets = []
+    for n in range(N):
+        row = []
+        for h in range(H_kv):
+            ids = list(rng.choice(P, size=5, replace=False))
+            ids += [ids[0], -1, P, 2 ** 31 - 1]       # duplicate and invalid IDs
+            ids.append(c[n] // S)                     # the page the limit falls in
+            row.append(ids)
+        sets.append(row)
+    sets[4][1] = [-3, P + 1]                          # empty support for KV head 1
+    return q, keys, values, sets, L, c, S
+
+
+def _pin_chunk_against_sdpa(qmod, g):
+    q, keys, values, sets, L, c, S = _chunk_case(40 + g, g)
+    scale = 1 / math.sqrt(q.shape[2])
+    out, lse = qmod.chunk_attention(q, keys, values, sets, L, c, S, g, scale=scale)
+    mask = _membership_mask(sets, L, c, S, keys.shape[0], g)
+    o_ref, lse_ref = _sdpa_masked(q, keys, values, mask, scale)
+    empty = ~mask.any(axis=2)
+    assert empty.any() and not empty.all()
+    np.testing.assert_allclose(out[~empty], o_ref[~empty], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[~empty], lse_ref[~empty], rtol=1e-12, atol=1e-12)
+    assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+def test_chunk_attention_equals_masked_sdpa(g):
+    """Multi-query chunk ([PageWeaver] eq. (1)-(2)) with per-query lengths,
+    causal limits inside pages and query head i on KV head i // g."""
+    _pin_chunk_against_sdpa(quest, g)
+
+
+def _pin_decode_gqa_against_sdpa(qmod, g):
+    """decode_request at g > 1 on given lists and on its own top-K lists:
+    c = L - 1, query head i on KV head i // g."""
+    rng = _rng(50 + g)
+    H_kv, d, S, L = 3, 8, 4, 45
+    keys = rng.normal(size=(L, H_kv, d)) * np.arange(1, H_kv + 1)[None, :, None]
+    values = rng.normal(size=(L, H_kv, d)) + 2.0 * np.arange(H_kv)[None, :, None]
+    q = rng.normal(size=(H_kv * g, d))
+    scale = 1 / math.sqrt(d)
+    P = quest.num_pages(L, S)
+    given = [[0, 3, 3, -1, P - 1], [5, 7, P], [1, 2, 4, 6, 8, 10]]
+    for ids in (given, None):
+        res = qmod.decode_request(q, keys, values, L, S, 4, scale=scale, page_ids=ids)
+        lists = res["sel"] if ids is None else ids
+        mask = _membership_mask([lists], [L], [L - 1], S, L, g)
+        o_ref, lse_ref = _sdpa_masked(q[None], keys, values, mask, scale)
+        np.testing.assert_allclose(res["out"], o_ref[0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"], lse_ref[0], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_decode_request_gqa_equals_masked_sdpa(g):
+    _pin_decode_gqa_against_sdpa(quest, g)
+
+
+def _planted(old, new, where):
+    """A copy of oracle.quest with one line of function `where` replaced."""
+    import types
+    src = open(quest.__file__).read()
+    head, sep, body = src.partition(f"def {where}(")
+    first, nxt, rest = body.partition("\ndef ")
+    assert sep and old in first, (where, old)
+    mod = types.ModuleType("quest_planted")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(head + sep + first.replace(old, new) + nxt + rest, "quest_planted", "exec"),
+         mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("old,new,where,pin", [
+    ("support(sets[n][h], L[n], c[n], S)", "support(sets[n][h], L[n], L[n] - 1, S)",
+     "chunk_attention", "chunk"),                                  # ignores c_n
+    ("h = i // g", "h = i % keys.shape[1]", "chunk_attention", "chunk"),  # wrong head map
+    ("h = i // g", "h = i % H_kv", "decode_request", "decode"),
+    ("support(lists[h], L, L - 1, S)", "support(lists[h], L, L - 2, S)",
+     "decode_request", "decode"),                                   # exclusive limit
+])
+def test_planted_attention_mistakes_fail_a_pin(old, new, where, pin):
+    """Each mistake planted in a copy of the oracle fails the SDPA pins."""
+    mod = _planted(old, new, where)
+    fn = _pin_chunk_against_sdpa if pin == "chunk" else _pin_decode_gqa_against_sdpa
+    failed = 0
+    for g in (2, 4):
+        try:
+            fn(mod, g)
+        except AssertionError:
+            failed += 1
+    assert failed == 2, f"planted '{new}' in {where} passed a pin"
+
+
 def test_workload_cases_are_well_formed():
     c1 = tiny_single_head()
     assert c1.keys[0].shape == (64, 1, 16) and c1.K == 4
