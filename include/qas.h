@@ -13,7 +13,8 @@
  *   "device" must point to device memory of the current HIP device; the
  *   library keeps no pointer after a call returns and allocates no memory
  *   (scratch space is passed in as a workspace).  The library has no global
- *   state apart from a thread-local error string, and may be called from
+ *   state apart from a thread-local error string and the static per-GPU
+ *   scratch array of qas_decode_layer_noalloc, and may be called from
  *   several threads.
  * Execution.  Work is enqueued asynchronously on `stream` (a hipStream_t
  *   passed as void*; NULL is the null stream).  No call synchronises.
@@ -261,6 +262,29 @@ qas_status qas_decode_layer_mixed(const qas_cache* cache, const qas_batch* batch
                                   const void* v_new, int32_t* sel_out, void* out,
                                   float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * qas_decode_layer_noalloc - qas_decode_layer for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same call, kernels and results, with
+ * its scratch space (page scores, split partials, counters) taken from a
+ * library-owned static device array of QAS_NOALLOC_SCRATCH_BYTES per GPU
+ * instead of a caller workspace.  Calls whose qas_workspace_bytes(
+ * QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, k) exceeds that maximum
+ * return QAS_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing (no hipMalloc / hipFree); on its first use on a device it looks up
+ * that device's copy of the array.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (several streams or threads)
+ * race and must be serialised by the caller.  Other arguments and errors as
+ * in qas_decode_layer.
+ */
+#define QAS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+qas_status qas_decode_layer_noalloc(const qas_cache* cache, const qas_batch* batch,
+                                    const void* q, int32_t q_dtype,
+                                    int32_t num_q_heads, int32_t k, float sm_scale,
+                                    const void* k_new, const void* v_new,
+                                    int32_t* sel_out, void* out, float* lse,
+                                    void* stream);
 
 /*
  * Multi-query chunk ([PageWeaver] eq. (1)-(2) per query; query unions and

@@ -62,6 +62,8 @@ _SIGNATURES = {
                               _P, _P, _P, ctypes.c_size_t, _P]),
     "qas_decode_layer_mixed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
                                     _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "qas_decode_layer_noalloc": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
+                                      _P, _P, _P]),
     "qas_workspace_bytes": (ctypes.c_size_t, [_I, _P, _P, _I, _I]),
     "qas_decode_positions": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
@@ -218,6 +220,16 @@ def qas_decode_layer(cache, batch, q, k, sm_scale, out, lse, workspace, k_new=No
                                 _stream(stream)))
 
 
+def qas_decode_layer_noalloc(cache, batch, q, k, sm_scale, out, lse, k_new=None, v_new=None,
+                             sel_out=None, stream=None):
+    """qas_decode_layer with the library's per-GPU static scratch instead of a
+    caller workspace (no device allocation; overlapping calls on one GPU race)."""
+    _check(_load().qas_decode_layer_noalloc(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
+                                            dtype_code(q), q.shape[1], int(k), float(sm_scale),
+                                            _ptr(k_new), _ptr(v_new), _ptr(sel_out), _ptr(out),
+                                            _ptr(lse), _stream(stream)))
+
+
 def qas_decode_layer_mixed(cache, batch, q, k, sink_tokens, local_tokens, sm_scale, out, lse,
                            workspace, k_new=None, v_new=None, sel_out=None, stream=None):
     _check(_load().qas_decode_layer_mixed(ctypes.byref(cache), ctypes.byref(batch), _ptr(q),
@@ -302,7 +314,8 @@ def version():
 
 
 __all__ = ["qas_append", "qas_rollback", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
-           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_decode_positions",
+           "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_decode_layer_noalloc",
+           "qas_decode_positions",
            "qas_positions_workspace_bytes", "qas_exact_top_r", "qas_exact_top_r_workspace_bytes",
            "qas_workspace_bytes", "make_workspace", "qas_chunk_groups", "qas_regroup_queries", "qas_union_pages",
            "qas_chunk_attention", "make_cache", "make_batch",

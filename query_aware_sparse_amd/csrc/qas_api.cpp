@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "qas.h"
 #include <stdint.h>
@@ -810,3 +811,58 @@ qas_status qas_chunk_attention(const qas_cache* cache, const qas_batch* batch,
 }
 
 }  // extern "C"
+
+// ------------------------------------------------- decode layer, no alloc ----
+// Scratch of qas_decode_layer_noalloc: a static device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code its
+// name stands for a host-side shadow, not a device address: kernels receive
+// the device address looked up per device below.  Zero-initialised at load;
+// the decode-layer call leaves the counters it uses at zero.
+static __device__ __align__(256) unsigned char scratch[QAS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.
+qas_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QAS_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(QAS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QAS_OK;
+}
+
+}  // namespace
+
+extern "C" qas_status qas_decode_layer_noalloc(const qas_cache* cache, const qas_batch* batch,
+                                               const void* q, int32_t q_dtype,
+                                               int32_t num_q_heads, int32_t k, float sm_scale,
+                                               const void* k_new, const void* v_new,
+                                               int32_t* sel_out, void* out, float* lse,
+                                               void* stream) {
+  const size_t need = qas_workspace_bytes(QAS_OP_DECODE_LAYER, cache, batch, num_q_heads, k);
+  if (need > QAS_NOALLOC_SCRATCH_BYTES)
+    return fail(QAS_ERR_WORKSPACE, "decode layer needs %zu bytes of scratch, above the %zu-byte "
+                "maximum of qas_decode_layer_noalloc", need, (size_t)QAS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const qas_status st = scratch_address(&ws);
+  if (st) return st;
+  // argument checks (and the launch) are the workspace entry point's
+  return qas_decode_layer(cache, batch, q, q_dtype, num_q_heads, k, sm_scale, k_new, v_new,
+                          sel_out, out, lse, ws, QAS_NOALLOC_SCRATCH_BYTES, stream);
+}
