@@ -134,10 +134,47 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(case, seconds):
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+_CPU = {}       # arrays shared with forked oracle workers (set before the fork)
+
+
+def _cpu_heads(heads):
+    """Oracle of one decode-layer call restricted to KV heads `heads`: bounds
+    of every page, the group score, top-K and attention per query head."""
+    from oracle import quest
+    c = _CPU
+    g, S, K, L = c["g"], c["S"], c["K"], c["L"]
+    for h in heads:
+        qh = c["q"][h * g:(h + 1) * g]
+        U = quest.kv_head_scores(quest.head_bounds(qh, c["m"][:, h:h + 1], c["M"][:, h:h + 1]),
+                                 1)[0]
+        sel = quest.top_k_pages(U, K)
+        A = quest.support(sel, L, L - 1, S)
+        for i in range(g):
+            quest.attend(qh[i], c["keys"][:, h], c["values"][:, h], A, c["scale"])
+    return len(heads)
+
+
+def cpu_baseline(case, seconds, workers):
     """The oracle as it stands, timed on the host on the same call with the
     summaries prebuilt (the GPU keeps them current): bounds of every page,
-    group scores, top-K and attention per head.  BLAS is held to one thread."""
+    group scores, top-K and attention per head.  Two runs: one thread (BLAS
+    held to one thread), then the KV heads spread over `workers` forked
+    processes of one thread each (the oracle's (request, KV head) units are
+    independent).  Runs before the GPU is touched."""
+    import multiprocessing
+
     import threadpoolctl
 
     import oracle
@@ -147,31 +184,40 @@ def cpu_baseline(case, seconds):
     L = int(case.seq_lens[0])
     keys, values = oracle.decoded_kv(case, 0)
     m, M = quest.page_summaries(keys, L, case.S)
-    q = oracle.decode(case.q[0][0], case.q_dtype)
-    calls = 0
-    with threadpoolctl.threadpool_limits(1):
-        t0 = time.perf_counter()
-        while True:
-            U = quest.kv_head_scores(quest.head_bounds(q, m, M), case.H_kv)
-            for h in range(case.H_kv):
-                sel = quest.top_k_pages(U[h], case.K)
-                for i in range(h * case.g, (h + 1) * case.g):
-                    A = quest.support(sel, L, L - 1, case.S)
-                    quest.attend(q[i], keys[:, h], values[:, h], A, case.sm_scale)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    per_call = el / calls
+    _CPU.update(keys=keys, values=values, m=m, M=M, q=oracle.decode(case.q[0][0], case.q_dtype),
+                g=case.g, S=case.S, K=case.K, L=L, scale=case.sm_scale)
     nbytes = traffic.decode_layer_bytes(
         B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=2, q_bytes=2,
         pages_scanned=len(m), page_heads_selected=case.H_kv * case.K)["total"]
-    return {"value": round(nbytes / per_call / 1e9, 4), "unit": "GB/s", "cores": 1,
+    heads = list(range(case.H_kv))
+
+    def run(fn):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return calls, el
+
+    with threadpoolctl.threadpool_limits(1):
+        n1, el1 = run(lambda: _cpu_heads(heads))
+        ctx = multiprocessing.get_context("fork")
+        with ctx.Pool(workers) as pool:
+            chunks = [heads[w::workers] for w in range(workers) if heads[w::workers]]
+            pool.map(_cpu_heads, chunks)                     # warm the workers
+            nw, elw = run(lambda: pool.map(_cpu_heads, chunks))
+    _CPU.clear()
+    per1, perw = el1 / n1, elw / nw
+    return {"value": round(nbytes / perw / 1e9, 4), "unit": "GB/s", "cores": workers,
             "kind": "oracle",
-            "sample": (f"{calls} full decode-layer calls of the same workload (layer 0, "
-                       f"summaries prebuilt), {el:.1f} s, float64 numpy, 1 thread; "
-                       f"{per_call * 1e3:.1f} ms per call"),
-            "cpu": platform.processor() or platform.machine()}
+            "sample": (f"{nw} full decode-layer calls of the headline workload (layer 0, "
+                       f"summaries prebuilt), {elw:.1f} s, float64 numpy, KV heads over "
+                       f"{workers} single-threaded processes; {perw * 1e3:.1f} ms per call"),
+            "cpu": cpu_model(),
+            "single_thread": {"value": round(nbytes / per1 / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "calls": n1, "seconds": round(el1, 1),
+                              "ms_per_call": round(per1 * 1e3, 2)}}
 
 
 def chunk_accounting(case, ids=None):
@@ -206,7 +252,9 @@ def chunk_accounting(case, ids=None):
             "mean_union_pages": union_pages / (H * (-(-N // case.group)))}
 
 
-def bench_chunk(args):
+def bench_chunk(args, NL=4, emit=True):
+    """The multi-query chunk call; returns its result dict (and prints it as
+    a line of its own if `emit`)."""
     import torch
 
     import query_aware_sparse_amd as qas
@@ -215,7 +263,7 @@ def bench_chunk(args):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    NL = max(1, args.layers)
+    NL = max(1, NL)
     case = multiquery_chunk()
     log(f"[bench] workload {case.name}: L={case.L} S={case.S} N={case.N} "
         f"kq={case.kq} heads={case.H_q}/{case.H_kv} copies={NL}")
@@ -250,35 +298,10 @@ def bench_chunk(args):
     def timed(fn):
         """Graph of one pass over the copies, replayed; returns (wall ms per
         call, event-timed us per call, calls)."""
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            for w in range(max(NL, args.warmup)):
-                fn(w % NL)
-        torch.cuda.current_stream().wait_stream(stream)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(NL):
-                fn(i)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        reps = max(1, math.ceil(args.steps / NL))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        rs = torch.cuda.current_stream()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for e0, e1 in evs:
-            e0.record(rs)
-            graph.replay()
-            e1.record(rs)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        n = reps * NL
-        return (wall * 1e3 / n, float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL,
-                n)
+        steps = max(NL, args.chunk_steps)
+        ms, us = graph_time(torch, [lambda i=i: fn(i) for i in range(NL)], steps,
+                            max(NL, min(args.warmup, 8)))
+        return ms, us, steps
 
     # original order (the line's value), then the windowed regroup
     ms, call_us, steps = timed(call)
@@ -349,46 +372,82 @@ def bench_chunk(args):
                      "us_per_launch": round(call_us, 3),
                      "useful_tflops": round(use, 2)},
     }
-    print(json.dumps(result), flush=True)
+    if emit:
+        print(json.dumps(result), flush=True)
+    del copies, base, out, lse, ids, shuf
+    torch.cuda.empty_cache()
+    return result
 
 
-def time_decode_calls(torch, args, NL, call, out):
-    """Eager warm-up, one pass over the layers captured in a HIP graph and
-    replayed; the graph's outputs must equal the eager ones.  Returns (wall
-    ms per call, event-timed us per call, calls timed)."""
+def graph_time(torch, calls, steps, warmup, check=None):
+    """Time exactly `steps` calls cycling through `calls` (zero-argument
+    callables, e.g. one per layer cache): `warmup` eager calls (at least one
+    pass), then a HIP graph of one pass (and one of the first steps % n calls)
+    replayed so that the timed region holds exactly `steps` calls, bracketed
+    by a device synchronisation on both sides and by events on the stream the
+    graphs replay on; a pass shorter than 32 calls is repeated inside the
+    graph.  ``check`` (a tensor the calls write) must come out of
+    a replay equal to the eager result.  Returns (wall ms per call,
+    event-timed us per call)."""
+    # short passes are repeated inside one graph (at least 32 calls), so that
+    # a replay's host-side launch cost stays below its GPU time
+    calls = list(calls) * max(1, -(-32 // len(calls)))
+    n = len(calls)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
-        for w in range(max(NL, args.warmup)):
-            call(w % NL)
+        for w in range(max(n, warmup)):
+            calls[w % n]()
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
-    eager_out = out.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(NL):
-            call(i)
+    eager = None if check is None else check.clone()
+    full = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(full, stream=stream):
+        for c in calls:
+            c()
+    part = None
+    if steps % n:
+        part = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(part, stream=stream):
+            for c in calls[:steps % n]:
+                c()
     torch.cuda.synchronize()
-    for _ in range(max(1, args.warmup // NL)):
-        graph.replay()
+    full.replay()
     torch.cuda.synchronize()
-    if not torch.equal(out, eager_out):
+    if eager is not None and not torch.equal(check, eager):
         raise RuntimeError("graph replay differs from the eager calls")
-    reps = max(1, math.ceil(args.steps / NL))
-    steps = reps * NL
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
+    rs = torch.cuda.current_stream()          # graph.replay() launches here
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    replay_stream = torch.cuda.current_stream()   # graph.replay() launches here
-    for e0, e1 in evs:
-        e0.record(replay_stream)
-        graph.replay()
-        e1.record(replay_stream)
+    e0.record(rs)
+    for _ in range(steps // n):
+        full.replay()
+    if part is not None:
+        part.replay()
+    e1.record(rs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3 / NL
-    return wall * 1e3 / steps, call_us, steps
+    return wall * 1e3 / steps, e0.elapsed_time(e1) * 1e3 / steps
+
+
+def event_percentiles(torch, fn, n=200, warm=20, busy_cycles=40000):
+    """p50 / p95 (us) of single calls: before each call the stream is kept
+    busy by a spin kernel, so that the start event is taken when the GPU
+    reaches the call rather than when the host issued it."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(warm + n):
+        torch.cuda._sleep(busy_cycles)
+        if i >= warm:
+            evs[i - warm][0].record()
+        fn(i)
+        if i >= warm:
+            evs[i - warm][1].record()
+    torch.cuda.synchronize()
+    t = np.sort([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return float(np.percentile(t, 50)), float(np.percentile(t, 95))
 
 
 def time_cold_flush(torch, call, warm=20, timed=200):
@@ -455,13 +514,166 @@ def bench_next_rows(torch, qas, args, case, exact, db, qs, NL):
     res = {}
     for name, fn, o in (("speculative_positions_gamma4", call_pos, out_pos),
                         ("exact_top_r_64", call_topr, tok), ("rollback_rescan", call_rb, pr)):
-        _, us, _ = time_decode_calls(torch, args, NL, fn, o)
+        _, us = graph_time(torch, [lambda i=i, fn=fn: fn(i) for i in range(NL)], NL,
+                           args.warmup, o)
         res[name] = {"us_per_call": round(us, 3)}
         log(f"[bench] {name}: {us:.2f} us/call")
     prh = pr.cpu().numpy()
     res["exact_top_r_64"]["pages_read_per_head"] = {
         "mean": round(float(prh.mean()), 1), "min": int(prh.min()), "max": int(prh.max()),
         "of": L // case.S}
+    return res
+
+
+def _free(torch):
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def bench_decode_case(torch, qas, args, case, copies, steps_per_copy=1, corrupt=False):
+    """A decode-layer workload other than the headline: `copies` device copies
+    of its cache (visited in turn so that no call finds its bytes in the
+    Infinity Cache), and for a case with append steps one call per step, each
+    appending that step's token.  Returns a dict with us per call, the
+    algorithmic bytes of the average call and the achieved rate.  With
+    `corrupt`, also the attention alone on seeded corrupted lists (duplicates,
+    invalid IDs, empty rows) through qas_sparse_decode."""
+    from query_aware_sparse_amd import traffic
+    from query_aware_sparse_amd.staging import DeviceBatch, PagedCache, prefill, to_device
+    from workloads import corrupt_lists
+
+    base = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype,
+                      poison=False)
+    prefill(base, case)
+    caches = [base.cache]
+    keep = [base]
+    for _ in range(1, copies):
+        pc = PagedCache(case.num_pool_pages, case.H_kv, case.S, case.d, case.kv_dtype,
+                        poison=False)
+        pc.k_pool.copy_(base.k_pool)
+        pc.v_pool.copy_(base.v_pool)
+        pc.summary.copy_(base.summary)
+        caches.append(pc.cache)
+        keep.append(pc)
+    n_steps = max(1, case.steps) if steps_per_copy else 1
+    kvb = {"f32": 4, "f16": 2, "bf16": 2}[case.kv_dtype]
+    plans, nbytes = [], []
+    for s in range(n_steps):
+        step = s if case.steps else -1
+        L = case.lengths(step)
+        db = DeviceBatch(L, case.pages, case.S)
+        q = to_device(case.q[step + 1], case.q_dtype)
+        kn = vn = None
+        if case.steps:
+            kn = to_device(np.stack([case.keys[r][L[r] - 1] for r in range(case.B)]),
+                           case.kv_dtype)
+            vn = to_device(np.stack([case.values[r][L[r] - 1] for r in range(case.B)]),
+                           case.kv_dtype)
+        P = [-(-int(x) // case.S) for x in L]
+        plans.append((db, q, kn, vn))
+        nbytes.append(traffic.decode_layer_bytes(
+            B=case.B, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S, kv_bytes=kvb,
+            q_bytes=kvb, pages_scanned=sum(P),
+            page_heads_selected=case.H_kv * sum(min(case.K, p) for p in P),
+            append_tokens=case.B if case.steps else 0)["total"])
+    max_pages = max(p[0].max_pages for p in plans)
+    big = max(plans, key=lambda p: p[0].max_pages)[0]
+    ws = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, caches[0], big.batch, case.H_q, case.K)
+    out = torch.empty((copies, case.B, case.H_q, case.d), dtype=plans[0][1].dtype, device="cuda")
+    lse = torch.empty((copies, case.B, case.H_q), device="cuda")
+    calls = []
+    for s, (db, q, kn, vn) in enumerate(plans):
+        for c in range(copies):
+            calls.append(lambda c=c, db=db, q=q, kn=kn, vn=vn: qas.qas_decode_layer(
+                caches[c], db.batch, q, case.K, case.sm_scale, out[c], lse[c], ws,
+                k_new=kn, v_new=vn))
+    steps = max(len(calls), args.sub_steps - args.sub_steps % len(calls))
+    ms, us = graph_time(torch, calls, steps, len(calls))
+    avg = float(np.mean(nbytes))
+    res = {"us_per_call": round(us, 3), "wall_us_per_call": round(ms * 1e3, 3),
+           "calls_timed": steps, "bytes_per_call": int(round(avg)),
+           "GB/s": round(avg / (us * 1e-6) / 1e9, 1),
+           "frac_of_hbm_peak": round(avg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "cache_copies": copies, "kv_dtype": case.kv_dtype, "batch": case.B,
+           "q_heads": case.H_q, "kv_heads": case.H_kv, "page_size": case.S,
+           "top_k_pages": case.K, "max_pages": max_pages,
+           "seq_lens": [int(x) for x in case.seq_lens]}
+    if case.steps:
+        res["steps"] = n_steps
+        res["append_current_token"] = True
+    if corrupt:
+        db = plans[0][0]
+        q = plans[0][1]
+        sel = torch.empty((case.B, case.H_kv, case.K), dtype=torch.int32, device="cuda")
+        qas.qas_decode_layer(caches[0], db.batch, q, case.K, case.sm_scale, out[0], lse[0], ws,
+                             sel_out=sel)
+        torch.cuda.synchronize()
+        P = [-(-int(x) // case.S) for x in case.seq_lens]
+        bad, cat = corrupt_lists(sel.cpu().numpy(), P, seed=5)
+        bad_t = torch.from_numpy(bad).cuda()
+        wsd = qas.make_workspace(qas.QAS_OP_SPARSE_DECODE, caches[0], db.batch, case.H_q, case.K)
+        scalls = [lambda c=c: qas.qas_sparse_decode(caches[c], db.batch, q, bad_t, case.K,
+                                                    case.sm_scale, out[c], lse[c], wsd)
+                  for c in range(copies)]
+        _, us_c = graph_time(torch, scalls, max(copies, args.sub_steps), copies)
+        distinct = 0
+        for r in range(case.B):
+            for h in range(case.H_kv):
+                distinct += len({int(x) for x in bad[r, h] if 0 <= x < P[r]})
+        cb = traffic.decode_layer_bytes(B=case.B, H_q=case.H_q, H_kv=case.H_kv, d=case.d,
+                                        S=case.S, kv_bytes=kvb, q_bytes=kvb, pages_scanned=0,
+                                        page_heads_selected=distinct)["total"]
+        res["corrupted_lists_attention"] = {
+            "us_per_call": round(us_c, 3), "bytes_per_call": cb,
+            "GB/s": round(cb / (us_c * 1e-6) / 1e9, 1),
+            "empty_rows": int((cat == 4).sum()), "rows": int(cat.size),
+            "entry_point": "qas_sparse_decode (dedupe, invalid IDs dropped)"}
+    del keep, caches, plans, ws, out, lse, calls
+    _free(torch)
+    return res
+
+
+def bench_stages(torch, qas, args, case, exact, db, qs, NL):
+    """Stages of the headline call timed through their own entry points over
+    the same layer caches: page scores (qas_score_pages), top-K
+    (qas_topk_pages; mean of a graph replay, and p50 / p95 of single calls)
+    and attention with the split merge on those lists (qas_sparse_decode)."""
+    from query_aware_sparse_amd import traffic
+    L = int(case.seq_lens[0])
+    P = L // case.S
+    scores = torch.empty((NL, P * case.H_kv), device="cuda")
+    sel = torch.empty((NL, 1, case.H_kv, case.K), dtype=torch.int32, device="cuda")
+    out = torch.empty((NL, 1, case.H_q, case.d), dtype=torch.float16, device="cuda")
+    lse = torch.empty((NL, 1, case.H_q), device="cuda")
+    wsd = qas.make_workspace(qas.QAS_OP_SPARSE_DECODE, exact[0], db.batch, case.H_q, case.K)
+    score = [lambda i=i: qas.qas_score_pages(exact[i], db.batch, qs[i], scores[i])
+             for i in range(NL)]
+    topk = [lambda i=i: qas.qas_topk_pages(scores[i], db.batch, case.H_kv, case.S, case.K, sel[i])
+            for i in range(NL)]
+    attn = [lambda i=i: qas.qas_sparse_decode(exact[i], db.batch, qs[i], sel[i], case.K,
+                                              case.sm_scale, out[i], lse[i], wsd)
+            for i in range(NL)]
+    _, us_s = graph_time(torch, score, NL, NL, scores)
+    _, us_t = graph_time(torch, topk, NL, NL, sel)
+    _, us_a = graph_time(torch, attn, NL, NL, out)
+    p50, p95 = event_percentiles(torch, lambda i: topk[i % NL]())
+    parts = traffic.decode_layer_bytes(B=1, H_q=case.H_q, H_kv=case.H_kv, d=case.d, S=case.S,
+                                       kv_bytes=2, q_bytes=2, pages_scanned=P,
+                                       page_heads_selected=case.H_kv * case.K)
+    sb = parts["summary"] + parts["q_out"] // 2
+    ab = parts["selected_kv"] + parts["q_out"]
+    log(f"[bench] stages: score {us_s:.2f} us, top-k {us_t:.2f} us (p50 {p50:.2f}, p95 {p95:.2f}),"
+        f" attention+merge {us_a:.2f} us")
+    res = {"score_us": round(us_s, 3), "score_GB/s": round(sb / (us_s * 1e-6) / 1e9, 1),
+           "topk_us": round(us_t, 3), "topk_p50_us": round(p50, 3), "topk_p95_us": round(p95, 3),
+           "attention_merge_us": round(us_a, 3),
+           "attention_GB/s": round(ab / (us_a * 1e-6) / 1e9, 1),
+           "note": ("each stage through its own entry point (qas_score_pages, qas_topk_pages, "
+                    "qas_sparse_decode) over the same 32 layer caches; the fused call runs "
+                    "the same stages with fewer kernel boundaries; top-K p50/p95 over 200 "
+                    "single event-timed calls")}
+    del scores, sel, out, lse, wsd
     return res
 
 
@@ -472,39 +684,69 @@ def main():
     ap.add_argument("--steps", type=int, default=640, help="timed decode-layer calls")
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--layers", type=int, default=32, help="layer caches visited in turn")
+    ap.add_argument("--sub-steps", type=int, default=256,
+                    help="timed calls of each other workload (rounded to whole passes)")
+    ap.add_argument("--chunk-steps", type=int, default=64, help="timed chunk calls per variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--workload", choices=("decode", "chunk"), default="decode")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", choices=("all", "decode", "chunk", "config1", "config3",
+                                           "config5"), default="all",
+                    help="all: the headline line with every workload; the others time "
+                         "one workload alone (profiling passes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip the NEXT-4 timings (counter passes of the decode-layer call)")
+                    help="skip the NEXT-4 timings")
     ap.add_argument("--no-cold-flush", action="store_true",
-                    help="skip the cold-cache protocol (counter passes of the decode-layer call)")
+                    help="skip the cold-cache protocol")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but the path runs on one GPU "
               "(no multi-GPU mode); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        sys.exit("bench.py: --steps must be >= 1")
     if args.copy_calibration:
         return copy_calibration()
     if args.workload == "chunk":
-        if args.layers == 32:
-            args.layers = 4
-        return bench_chunk(args)
+        args.chunk_steps = args.steps
+        return bench_chunk(args, NL=4 if args.layers == 32 else args.layers)
+
+    from workloads import (batched_gqa_append, layer_queries, llama2_7b_layer,
+                           stress_long_context, tiny_single_head)
+
+    case = llama2_7b_layer()
+    cpu = None
+    if args.workload in ("all", "decode") and not args.no_cpu_baseline:
+        # the oracle runs before the GPU is touched (its workers are forked)
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"[bench] timing the oracle on the host (1 thread, then {workers} processes) ...")
+        cpu = cpu_baseline(case, args.cpu_seconds, workers)
 
     import torch
 
     import query_aware_sparse_amd as qas
     from query_aware_sparse_amd import traffic
     from query_aware_sparse_amd.staging import PagedCache, prefill, to_device
-    from workloads import llama2_7b_layer, layer_queries
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    subs = {"config1": (lambda: tiny_single_head(), 1, "tiny single instance (d16, S4, 64 tokens)"),
+            "config3": (lambda: batched_gqa_append(), 8,
+                        "batched GQA decode with append (8 requests, 8K-64K, 32/8 heads, bf16)"),
+            "config5": (lambda: stress_long_context(), 2,
+                        "stress: 16 requests x 131072 tokens, 32/8 heads, S32, K41, fp16")}
+    if args.workload in subs:
+        make, copies, what = subs[args.workload]
+        res = bench_decode_case(torch, qas, args, make(), copies,
+                                corrupt=args.workload == "config5")
+        res["workload"] = what
+        print(json.dumps({"workload": args.workload, **res}), flush=True)
+        return
+
     NL = args.layers
-    case = llama2_7b_layer()
     L = int(case.seq_lens[0])
     log(f"[bench] workload {case.name}: L={L} P={L // case.S} K={case.K} "
         f"H={case.H_q}x{case.d} layers={NL}")
@@ -543,8 +785,13 @@ def main():
         qas.qas_decode_layer(layers[i].cache, db.batch, qs[i], case.K, case.sm_scale,
                              out[i], lse[i], ws, k_new=k_new, v_new=v_new)
 
-    ms_per_step, call_us, steps = time_decode_calls(torch, args, NL, call, out)
-    ms_fp8, us_fp8, _ = time_decode_calls(torch, args, NL, call_fp8, out)
+    calls = [lambda i=i: call(i) for i in range(NL)]
+    ms_per_step, call_us = graph_time(torch, calls, args.steps, args.warmup, out)
+    sub_steps = max(NL, args.sub_steps - args.sub_steps % NL)
+    ms_fp8, us_fp8 = graph_time(torch, [lambda i=i: call_fp8(i) for i in range(NL)], sub_steps,
+                                NL, out)
+    p50c, p95c = event_percentiles(torch, lambda i: call(i % NL))
+    log(f"[bench] single calls: p50 {p50c:.2f} us, p95 {p95c:.2f} us")
     cold = None
     if not args.no_cold_flush:
         cold_p50, cold_p95 = time_cold_flush(torch, call)
@@ -553,6 +800,7 @@ def main():
         cold = {"protocol": "1 GiB read (sum) before each call, eager launch, "
                             "20 warm-up + 200 timed calls, event-timed each",
                 "p50_us": round(cold_p50, 3), "p95_us": round(cold_p95, 3)}
+    stages = bench_stages(torch, qas, args, case, exact, db, qs, NL)
     next_rows = None if args.no_next_rows else bench_next_rows(torch, qas, args, case, exact, db,
                                                                qs, NL)
     bytes_fp8 = traffic.decode_layer_bytes(
@@ -571,12 +819,33 @@ def main():
         cold["GB/s_p50"] = round(total / (cold["p50_us"] * 1e-6) / 1e9, 1)
     value = total / (ms_per_step * 1e-3) / 1e9
     achieved = total / (call_us * 1e-6) / 1e9
-    log(f"[bench] {steps} calls: {ms_per_step * 1e3:.2f} us/call (wall), "
+    log(f"[bench] {args.steps} calls: {ms_per_step * 1e3:.2f} us/call (wall), "
         f"{call_us:.2f} us/call (events), {value:.1f} GB/s")
+    del layers, exact, out, lse, ws, qs
+    _free(torch)
+
+    # the other workloads, each with its own roofline fraction
+    workloads = {}
+    for key, (make, copies, what) in subs.items():
+        log(f"[bench] {key}: {what} ...")
+        res = bench_decode_case(torch, qas, args, make(), copies, corrupt=key == "config5")
+        res["workload"] = what
+        workloads[key] = res
+        log(f"[bench] {key}: {res['us_per_call']:.2f} us/call, {res['GB/s']:.1f} GB/s")
+    log("[bench] config4: multi-query chunk ...")
+    chunk = bench_chunk(args, NL=4, emit=False)
+    workloads["config4"] = {"workload": "multi-query chunk, 64K context, 512 queries, union-8, "
+                                        "fp8 K/V",
+                            "us_per_call": chunk["value"], **chunk["config"],
+                            "roofline": chunk["roofline"]}
+    workloads["config2"] = {"workload": "the headline line (this line's value)",
+                            "us_per_call": round(call_us, 3),
+                            "GB/s": round(achieved, 1),
+                            "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4)}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": "llama2-7b-shaped decode layer, 32K context",
@@ -586,22 +855,24 @@ def main():
                    "layer_caches": NL, "append_current_token": True,
                    "hip_graph": True, "us_per_call": round(ms_per_step * 1e3, 3),
                    "bytes_per_call": total, "bytes_parts": nbytes,
+                   "single_call_p50_us": round(p50c, 3), "single_call_p95_us": round(p95c, 3),
+                   "stages": stages,
                    "fp8_summary_copy": {
                        "us_per_call": round(us_fp8, 3), "bytes_per_call": bytes_fp8,
                        "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
                        "ms_per_step_wall": round(ms_fp8, 6),
                        "traffic": pmc_traffic_bytes(fp8=True)},
                    "cold_flush": cold,
-                   "next_rows": next_rows},
+                   "next_rows": next_rows,
+                   "workloads": workloads},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic_bytes(),
                      "kernel": "decode-layer call (score with fused append, top-k, attention with merge)",
                      "us_per_launch": round(call_us, 3)},
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host ...")
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
