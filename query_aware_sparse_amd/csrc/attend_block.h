@@ -1,0 +1,284 @@
+// Workgroup-level sparse attention over a list of pages staged in LDS, with
+// the split merge: the streaming and merging half of the decode attention
+// kernel (decode_kernel.h), kept apart from the list building.
+//
+// Semantics ("PageWeaver" notes, eq. (1)-(2); "3.1.1 · Quest", §2.1): for
+// each query head of the KV head's group, exact softmax attention over the
+// token rows of the staged pages (a page contributes its first ntok rows);
+// the partial softmax states of the splits of a row are merged by
+// log-sum-exp (the QuantSpec post's flash-decoding chunk merge), and an
+// empty support gives out = 0 and lse = -inf.
+//
+// Execution.  The workgroup's waves stream "token groups" (TPI token rows of
+// one page = one 16-byte load per lane for K and one for V), UNR groups per
+// wave in flight.  Each lane keeps a private online-softmax state (max, sum,
+// accumulator of its 16-byte dim chunk) per query head of the group over the
+// token rows it sees; lanes of one token row share the logit after a DPP
+// reduction.  States are merged across lanes, then waves (LDS).  With
+// several splits per row, each split stores its state and takes a ticket
+// from the row's counter; the split that arrives last merges all states by
+// log-sum-exp and writes the output.
+//
+// Memory ordering of the split merge (gfx950).  A split's states are
+// written with agent-scope relaxed atomic stores, which compile to global
+// stores with the sc1 (device-coherence) bit: they are written through the
+// XCD's L2 to the device's coherence point instead of staying dirty in it.
+// Each thread then waits for its stores with s_waitcnt vmcnt(0); the memory
+// model's own agent-scope sequences rely on that wait meaning the store is
+// performed at the coherence point (a device-scope store followed by that
+// wait is what orders it before a later operation).  The workgroup meets at
+// a barrier, and only then does one thread take the ticket with an
+// agent-scope atomic add, performed at the same point.  The split that
+// draws the last ticket value therefore follows every other split's ticket,
+// each taken after that split's states were performed, and it reads the
+// states with agent-scope loads (sc1: served from the coherence point, not
+// from a line its own XCD's L2 may hold).  The release/acquire pairing of
+// the HIP memory model would add an L2 writeback (buffer_wbl2) before each
+// ticket and an L2 invalidate (buffer_inv) after the last one; measured on
+// this part they cost about 2 us per decode-layer call here (and far more
+// where many workgroups hand off), and with every shared word written and
+// read device-coherently there is nothing dirty for them to write back or
+// stale for them to drop.
+#pragma once
+
+#include "qas_device.h"
+
+namespace qas {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+namespace attend_detail {
+
+// Merge online-softmax state (m2, l2, acc2) into (m, l, acc); -inf max means
+// an empty state.
+template <int N>
+__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float m2,
+                                            float l2, const float* acc2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  const float a1 = fast_exp2(m - mm), a2 = fast_exp2(m2 - mm);
+  l = l * a1 + l2 * a2;
+#pragma unroll
+  for (int e = 0; e < N; ++e) acc[e] = acc[e] * a1 + acc2[e] * a2;
+  m = mm;
+}
+
+// Device-coherent word stores / loads (agent scope, relaxed; sc1 on this
+// part): see the ordering note above.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace attend_detail
+
+// Where the split's result goes.
+struct AttendOut {
+  void* out;                 // [rows][H_q][D] (row = request or draft row)
+  float* lse;                // [rows][H_q] or NULL
+  float* partials;           // [rows][H_q][n_split][2 + D]
+  unsigned int* ticket;      // this (row, KV head)'s split counter (n_split > 1)
+  size_t rowq0;              // index of the group's first query head: row * H_q + h * G
+  int n_split, split;
+};
+
+// The workgroup (NW waves) attends over npg pages staged in s_phys / s_ntok
+// (physical page, token rows to read).  qraw holds this
+// lane's 16-byte chunk (lane % (D / epl)) of each query head of the group.
+// Every thread of the workgroup must call this; LDS of the staged lists may
+// be reused only after it returns.
+template <int DT, int D, int G, int UNR, int NW>
+__device__ __forceinline__ void attend_split(const int* s_phys, const int* s_ntok, int npg,
+                                             int S, const char* kbase, const char* vbase,
+                                             size_t pstride, uint32_t hoff_head,
+                                             const uint4* qraw, float sm_scale,
+                                             const AttendOut& o) {
+  using namespace attend_detail;
+  constexpr int NT = NW * kWave;
+  constexpr int EPL = epl<DT>();
+  constexpr int RL = D / EPL;                 // lanes per token row
+  constexpr int TPI = kWave / RL;             // token rows per wave load
+  constexpr int BYTES = DType<DT>::bytes;
+  __shared__ float red_m[NW][G];
+  __shared__ float red_l[NW][G];
+  __shared__ float red_acc[NW][G][D];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int c = lane % RL;
+  const int trow = lane / RL;
+  const int NI = S > TPI ? S / TPI : 1;       // token groups per page (a power of two)
+  const int lni = __ffs(NI) - 1;
+  const int units = npg * NI;
+  // byte offsets: page stride and head offset are uniform, so a load's
+  // address is one 64-bit multiply-add of its physical page
+  const uint32_t hoff = hoff_head + c * 16;
+  const float qscale = sm_scale * kLog2e;     // logits in log2 units
+  float qf[G][EPL];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    unpack16<DT>(qraw[gg], qf[gg]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[gg][e] *= qscale;
+  }
+  float m_run[G], l_run[G], acc[G][EPL];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    m_run[gg] = -INFINITY;
+    l_run[gg] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[gg][e] = 0.f;
+  }
+
+  for (int u0 = wave; u0 < units; u0 += NW * UNR) {
+    uint4 kr[UNR], vr[UNR];
+    bool ok[UNR];
+    // Every load is unconditional: a unit past the end is clamped to the last
+    // unit and a token row past the page's tokens to the page's last row, so
+    // each address stays inside an allocated page, and `ok` drops the value.
+    // (A load under a branch makes the compiler wait for every earlier load
+    // before it.)  All K loads go first, so the logits start while V is still
+    // in flight.
+    size_t offs[UNR];
+#pragma unroll
+    for (int b = 0; b < UNR; ++b) {
+      const int u = min(u0 + b * NW, units - 1);
+      const int pi = u >> lni, gi = u & (NI - 1);
+      const int tip = gi * TPI + trow;
+      ok[b] = (u0 + b * NW < units) & (tip < s_ntok[pi]);
+      offs[b] = (size_t)(uint32_t)s_phys[pi] * pstride +
+                (hoff + (uint32_t)(min(tip, S - 1) * D * BYTES));
+    }
+#pragma unroll
+    for (int b = 0; b < UNR; ++b) kr[b] = load16(kbase + offs[b]);
+#pragma unroll
+    for (int b = 0; b < UNR; ++b) vr[b] = load16(vbase + offs[b]);
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      float z[UNR];
+      float zmax = m_run[gg];
+#pragma unroll
+      for (int b = 0; b < UNR; ++b) {
+        float kf[EPL];
+        unpack16<DT>(kr[b], kf);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot += qf[gg][e] * kf[e];
+        dot = group_sum<RL>(dot);
+        z[b] = ok[b] ? dot : -INFINITY;
+        zmax = fmaxf(zmax, z[b]);
+      }
+      // No branch on the batch's content: a branch here lets the compiler
+      // sink the V loads below the logits, a second round trip per batch.
+      // With no valid logit yet the stand-in maximum 0 gives alpha = 0 and
+      // p = 0 on a zero state; rows not loaded read as zero words.
+      const float zm = zmax == -INFINITY ? 0.f : zmax;
+      const float alpha = fast_exp2(m_run[gg] - zm);
+      float l = l_run[gg] * alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[gg][e] *= alpha;
+#pragma unroll
+      for (int b = 0; b < UNR; ++b) {
+        const float p = ok[b] ? fast_exp2(z[b] - zm) : 0.f;
+        const uint4 w = ok[b] ? vr[b] : make_uint4(0, 0, 0, 0);
+        float vf[EPL];
+        unpack16<DT>(w, vf);
+        l += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[gg][e] += p * vf[e];
+      }
+      l_run[gg] = l;
+      m_run[gg] = zmax;
+    }
+  }
+
+  // ---- merge lanes of one dim chunk, then the waves ------------------------
+#pragma unroll
+  for (int off = RL; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float m2 = shfl_xor_f(m_run[gg], off);
+      const float l2 = shfl_xor_f(l_run[gg], off);
+      float acc2[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc2[e] = shfl_xor_f(acc[gg][e], off);
+      merge_state<EPL>(m_run[gg], l_run[gg], acc[gg], m2, l2, acc2);
+    }
+  }
+  if (lane < RL) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      if (lane == 0) {
+        red_m[wave][gg] = m_run[gg];
+        red_l[wave][gg] = l_run[gg];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red_acc[wave][gg][c * EPL + e] = acc[gg][e];
+    }
+  }
+  __syncthreads();
+  const bool single = o.n_split == 1;
+  for (int t = tid; t < G * D; t += NT) {
+    const int gg = t / D, dim = t - (t / D) * D;
+    float m = -INFINITY, l = 0.f, ov = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float one[1] = {red_acc[w][gg][dim]};
+      merge_state<1>(m, l, &ov, red_m[w][gg], red_l[w][gg], one);
+    }
+    const size_t rowq = o.rowq0 + gg;
+    if (single) {
+      store_rn<DT>(o.out, rowq * D + dim, m == -INFINITY ? 0.f : ov / l);
+      if (dim == 0 && o.lse)
+        o.lse[rowq] = m == -INFINITY ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
+      continue;
+    }
+    float* part = o.partials + (rowq * o.n_split + o.split) * (D + 2);
+    if (dim == 0) {
+      store_coherent(part, m);
+      store_coherent(part + 1, l);
+    }
+    store_coherent(part + 2 + dim, ov);
+  }
+  if (single) return;
+
+  // ---- the last split of the row merges all split states -----------------
+  __builtin_amdgcn_s_waitcnt(0);             // this thread's states are stored
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(o.ticket, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(o.n_split - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  constexpr int MB = 16;
+  for (int t = tid; t < G * D; t += NT) {
+    const int gg = t / D, dim = t - (t / D) * D;
+    const size_t rowq = o.rowq0 + gg;
+    const float* part = o.partials + rowq * o.n_split * (D + 2);
+    float M = -INFINITY, lsum = 0.f, ov = 0.f;
+    for (int sb = 0; sb < o.n_split; sb += MB) {
+      float ms[MB], ls[MB], os[MB];
+#pragma unroll
+      for (int k = 0; k < MB; ++k) {
+        const int sp = sb + k;
+        const bool in = sp < o.n_split;
+        ms[k] = in ? load_coherent(part + sp * (D + 2)) : -INFINITY;
+        ls[k] = in ? load_coherent(part + sp * (D + 2) + 1) : 0.f;
+        os[k] = in ? load_coherent(part + sp * (D + 2) + 2 + dim) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < MB; ++k) merge_state<1>(M, lsum, &ov, ms[k], ls[k], &os[k]);
+    }
+    store_rn<DT>(o.out, rowq * D + dim, M == -INFINITY ? 0.f : ov / lsum);
+    if (dim == 0 && o.lse)
+      o.lse[rowq] = M == -INFINITY ? -INFINITY : (M + log2f(lsum)) * 0.6931471805599453f;
+  }
+  // leave the counter at zero for the next call
+  if (tid == 0) __hip_atomic_store(o.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace qas

@@ -1,11 +1,10 @@
 // Kernel templates of the sparse paged decode attention over each query's
-// support ("PageWeaver"
-// notes, eq. (1)-(2): pages in the selected list, t < L, invalid IDs
-// ignored, duplicates once, empty support -> 0), reading the selected pages
-// in place through the page table ("3.1.1 · Quest", §2.1), with split-page
-// partial softmax states merged by log-sum-exp (the QuantSpec post's
-// flash-decoding chunk merge; §2.1 of the Quest page on one global max and
-// sum per row).
+// support ("PageWeaver" notes, eq. (1)-(2): pages in the selected list,
+// t < L, invalid IDs ignored, duplicates once, empty support -> 0), reading
+// the selected pages in place through the page table ("3.1.1 · Quest",
+// §2.1), with split-page partial softmax states merged by log-sum-exp (the
+// QuantSpec post's flash-decoding chunk merge; §2.1 of the Quest page on one
+// global max and sum per row).
 //
 // Grid (split, KV head, request).  A workgroup first finds the distinct
 // valid physical pages of its slice of the selected list and stages them in
@@ -14,24 +13,15 @@
 // page scores (the top-K stage of the decode layer, topk_block.h: every
 // split of a row repeats the same selection over the row's scores and keeps
 // its own slice, which saves a kernel boundary and a round trip of the list
-// through memory).  Its four waves then stream "token groups" (TPI token
-// rows of one page = one 16-byte load per lane for K and one for V), all of
-// a wave's groups in flight at once where registers allow.  Each lane keeps
-// a private online-softmax state (max, sum, accumulator of its 16-byte dim
-// chunk) per query head of the group over the token rows it sees; lanes of
-// one token row share the logit after a DPP reduction.  States are merged
-// across lanes, then waves.  With several splits per row, each split stores
-// its state with device-coherent stores and takes a ticket from the row's
-// counter; the split that arrives last merges all states by log-sum-exp and
-// writes the output.  Coherent (sc1) stores and loads keep this free of the
-// L2 writeback and invalidate that a device-scope fence costs on this
-// multi-XCD part.
+// through memory).  The workgroup then streams the pages' K/V and merges the
+// split states (attend_block.h).
 //
 // Included by one translation unit per K/V dtype (decode_f32.hip, ...).
 #pragma once
 
 #include "qas_device.h"
 #include "qas_internal.h"
+#include "attend_block.h"
 #include "topk_block.h"
 
 namespace qas {
@@ -47,7 +37,6 @@ template <int DT, int G> constexpr int dec_unroll() {
 constexpr int kDecMaxList = 1024;      // selected entries per split
 constexpr int kDecMaxRow = 4096;       // entries of a row when deduplicating
 constexpr int kDecFusedTopkPT = 8;    // in-kernel top-K: scores per thread at most
-constexpr float kLog2e = 1.4426950408889634f;
 
 namespace decode_detail {
 
@@ -72,29 +61,6 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* scratch, int* to
   return before + in_wave;
 }
 
-// Merge online-softmax state (m2, l2, acc2) into (m, l, acc); -inf max means
-// an empty state.
-template <int N>
-__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float m2,
-                                            float l2, const float* acc2) {
-  const float mm = fmaxf(m, m2);
-  if (mm == -INFINITY) return;
-  const float a1 = fast_exp2(m - mm), a2 = fast_exp2(m2 - mm);
-  l = l * a1 + l2 * a2;
-#pragma unroll
-  for (int e = 0; e < N; ++e) acc[e] = acc[e] * a1 + acc2[e] * a2;
-  m = mm;
-}
-
-// Device-coherent float store / load (agent scope, relaxed): visible across
-// XCDs without cache maintenance.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // TPT = 0: the caller's lists; TPT > 0: select the top-K pages in the
 // workgroup from the page scores, TPT scores per thread at most.
 template <int DT, int D, int G, int TPT>
@@ -108,10 +74,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   __shared__ int s_ntok[kDecMaxList];
   __shared__ unsigned char s_keep[kDecMaxList];
   __shared__ int s_cnt[kDecWaves];
-  __shared__ float red_m[kDecWaves][G];
-  __shared__ float red_l[kDecWaves][G];
-  __shared__ float red_acc[kDecWaves][G][D];
-  __shared__ int s_last;
 
   const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int H = a.H_kv, S = a.S;
@@ -207,185 +169,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- 2. stream K/V of the pages, online softmax per lane -----------------
-  const int c = lane % RL;
-  const int trow = lane / RL;
-  const int NI = S > TPI ? S / TPI : 1;       // token groups per page (a power of two)
-  const int lni = __ffs(NI) - 1;
-  const int units = npg * NI;
-  // byte offsets: page stride and head offset are uniform, so a load's
-  // address is one 64-bit multiply-add of its physical page
-  const size_t pstride = (size_t)H * S * D * BYTES;
-  const uint32_t hoff = (uint32_t)(h * S * D * BYTES) + c * 16;
-  const float qscale = a.sm_scale * kLog2e;   // logits in log2 units
-  float qf[G][EPL];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    unpack16<DT>(qraw[gg], qf[gg]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[gg][e] *= qscale;
-  }
-  float m_run[G], l_run[G], acc[G][EPL];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    m_run[gg] = -INFINITY;
-    l_run[gg] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[gg][e] = 0.f;
-  }
-  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
-  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
-
-  constexpr int UNR = dec_unroll<DT, G>();
-  for (int u0 = wave; u0 < units; u0 += kDecWaves * UNR) {
-    uint4 kr[UNR], vr[UNR];
-    bool ok[UNR];
-    // Every load is unconditional: a unit past the end is clamped to the last
-    // unit and a token row past the page's tokens to the page's last row, so
-    // each address stays inside an allocated page, and `ok` drops the value.
-    // (A load under a branch makes the compiler wait for every earlier load
-    // before it.)  All K loads go first, so the logits start while V is still
-    // in flight.
-    size_t offs[UNR];
-#pragma unroll
-    for (int b = 0; b < UNR; ++b) {
-      const int u = min(u0 + b * kDecWaves, units - 1);
-      const int pi = u >> lni, gi = u & (NI - 1);
-      const int tip = gi * TPI + trow;
-      ok[b] = (u0 + b * kDecWaves < units) & (tip < s_ntok[pi]);
-      offs[b] = (size_t)(uint32_t)s_phys[pi] * pstride +
-                (hoff + (uint32_t)(min(tip, S - 1) * D * BYTES));
-    }
-#pragma unroll
-    for (int b = 0; b < UNR; ++b) kr[b] = load16(kbase + offs[b]);
-#pragma unroll
-    for (int b = 0; b < UNR; ++b) vr[b] = load16(vbase + offs[b]);
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      float z[UNR];
-      float zmax = m_run[gg];
-#pragma unroll
-      for (int b = 0; b < UNR; ++b) {
-        float kf[EPL];
-        unpack16<DT>(kr[b], kf);
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dot += qf[gg][e] * kf[e];
-        dot = group_sum<RL>(dot);
-        z[b] = ok[b] ? dot : -INFINITY;
-        zmax = fmaxf(zmax, z[b]);
-      }
-      // No branch on the batch's content: a branch here lets the compiler
-      // sink the V loads below the logits, a second round trip per batch.
-      // With no valid logit yet the stand-in maximum 0 gives alpha = 0 and
-      // p = 0 on a zero state; rows not loaded read as zero words.
-      const float zm = zmax == -INFINITY ? 0.f : zmax;
-      const float alpha = fast_exp2(m_run[gg] - zm);
-      float l = l_run[gg] * alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[gg][e] *= alpha;
-#pragma unroll
-      for (int b = 0; b < UNR; ++b) {
-        const float p = ok[b] ? fast_exp2(z[b] - zm) : 0.f;
-        const uint4 w = ok[b] ? vr[b] : make_uint4(0, 0, 0, 0);
-        float vf[EPL];
-        unpack16<DT>(w, vf);
-        l += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[gg][e] += p * vf[e];
-      }
-      l_run[gg] = l;
-      m_run[gg] = zmax;
-    }
-  }
-
-  // ---- 3. merge lanes of one dim chunk, then the waves ---------------------
-#pragma unroll
-  for (int off = RL; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float m2 = shfl_xor_f(m_run[gg], off);
-      const float l2 = shfl_xor_f(l_run[gg], off);
-      float acc2[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc2[e] = shfl_xor_f(acc[gg][e], off);
-      merge_state<EPL>(m_run[gg], l_run[gg], acc[gg], m2, l2, acc2);
-    }
-  }
-  if (lane < RL) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      if (lane == 0) {
-        red_m[wave][gg] = m_run[gg];
-        red_l[wave][gg] = l_run[gg];
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red_acc[wave][gg][c * EPL + e] = acc[gg][e];
-    }
-  }
-  __syncthreads();
-  const bool single = a.n_split == 1;
-  for (int t = tid; t < G * D; t += kDecThreads) {
-    const int gg = t / D, dim = t - (t / D) * D;
-    float m = -INFINITY, l = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float one[1] = {red_acc[w][gg][dim]};
-      merge_state<1>(m, l, &o, red_m[w][gg], red_l[w][gg], one);
-    }
-    const size_t rowq = (size_t)r * a.H_q + h * G + gg;
-    if (single) {
-      store_rn<DT>(a.out, rowq * D + dim, m == -INFINITY ? 0.f : o / l);
-      if (dim == 0 && a.lse)
-        a.lse[rowq] = m == -INFINITY ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
-      continue;
-    }
-    float* part = a.partials + (rowq * a.n_split + split) * (D + 2);
-    if (dim == 0) {
-      store_coherent(part, m);
-      store_coherent(part + 1, l);
-    }
-    store_coherent(part + 2 + dim, o);
-  }
-  if (single) return;
-
-  // ---- 4. the last split of the row merges all split states ---------------
-  __builtin_amdgcn_s_waitcnt(0);             // this thread's states are stored
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.tickets + (size_t)r * H + h, 1u,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (unsigned)(a.n_split - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  constexpr int MB = 16;
-  for (int t = tid; t < G * D; t += kDecThreads) {
-    const int gg = t / D, dim = t - (t / D) * D;
-    const size_t rowq = (size_t)r * a.H_q + h * G + gg;
-    const float* part = a.partials + rowq * a.n_split * (D + 2);
-    float M = -INFINITY, lsum = 0.f, o = 0.f;
-    for (int sb = 0; sb < a.n_split; sb += MB) {
-      float ms[MB], ls[MB], os[MB];
-#pragma unroll
-      for (int k = 0; k < MB; ++k) {
-        const int sp = sb + k;
-        const bool in = sp < a.n_split;
-        ms[k] = in ? load_coherent(part + sp * (D + 2)) : -INFINITY;
-        ls[k] = in ? load_coherent(part + sp * (D + 2) + 1) : 0.f;
-        os[k] = in ? load_coherent(part + sp * (D + 2) + 2 + dim) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < MB; ++k) merge_state<1>(M, lsum, &o, ms[k], ls[k], &os[k]);
-    }
-    store_rn<DT>(a.out, rowq * D + dim, M == -INFINITY ? 0.f : o / lsum);
-    if (dim == 0 && a.lse)
-      a.lse[rowq] = M == -INFINITY ? -INFINITY : (M + log2f(lsum)) * 0.6931471805599453f;
-  }
-  // leave the counter at zero for the next call
-  if (tid == 0)
-    __hip_atomic_store(a.tickets + (size_t)r * H + h, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  // ---- 2. stream K/V of the pages, merge the states ----------------------
+  AttendOut o;
+  o.out = a.out;
+  o.lse = a.lse;
+  o.partials = a.partials;
+  o.ticket = a.tickets + (size_t)r * H + h;
+  o.rowq0 = (size_t)r * a.H_q + h * G;
+  o.n_split = a.n_split;
+  o.split = split;
+  attend_split<DT, D, G, dec_unroll<DT, G>(), kDecWaves>(
+      s_phys, s_ntok, npg, S, reinterpret_cast<const char*>(a.k_pool),
+      reinterpret_cast<const char*>(a.v_pool), (size_t)H * S * D * BYTES,
+      (uint32_t)(h * S * D * BYTES), qraw, a.sm_scale, o);
 }
 
 template <int DT, int D, int G>
