@@ -134,6 +134,32 @@ qas_status qas_append(const qas_cache* cache, const qas_batch* batch,
                       void* stream);
 
 /*
+ * qas_append_fp8 - write new tokens' K/V rows into the FP8 E4M3 cache that
+ * qas_chunk_attention reads ([PageWeaver] SS2UKVF2: FP8 E4M3 K/V with a
+ * per-KV-head scale, BF16 queries).  Each element x of KV head h is stored
+ * as the e4m3 code of x / scale[h] (quotient in fp32, clamped to +-448,
+ * rounded to the nearest code, ties to even; k_scale for K, v_scale for V),
+ * so the chunk call reads scale[h] * code.  Codes are placed in the MFMA
+ * operand order of qas_chunk_attention's pools: a (page, KV head) tile the
+ * new tokens open is written whole, with zero codes in its rows past the
+ * new tokens; a tile they extend keeps its earlier rows.  No summary is kept
+ * (the chunk path reads none).
+ *
+ * batch->seq_lens are the lengths BEFORE the append, and new_indptr /
+ * total_new / max_new are as in qas_append.
+ *   cache         kv_dtype QAS_FP8_E4M3, head_dim 128, page_size 32 or 64,
+ *                 k_pool / v_pool / k_scale / v_scale given
+ *   k_new, v_new  device [total_new][H_kv][128] in new_dtype (QAS_F32,
+ *                 QAS_F16 or QAS_BF16)
+ * Errors: QAS_ERR_DTYPE for a cache that is not FP8, QAS_ERR_UNSUPPORTED
+ * for other input dtypes, head sizes or page sizes.
+ */
+qas_status qas_append_fp8(const qas_cache* cache, const qas_batch* batch,
+                          const int32_t* new_indptr, int32_t total_new,
+                          int32_t max_new, const void* k_new, const void* v_new,
+                          int32_t new_dtype, void* stream);
+
+/*
  * qas_rollback - restore the summaries after the cache is cut back
  * ([Quest] §3, cache lifecycle: rollback).  batch->seq_lens are the lengths
  * AFTER the cut.  Pages wholly past a request's new length are the caller's

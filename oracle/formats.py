@@ -16,6 +16,11 @@ The K/V dtypes of the workloads (fp16, bf16, fp8 e4m3 with a per-KV-head
 scale) are the ones the Quest page (§2, eq. (9)-(11), FP16 KV) and the
 PageWeaver notes (FP8 E4M3 KV with BF16 queries) name.  fp32 inputs need
 no decoder.
+
+One encoder: real values to E4M3 "fn" codes by round-to-nearest, ties to
+the even code (the code whose lowest fraction bit is 0), after clamping to
+the finite range [-448, 448]; it picks among the decoded finite values, so it
+shares nothing with the decoder but the table of codes.
 """
 import numpy as np
 
@@ -88,3 +93,30 @@ def decode(raw, dtype):
     if dtype == "e4m3":
         return _table("e4m3")[raw.view(np.uint8)]
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _e4m3_code_table():
+    """(sorted distinct finite values, the code of each) of E4M3 fn; zero is
+    the +0 code."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = decode_e4m3fn(codes)
+    keep = np.isfinite(vals) & ~((codes == 0x80))       # one zero: +0
+    order = np.argsort(vals[keep], kind="stable")
+    return vals[keep][order], codes[keep][order]
+
+
+def encode_e4m3fn_rne(x):
+    """Real values (float64 array) -> E4M3 fn codes (uint8): clamp to
+    [-448, 448], then the nearest finite value, a tie going to the even code.
+    NaN input is not allowed (the writers never produce it)."""
+    vals, codes = _e4m3_code_table()
+    x = np.clip(np.asarray(x, np.float64), -448.0, 448.0)
+    assert not np.isnan(x).any(), "NaN has no rounding"
+    hi = np.clip(np.searchsorted(vals, x, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    exact = vals[hi] == x
+    d_lo = x - vals[lo]
+    d_hi = vals[hi] - x
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((codes[hi] & 1) == 0))
+    pick = np.where(exact | take_hi, hi, lo)
+    return codes[pick].astype(np.uint8)

@@ -33,7 +33,7 @@ import math
 
 import numpy as np
 
-from .formats import decode_e4m3fn
+from .formats import decode_e4m3fn, encode_e4m3fn_rne
 
 
 # ---------------------------------------------------------------- pages ----
@@ -176,6 +176,19 @@ def fp8_summaries(m, M):
                 m_hat[p, h, j] = s * e4m3_down(m[p, h, j] / s)
                 M_hat[p, h, j] = s * e4m3_up(M[p, h, j] / s)
     return m_hat, M_hat, scale
+
+
+def quantize_kv_e4m3(x, scale):
+    """FP8 E4M3 K or V of the multi-query path ([PageWeaver] SS2UKVF2: FP8
+    E4M3 K/V, BF16 queries): each element of KV head h is stored as the
+    code of x / scale[h], rounded to nearest (ties to even) after clamping
+    to +-448, and read back as scale[h] * code.  x is [T][H][d] float32; the
+    quotient is formed in float32 (the precision of the stored inputs and
+    scales, so the code - an integer - is decided in the writer's
+    precision).  Returns uint8 codes [T][H][d]."""
+    x = np.asarray(x, np.float32)
+    s = np.asarray(scale, np.float32)[None, :, None]
+    return encode_e4m3fn_rne((x / s).astype(np.float64))
 
 
 # ---------------------------------------------------------------- top-K ----

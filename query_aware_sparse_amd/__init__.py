@@ -51,6 +51,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SIGNATURES = {
     "qas_append": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
+    "qas_append_fp8": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _P]),
     "qas_rollback": (_I, [_P, _P, _P]),
     "qas_score_pages": (_I, [_P, _P, _P, _I, _I, _P, _P]),
     "qas_topk_pages": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
@@ -157,6 +158,16 @@ def qas_append(cache, batch, new_indptr, total_new, max_new, k_new, v_new, strea
     _check(_load().qas_append(ctypes.byref(cache), ctypes.byref(batch), _ptr(new_indptr),
                           int(total_new), int(max_new), _ptr(k_new), _ptr(v_new),
                           _stream(stream)))
+
+
+def qas_append_fp8(cache, batch, new_indptr, total_new, max_new, k_new, v_new, stream=None):
+    """Quantise new K/V rows (f32/f16/bf16 tensors [total_new][H_kv][128])
+    into an FP8 E4M3 chunk cache with its per-head scales (see qas.h)."""
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    _check(_load().qas_append_fp8(ctypes.byref(cache), ctypes.byref(batch), _ptr(new_indptr),
+                              int(total_new), int(max_new), _ptr(k_new), _ptr(v_new),
+                              dtype_code(k_new), _stream(stream)))
 
 
 def qas_rollback(cache, batch, stream=None):
@@ -313,7 +324,7 @@ def version():
     return _load().qas_version().decode()
 
 
-__all__ = ["qas_append", "qas_rollback", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
+__all__ = ["qas_append", "qas_append_fp8", "qas_rollback", "qas_score_pages", "qas_topk_pages", "qas_selection_capacity",
            "qas_select_pages", "qas_sparse_decode", "qas_decode_layer", "qas_decode_layer_mixed", "qas_decode_layer_noalloc",
            "qas_decode_positions",
            "qas_positions_workspace_bytes", "qas_exact_top_r", "qas_exact_top_r_workspace_bytes",

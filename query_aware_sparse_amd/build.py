@@ -28,7 +28,7 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-SOURCES = ["qas_api.cpp", "append.hip", "score.hip", "topk.hip", "decode.hip", "decode_f32.hip",
+SOURCES = ["qas_api.cpp", "append.hip", "append_fp8.hip", "score.hip", "topk.hip", "decode.hip", "decode_f32.hip",
            "decode_f16.hip", "decode_bf16.hip", "union.hip", "regroup.hip", "topr.hip"]
 
 

@@ -285,6 +285,51 @@ qas_status qas_append(const qas_cache* cache, const qas_batch* batch, const int3
   return ok();
 }
 
+qas_status qas_append_fp8(const qas_cache* cache, const qas_batch* batch,
+                          const int32_t* new_indptr, int32_t total_new, int32_t max_new,
+                          const void* k_new, const void* v_new, int32_t new_dtype,
+                          void* stream) {
+  if (!cache) return fail(QAS_ERR_NULL, "cache is NULL");
+  if (cache->kv_dtype != QAS_FP8_E4M3)
+    return fail(QAS_ERR_DTYPE, "kv_dtype %d: the fp8 writer needs an FP8 E4M3 cache",
+                cache->kv_dtype);
+  if (cache->num_kv_heads < 1) return fail(QAS_ERR_SHAPE, "num_kv_heads %d < 1", cache->num_kv_heads);
+  if (cache->num_pool_pages < 1)
+    return fail(QAS_ERR_SHAPE, "num_pool_pages %d < 1", cache->num_pool_pages);
+  if (!qas::append_fp8_supported(new_dtype, cache->head_dim, cache->page_size))
+    return fail(QAS_ERR_UNSUPPORTED,
+                "fp8 writer: inputs f32/f16/bf16, d = 128, page size 32 or 64 "
+                "(dtype %d, d %d, S %d)", new_dtype, cache->head_dim, cache->page_size);
+  if (!cache->k_pool || !cache->v_pool || !cache->k_scale || !cache->v_scale)
+    return fail(QAS_ERR_NULL, "k_pool / v_pool / k_scale / v_scale is NULL");
+  qas_status st = check_batch(batch);
+  if (st) return st;
+  if (!new_indptr) return fail(QAS_ERR_NULL, "new_indptr is NULL");
+  if (total_new < 0 || max_new < 0 || max_new > total_new)
+    return fail(QAS_ERR_SHAPE, "total_new %d / max_new %d inconsistent", total_new, max_new);
+  if (total_new == 0) return ok();
+  if (!k_new || !v_new) return fail(QAS_ERR_NULL, "k_new / v_new is NULL");
+  qas::Fp8AppendArgs a;
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = new_dtype;
+  a.seq_lens = batch->seq_lens;
+  a.new_indptr = new_indptr;
+  a.page_indptr = batch->page_indptr;
+  a.page_indices = batch->page_indices;
+  a.B = batch->batch;
+  a.H_kv = cache->num_kv_heads;
+  a.S = cache->page_size;
+  a.max_new = max_new;
+  hipError_t e = qas::launch_append_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 append launch");
+  return ok();
+}
+
 qas_status qas_rollback(const qas_cache* cache, const qas_batch* batch, void* stream) {
   qas_status st = check_cache(cache, true, true);
   if (st) return st;

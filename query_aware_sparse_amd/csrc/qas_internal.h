@@ -75,6 +75,23 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 bool append_supported(int kv_dtype, int d);
 
+struct Fp8AppendArgs {
+  void* k_pool;              // e4m3 tiles in the union kernel's operand order
+  void* v_pool;
+  const float* k_scale;      // [H_kv]
+  const float* v_scale;
+  const void* k_new;         // [total_new][H_kv][128] in new_dtype
+  const void* v_new;
+  int new_dtype;
+  const int32_t* seq_lens;   // lengths before the new tokens
+  const int32_t* new_indptr; // [B+1]
+  const int32_t* page_indptr;
+  const int32_t* page_indices;
+  int B, H_kv, S, max_new;
+};
+hipError_t launch_append_fp8(const Fp8AppendArgs& a, hipStream_t s);
+bool append_fp8_supported(int new_dtype, int d, int S);
+
 struct ToprArgs {
   const void* k_pool;
   const void* summary;

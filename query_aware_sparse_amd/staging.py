@@ -8,7 +8,7 @@ query_aware_sparse_amd's entry points.
 import numpy as np
 import torch
 
-from . import make_batch, make_cache, qas_append
+from . import make_batch, make_cache, qas_append, qas_append_fp8
 
 TORCH_KV = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
             "e4m3": torch.float8_e4m3fn}
@@ -160,12 +160,15 @@ def union_v_order(S, d=128):
 
 class ChunkBatch:
     """Device state of one or more multi-query chunks (one per request) sharing
-    an fp8 pool: pages of request r are placed after those of r - 1.  K/V
-    tokens go to their pages by plain copies (this path reads no summaries),
-    each (page, KV head) tile of S * d bytes in the union kernel's operand
-    order (union_k_order, union_v_order)."""
+    an fp8 pool: pages of request r are placed after those of r - 1, each
+    (page, KV head) tile of S * d bytes in the union kernel's operand order.
 
-    def __init__(self, cases, device="cuda"):
+    writer="library" (default) quantises each request's float32 K/V with the
+    per-head scales through qas_append_fp8, one call per request.
+    writer="host" places the case's own e4m3 codes by plain copies in the
+    order union_k_order / union_v_order give (no library call)."""
+
+    def __init__(self, cases, device="cuda", writer="library"):
         c0 = cases[0]
         H, S, d = c0.H_kv, c0.S, c0.d
         self.S = S
@@ -173,25 +176,23 @@ class ChunkBatch:
         shape = (pool, H, S, d)                     # sizes only: tiles are in operand order
         self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)   # e4m3 NaN
         self.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
-        korder = torch.from_numpy(union_k_order(S, d)).to(device)
-        vorder = torch.from_numpy(union_v_order(S, d)).to(device)
-        lengths, pages, off = [], [], 0
-        for c in cases:
-            P = ceil_div(c.L, S)
-            phys = torch.from_numpy(np.asarray(c.pages[:P], np.int64) + off).to(device)
-            for pool_t, raw, order in ((self.k_pool, c.keys, korder), (self.v_pool, c.values, vorder)):
-                t = np.zeros((P * S, H, d), np.uint8)
-                t[:c.L] = raw[:c.L]
-                tt = torch.from_numpy(t).to(device).view(P, S, H, d).permute(0, 2, 1, 3)
-                pool_t.view(pool, H, S * d)[phys] = tt.reshape(P, H, S * d)[..., order].contiguous()
-            lengths.append(c.L)
-            pages.append(np.asarray(c.pages[:P], np.int32) + off)
-            off += c.num_pool_pages
         self.k_scale = torch.from_numpy(np.asarray(c0.k_scale, np.float32)).to(device)
         self.v_scale = torch.from_numpy(np.asarray(c0.v_scale, np.float32)).to(device)
         self.cache = make_cache(self.k_pool.view(torch.float8_e4m3fn),
                                 self.v_pool.view(torch.float8_e4m3fn), None,
                                 self.k_scale, self.v_scale)
+        lengths, pages, off = [], [], 0
+        for c in cases:
+            P = ceil_div(c.L, S)
+            lengths.append(c.L)
+            pages.append(np.asarray(c.pages[:P], np.int32) + off)
+            off += c.num_pool_pages
+        if writer == "library":
+            self._write_library(cases, lengths, pages, device)
+        elif writer == "host":
+            self._write_host(cases, lengths, pages, device)
+        else:
+            raise ValueError(f"unknown writer {writer!r}")
         self.db = DeviceBatch(lengths, pages, S, device)
         q_indptr = np.zeros(len(cases) + 1, np.int32)
         q_indptr[1:] = np.cumsum([c.N for c in cases])
@@ -202,3 +203,36 @@ class ChunkBatch:
             np.concatenate([c.sets for c in cases]), np.int32)).to(device)
         self.N = int(q_indptr[-1])
         self.group = c0.group
+
+    def _write_library(self, cases, lengths, pages, device):
+        B = len(cases)
+        S = self.S
+        before = DeviceBatch(np.zeros(B, np.int32), pages, S, device)
+        full = DeviceBatch(lengths, pages, S, device)
+        batch = make_batch(before.seq_lens, full.page_indptr, full.page_indices,
+                           full.total_pages, full.max_pages)
+        for r, c in enumerate(cases):
+            if c.keys_src is None:
+                raise ValueError("the library writer needs the case's float32 K/V")
+            new_indptr = np.zeros(B + 1, np.int32)
+            new_indptr[r + 1:] = c.L
+            k = torch.from_numpy(np.ascontiguousarray(c.keys_src[:c.L], np.float32)).to(device)
+            v = torch.from_numpy(np.ascontiguousarray(c.values_src[:c.L], np.float32)).to(device)
+            qas_append_fp8(self.cache, batch, torch.from_numpy(new_indptr).to(device), c.L, c.L,
+                           k, v)
+            del k, v
+        torch.cuda.synchronize()
+
+    def _write_host(self, cases, lengths, pages, device):
+        H, S, d = cases[0].H_kv, self.S, cases[0].d
+        pool = self.k_pool.shape[0]
+        korder = torch.from_numpy(union_k_order(S, d)).to(device)
+        vorder = torch.from_numpy(union_v_order(S, d)).to(device)
+        for c, pg in zip(cases, pages):
+            P = len(pg)
+            phys = torch.from_numpy(np.asarray(pg, np.int64)).to(device)
+            for pool_t, raw, order in ((self.k_pool, c.keys, korder), (self.v_pool, c.values, vorder)):
+                t = np.zeros((P * S, H, d), np.uint8)
+                t[:c.L] = raw[:c.L]
+                tt = torch.from_numpy(t).to(device).view(P, S, H, d).permute(0, 2, 1, 3)
+                pool_t.view(pool, H, S * d)[phys] = tt.reshape(P, H, S * d)[..., order].contiguous()

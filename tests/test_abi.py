@@ -94,6 +94,33 @@ def test_validation_happens_before_any_launch(qas):
                                None) == 2
 
 
+def test_fp8_writer_validation(qas):
+    """qas_append_fp8 checks its cache, dtypes and sizes before any launch."""
+    lib, byref = qas.lib, ctypes.byref
+    fp8 = _cache(qas, kv_dtype=qas.QAS_FP8_E4M3, page_size=64, k_scale=8, v_scale=8)
+    b = _batch(qas)
+    args = (8, 16, 16, 8, 8)          # new_indptr, total_new, max_new, k_new, v_new
+    assert lib.qas_append_fp8(None, byref(b), *args, qas.QAS_F32, None) == 1
+    # not an fp8 cache
+    assert lib.qas_append_fp8(byref(_cache(qas)), byref(b), *args, qas.QAS_F32, None) == 3
+    # unsupported input dtype, head size, page size
+    assert lib.qas_append_fp8(byref(fp8), byref(b), *args, qas.QAS_FP8_E4M3, None) == 4
+    assert lib.qas_append_fp8(byref(_cache(qas, kv_dtype=qas.QAS_FP8_E4M3, page_size=16,
+                                           k_scale=8, v_scale=8)),
+                              byref(b), *args, qas.QAS_F32, None) == 4
+    assert lib.qas_append_fp8(byref(_cache(qas, kv_dtype=qas.QAS_FP8_E4M3, page_size=64,
+                                           head_dim=64, k_scale=8, v_scale=8)),
+                              byref(b), *args, qas.QAS_BF16, None) == 4
+    # scales missing
+    assert lib.qas_append_fp8(byref(_cache(qas, kv_dtype=qas.QAS_FP8_E4M3, page_size=32)),
+                              byref(b), *args, qas.QAS_F16, None) == 1
+    # inconsistent counts, missing rows
+    assert lib.qas_append_fp8(byref(fp8), byref(b), 8, 4, 16, 8, 8, qas.QAS_F32, None) == 2
+    assert lib.qas_append_fp8(byref(fp8), byref(b), 8, 16, 16, None, 8, qas.QAS_F32, None) == 1
+    # nothing to write is a no-op
+    assert lib.qas_append_fp8(byref(fp8), byref(b), 8, 0, 0, None, None, qas.QAS_F32, None) == 0
+
+
 def test_workspace_sizes_are_consistent(qas):
     lib = qas.lib
     c, b = _cache(qas), _batch(qas)

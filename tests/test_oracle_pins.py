@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import quest, run_decode
+from oracle import formats, quest, run_decode
 from tests.conftest import load_golden
 from workloads import tiny_single_head, llama2_7b_layer, batched_gqa_append, figure2_case, worked_example_case
 
@@ -791,3 +791,45 @@ def test_branch_and_bound_with_r_at_least_the_tokens_reads_everything():
     read, top, _ = quest.exact_top_r(q, keys[:, 0], L, S, 30, m[:, 0], M[:, 0])
     assert sorted(read) == list(range(quest.num_pages(L, S)))
     assert [t for _, t in top] == [t for _, t in quest.brute_top_r(q, keys[:, 0], L, L)]
+
+
+def test_kv_quantisation_is_per_head_and_in_float32():
+    """PageWeaver SS2UKVF2 (FP8 E4M3 K/V with a per-KV-head scale): code of
+    x / scale[h]; a value at the head's amax lands on 448 whatever the head,
+    and the quotient is the float32 one (a float64 quotient rounds a value
+    just below a code midpoint down where float32 rounds it to the midpoint
+    and then to the even code)."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((40, 3, 16)).astype(np.float32)
+    scale = (np.abs(x).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32)
+    codes = quest.quantize_kv_e4m3(x, scale)
+    vals = formats.decode_e4m3fn(codes)
+    for h in range(3):
+        at = np.unravel_index(np.abs(x[:, h]).argmax(), x[:, h].shape)
+        assert abs(vals[at[0], h, at[1]]) == 448.0
+    # each element is the nearest code value to its float32 quotient
+    q = (x / scale[None, :, None]).astype(np.float64)
+    grid = np.unique(formats.decode_e4m3fn(np.arange(256, dtype=np.uint8)))
+    grid = grid[np.isfinite(grid)]
+    nearest = np.abs(q[..., None] - grid).min(axis=-1)
+    assert np.allclose(np.abs(vals - q), nearest, rtol=0, atol=0)
+    # float32 vs float64 quotient: for these float32 values x / s is
+    # 1.18749999... (just below the midpoint of 1.125 and 1.25) in float64,
+    # but exactly the midpoint 1.1875 in float32, which ties to the even code
+    # 1.25 (0x3A) instead of 1.125 (0x39)
+    s = np.float32(0.9505132436752319)
+    xv = np.float32(1.1287344694137573)
+    assert float(xv) / float(s) < 1.1875 and float(xv / s) == 1.1875
+    assert quest.quantize_kv_e4m3(np.full((1, 1, 1), xv, np.float32), [s])[0, 0, 0] == 0x3A
+
+
+def test_chunk_workload_codes_are_the_oracle_quantisation():
+    """The fp8 chunk workload's stored codes (its input generator casts the
+    float32 quotients with torch) equal the oracle's quantisation of the same
+    float32 K/V with the same per-head scales, code for code."""
+    from workloads import multiquery_chunk
+    case = multiquery_chunk(seed=9, L=700, S=32, N=5, H_q=8, H_kv=2, kq=6, keep=4)
+    for codes, src, scale in ((case.keys, case.keys_src, case.k_scale),
+                              (case.values, case.values_src, case.v_scale)):
+        ref = quest.quantize_kv_e4m3(src, scale)
+        assert np.array_equal(formats.decode_e4m3fn(codes), formats.decode_e4m3fn(ref))

@@ -125,6 +125,10 @@ class ChunkCase:
     pages: np.ndarray         # physical page of each logical page
     num_pool_pages: int
     notes: str = ""
+    # fp8 cases: the float32 K/V drawn before quantisation ([L][H_kv][d]),
+    # the input of a writer that quantises itself
+    keys_src: Optional[np.ndarray] = None
+    values_src: Optional[np.ndarray] = None
 
     @property
     def g(self):
@@ -343,7 +347,6 @@ def multiquery_chunk(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
         k_scale, v_scale = (np.asarray(x, np.float32) for x in scales)
     k_codes = cast(keys / k_scale[None, :, None], "e4m3")
     v_codes = cast(values / v_scale[None, :, None], "e4m3")
-    del keys, values
     q = cast(_normal(seed, _QUERY, 0, (N, H_q, d)), "bf16")
     q_pos = (L - N + np.arange(N)).astype(np.int32)
     q_len = np.full(N, L, np.int32)
@@ -377,7 +380,8 @@ def multiquery_chunk(seed=4, L=65536, S=64, N=512, H_q=32, H_kv=8, d=128, kq=64,
     phys, pool = _pool_permutation(seed, P, 8)
     return ChunkCase("multiquery-chunk-64k", H_q, H_kv, d, S, L, N, kq,
                      group, "e4m3", "bf16", k_codes, v_codes, k_scale,
-                     v_scale, q, q_pos, q_len, sets, phys, pool)
+                     v_scale, q, q_pos, q_len, sets, phys, pool,
+                     keys_src=keys, values_src=values)
 
 
 def layer_queries(case, n_layers, seed=2):
