@@ -46,35 +46,45 @@ CHUNK_METRIC = "µs per multi-query chunk call + fp8 MFMA TFLOP/s, 64K ctx, 512 
 
 # HBM traffic of one decode-layer call from two rocprofv3 --pmc passes of this
 # bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the pass's
-# dispatches, `--no-next-rows --no-cold-flush`), scaled by what the same counters read for a
-# plain 1 GiB copy (`bench.py --copy-calibration`): FETCH_SIZE read 524301.6
-# KiB and WRITE_SIZE 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write
-# x1.0.  Valid only for the sources the decode-layer call is built from
-# (DECODE_SOURCES).
+# dispatches of each kernel instance; `--workload decode --no-cpu-baseline
+# --no-next-rows --no-cold-flush --steps 32 --warmup 4 --sub-steps 32
+# --chunk-steps 8`), scaled by what the same counters read for a plain 1 GiB
+# copy (`bench.py --copy-calibration`): FETCH_SIZE read 524300 KiB and
+# WRITE_SIZE 1048576 KiB for 1048576 KiB moved, so fetch x2.0 and write x1.0.
+# Valid only for the sources the decode-layer call is built from
+# (DECODE_SOURCES); with other sources the line reports null.
 DECODE_SOURCES = ("score.hip", "decode.hip", "decode_f32.hip", "decode_f16.hip",
-                  "decode_bf16.hip", "decode_kernel.h", "topk_block.h", "qas_device.h",
-                  "qas_internal.h", "qas_api.cpp")
+                  "decode_bf16.hip", "decode_kernel.h", "attend_block.h", "topk_block.h",
+                  "qas_device.h", "qas_internal.h", "qas_api.cpp")
 PMC_TRAFFIC = {
-    "sources_sha256": "a352bbf5bba14f890b4944b10e75ba4e6f9b96c6701450d07f5ab02ab8f42989",
-    "fetch_kib": {"score_kernel": 16562.1, "decode_kernel": 34061.7},
-    "write_kib": {"score_kernel": 610.0, "decode_kernel": 173.2},
+    "sources_sha256": "ddafd0f344c5b66254d3ed66434de0984749def8ae077d307d80182fa540f34b",
+    "fetch_kib": {"score_kernel": 16546.5, "decode_kernel": 34070.5},
+    "write_kib": {"score_kernel": 599.0, "decode_kernel": 173.3},
     # the same passes, call on the e4m3 summary copy
-    "fetch_kib_fp8": {"score8_kernel": 8498.1, "decode_kernel": 34061.7},
-    "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.2},
+    "fetch_kib_fp8": {"score8_kernel": 8498.2, "decode_kernel": 34070.5},
+    "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.3},
     "fetch_factor": 2.0,
     "write_factor": 1.0,
 }
 
 
-# Counters of the union attention kernel (the chunk line), from passes of
-# `bench.py --workload chunk --no-cpu-baseline --steps 16 --warmup 4`: medians
-# over the dispatches with the chunk's own sets (the phase the chunk line
-# times), the same scaling; valid only for CHUNK_SOURCES.
+# Counters of the union attention kernel (the chunk line), from the same
+# passes plus one of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+# SQ_INSTS_MFMA, SQ_INSTS_VALU, SQ_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_F8:
+# medians over the dispatches with the chunk's own sets (the phase the chunk
+# line times), the same scaling.  MFMA busy is a fraction of the SIMD cycles
+# while the kernel runs: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x
+# GRBM_GUI_ACTIVE / 8 XCDs, the counter's sum over the XCDs); executed fp8
+# flops are MOPS_F8 x 512 (98.30 GFLOP, the union accounting's figure).
+# Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "61dd3e0f23ea912b3fc18a060b7fa1717750c75b58f79554bcaf72631b6e795c",
-    "fetch_kib": 145403.2,
-    "write_kib": 4224.2,
+    "sources_sha256": "a4ddbf1243e37c1de21df0d3ead4ba21a6fc1234a07b511244938144bbb27872",
+    "fetch_kib": 152101.9,
+    "write_kib": 4224.6,
+    "mfma_busy_frac": 0.2033,
+    "valu_insts_per_mfma": 36.36,
+    "mfma_insts": 749984,
 }
 
 
@@ -93,14 +103,20 @@ def decode_sources_sha256():
     return sources_sha256(DECODE_SOURCES)
 
 
-def chunk_traffic_bytes():
-    """HBM bytes per chunk call of the union kernel from the recorded
-    counters, or None if its sources changed since they were taken."""
+def chunk_counters():
+    """HBM bytes per chunk call of the union kernel and its MFMA figures from
+    the recorded counters, or None if its sources changed since."""
     t = CHUNK_PMC_TRAFFIC
     if t["sources_sha256"] != sources_sha256(CHUNK_SOURCES):
         return None
     kib = t["fetch_kib"] * PMC_TRAFFIC["fetch_factor"] + t["write_kib"] * PMC_TRAFFIC["write_factor"]
-    return int(round(kib * 1024))
+    return {"traffic": int(round(kib * 1024)), "mfma_busy_frac": t["mfma_busy_frac"],
+            "valu_insts_per_mfma": t["valu_insts_per_mfma"], "mfma_insts": t["mfma_insts"]}
+
+
+def chunk_traffic_bytes():
+    c = chunk_counters()
+    return None if c is None else c["traffic"]
 
 
 def pmc_traffic_bytes(fp8=False):
@@ -370,7 +386,8 @@ def bench_chunk(args, NL=4, emit=True):
                      "unit": "TFLOP/s", "frac": round(exe / FP8_PEAK_TFLOPS, 4),
                      "traffic": chunk_traffic_bytes(), "kernel": "union_attn_kernel",
                      "us_per_launch": round(call_us, 3),
-                     "useful_tflops": round(use, 2)},
+                     "useful_tflops": round(use, 2),
+                     "counters": chunk_counters()},
     }
     if emit:
         print(json.dumps(result), flush=True)
