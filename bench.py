@@ -146,6 +146,120 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
 
 
+def bench_micro(args):
+    """Rates the decode path is measured against (libqas_micro.so): scattered
+    whole-tile reads in the attention kernel's load pattern (16 rows of 1 KiB
+    in flight per wave, 512 workgroups of 512 threads) against the same bytes
+    read in order, per buffer size and tile size; an empty kernel inside a HIP
+    graph; a chain of dependent global loads.  One JSON line."""
+    import ctypes
+
+    import torch
+
+    from query_aware_sparse_amd.build import MICRO_LIB
+    assert torch.cuda.is_available(), "bench.py --micro needs a GPU"
+    torch.cuda.set_device(0)
+    lib = ctypes.CDLL(MICRO_LIB)
+    P = ctypes.c_void_p
+    lib.qas_micro_read_tiles.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    lib.qas_micro_empty.argtypes = [P]
+    lib.qas_micro_chase.argtypes = [P, ctypes.c_int, P, P]
+    rng = np.random.default_rng(11)
+    n_wg = 512
+    sink = torch.zeros(n_wg, dtype=torch.int32, device="cuda")
+
+    def graph_us(launches, reps=20):
+        """Mean us per launch of a captured sequence, replayed `reps` times."""
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for fn in launches:
+                    fn(s.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+
+    read_bytes = 64 << 20          # bytes one launch reads (the attention's 64 MiB)
+    launches = 8                   # launches in a graph, each on its own tiles where room
+
+    def tiles(buf_bytes, tile, ordered):
+        n = read_bytes // tile
+        total = buf_bytes // tile
+        sets = []
+        for i in range(launches):
+            if ordered:
+                start = (i * n) % max(1, total - n + 1)
+                ids = np.arange(start, start + n, dtype=np.uint32)
+            elif total >= n * launches:
+                ids = rng.choice(total, n * launches, replace=False).astype(np.uint32)[i * n:(i + 1) * n]
+            else:
+                ids = rng.permutation(total)[:n].astype(np.uint32)
+            sets.append(torch.from_numpy(ids).cuda())
+        return sets
+
+    res = {"workload": "microbenchmarks (libqas_micro.so)", "read_bytes_per_launch": read_bytes,
+           "workgroups": n_wg, "reads": []}
+    cases = [(64 << 20, 4096), (512 << 20, 4096), (16 << 30, 4096), (16 << 30, 8192),
+             (16 << 30, 16384)]
+    bufs = {}
+    for buf_bytes, tile in cases:
+        if buf_bytes not in bufs:
+            bufs[buf_bytes] = torch.ones(buf_bytes // 4, dtype=torch.int32, device="cuda")
+        buf = bufs[buf_bytes]
+        for ordered in (False, True):
+            sets = tiles(buf_bytes, tile, ordered)
+            per = len(sets[0]) // n_wg
+            us = graph_us([lambda st, ids=ids: lib.qas_micro_read_tiles(
+                buf.data_ptr(), ids.data_ptr(), n_wg, per, tile, sink.data_ptr(), st)
+                for ids in sets])
+            entry = {"buffer_bytes": buf_bytes, "tile_bytes": tile,
+                     "order": "in order" if ordered else "scattered",
+                     "us_per_launch": round(us, 2),
+                     "TB/s": round(read_bytes / (us * 1e-6) / 1e12, 2)}
+            res["reads"].append(entry)
+            log(f"[micro] {buf_bytes >> 20} MiB buffer, {tile >> 10} KiB tiles, "
+                f"{entry['order']}: {us:.2f} us per 64 MiB, {entry['TB/s']} TB/s")
+    del bufs
+    torch.cuda.empty_cache()
+    # empty kernels back to back inside a graph
+    us = graph_us([lambda st: lib.qas_micro_empty(st) for _ in range(64)], reps=50)
+    res["empty_kernel_us_in_graph"] = round(us, 3)
+    log(f"[micro] empty kernel in a graph: {us:.3f} us each")
+    # dependent loads: one lane walks a random chain through 1 GiB (one slot per
+    # 4 KiB), a fresh chain per trial after 1 GiB of other reads, eager launch
+    slots = (1 << 30) // 4
+    hops = 2048
+    dev = torch.zeros(slots, dtype=torch.int32, device="cuda")
+    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    per_hop = []
+    for trial in range(3):
+        order = rng.permutation(slots // 1024)[:hops].astype(np.int64) * 1024
+        order = order[order != 0][:hops - 1]
+        chain = np.concatenate([[0], order])               # 0 -> order[0] -> ...
+        nxt = torch.from_numpy(np.roll(chain, -1).astype(np.int32)).cuda()
+        dev[torch.from_numpy(chain).cuda()] = nxt
+        torch.cuda.synchronize()
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.qas_micro_chase(dev.data_ptr(), len(chain), out.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+        e1.record()
+        torch.cuda.synchronize()
+        per_hop.append(e0.elapsed_time(e1) * 1e6 / len(chain))
+    res["dependent_load_ns"] = round(float(np.median(per_hop)), 1)
+    log(f"[micro] dependent global load, cold chain over 1 GiB: {res['dependent_load_ns']} ns each")
+    print(json.dumps(res), flush=True)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -710,6 +824,9 @@ def main():
                                            "config5"), default="all",
                     help="all: the headline line with every workload; the others time "
                          "one workload alone (profiling passes)")
+    ap.add_argument("--micro", action="store_true",
+                    help="only run the microbenchmarks of libqas_micro.so (read rates, "
+                         "kernel boundary, dependent loads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--no-next-rows", action="store_true",
@@ -725,6 +842,8 @@ def main():
         sys.exit("bench.py: --steps must be >= 1")
     if args.copy_calibration:
         return copy_calibration()
+    if args.micro:
+        return bench_micro(args)
     if args.workload == "chunk":
         args.chunk_steps = args.steps
         return bench_chunk(args, NL=4 if args.layers == 32 else args.layers)

@@ -16,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqas.so")
+MICRO_LIB = os.path.join(HERE, "libqas_micro.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -30,6 +31,8 @@ FLAGS = [
 
 SOURCES = ["qas_api.cpp", "append.hip", "append_fp8.hip", "score.hip", "topk.hip", "decode.hip", "decode_f32.hip",
            "decode_f16.hip", "decode_bf16.hip", "union.hip", "regroup.hip", "topr.hip"]
+# measurement kernels of bench.py --micro, in a library of their own
+MICRO_SOURCES = ["microbench.hip"]
 
 
 def _compile(src, verbose):
@@ -46,20 +49,27 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    """Compile every HIP source and link libqas.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    """Compile every HIP source, link libqas.so and the measurement library
+    libqas_micro.so (bench.py --micro); returns the libqas.so path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + MICRO_SOURCES
+    jobs = min(len(srcs), max(1, (os.cpu_count() or 2)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], MICRO_LIB, verbose)
     return LIB
 
 
