@@ -18,6 +18,9 @@
 // attention stage runs in a later kernel, so no synchronisation is needed.
 // The first workgroup of each request also zeroes the attention kernel's
 // split counters of that request.
+//
+// Grouped-query heads (g >= 2) with d = 128 and 16-bit records take
+// score_mfma_kernel instead: the same bound as a small GEMM on matrix cores.
 #include "qas_device.h"
 #include "qas_internal.h"
 
@@ -334,8 +337,211 @@ __global__ __launch_bounds__(512) void score8_kernel(ScoreArgs a) {
   }
 }
 
+// ---- grouped-query heads on matrix cores ----------------------------------
+// With G query heads per KV head the bound is a small GEMM.  Writing
+// max(q m, q M) = min(q, 0) m + max(q, 0) M (exact: one of the two products
+// is a product with zero), U_i = sum_k A[i][k] B[k][j] with A the sign-split
+// query rows [min(q_i, 0) | max(q_i, 0)] (16 x 256, rows i >= G zero) and B
+// the stored records [min | max] of 16 pages (256 x 16): eight
+// v_mfma_f32_16x16x32 steps per 16 pages, the products exact and summed in
+// fp32, as the VALU kernel does.  The group max is then a max over the G
+// output rows of each page column.
+//
+// Operand lanes (16x16x32 layout: A lane l holds row l % 16, k = 8 (l / 16)
+// + [0, 8) of the step; B lane l holds those k of column l % 16): k step s
+// covers bytes [64 s + 16 (l / 16), +16) of a page's record, so lane l takes
+// record element 32 s + 8 (l / 16) + e - a min for s < 4, the max of dim
+// 32 (s - 4) + 8 (l / 16) + e for s >= 4 - and the query row's matching
+// dims.  Loaded that way, every 16 consecutive lanes would touch 16 records;
+// instead each load instruction reads two whole records (lane l: record
+// 2 s + l / 32, bytes 16 (l % 32) + [0, 16)), and the wave turns them into
+// the operand layout through a private LDS tile (records 33 16-byte units
+// apart, so both the writes and the operand reads are free of bank
+// conflicts).  A task is 16 consecutive pages of one KV head; a workgroup
+// of 4 waves owns ng * 16 pages of one row, every KV head of them, and each
+// wave keeps T = 2 tasks' records (8 KiB each) in flight.  Small workgroups
+// with two tasks per wave measured faster than 8 waves or 4 tasks per wave
+// (more workgroups resident per CU, shorter tails).  Tasks go round-robin
+// over the waves with the head varying fastest, so the waves read
+// neighbouring heads of the same pages (one page's heads are contiguous)
+// and, when H_kv divides the wave count, every task of a wave has one head
+// whose query operands are loaded once.
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaTasks = 2;          // tasks in flight per wave
+constexpr int kMfmaD = 128;
+constexpr int kMfmaUnits = 33;         // LDS record stride in 16-byte units
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+template <int DT>
+__device__ __forceinline__ float4_t mfma_16x16x32(const uint4& a, const uint4& b,
+                                                  const float4_t& c) {
+  if constexpr (DT == kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Sign split of eight 16-bit floats: neg keeps the elements whose sign bit
+// is set (min(x, 0), up to the sign of zero), pos the others (max(x, 0)).
+__device__ __forceinline__ void sign_split(const uint4& x, uint4& neg, uint4& pos) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t n[4], p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = ((w[i] >> 15) & 0x00010001u) * 0xFFFFu;
+    n[i] = w[i] & m;
+    p[i] = w[i] & ~m;
+  }
+  neg = make_uint4(n[0], n[1], n[2], n[3]);
+  pos = make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// A operands of KV head h for this lane: its query row (lane % 16; zero when
+// it is not one of the G rows), split by sign into the 8 k steps.
+template <int G>
+__device__ __forceinline__ void load_a(const ScoreArgs& a, int r, int h, int col, int quad,
+                                       uint4* A) {
+  uint4 raw[4];
+  const int i = col < G ? col : 0;
+  const char* q = reinterpret_cast<const char*>(a.q) +
+                  (((size_t)r * a.H_q + h * G + i) * kMfmaD) * 2 + quad * 16;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) raw[s] = load16(q + s * 64);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (col >= G) raw[s] = make_uint4(0, 0, 0, 0);
+    sign_split(raw[s], A[s], A[s + 4]);
+  }
+}
+
+template <int DT, int G, bool ONE_HEAD>
+__global__ __launch_bounds__(kMfmaWaves * kWave) void score_mfma_kernel(ScoreArgs a, int ng) {
+  constexpr int D = kMfmaD;
+  constexpr int T = kMfmaTasks;
+  constexpr int BYTES = 2;
+  static_assert(DType<DT>::bytes == BYTES, "16-bit records");
+  __shared__ uint4 tile[kMfmaWaves][16 * kMfmaUnits];
+
+  const int r = blockIdx.y;
+  const int H = a.H_kv;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int col = lane & 15, quad = lane >> 4;
+  const int half = lane >> 5, unit = lane & 31;   // load layout: record 2 s + half
+  const int ntasks = H * ng;
+  const int j0 = blockIdx.x * 16 * ng;
+
+  const int req = r / a.gamma;                // request of the row (draft positions)
+  const int pbeg = a.page_indptr[req];
+  const int P_r = a.page_indptr[req + 1] - pbeg;
+  const int L = a.seq_lens[req] - (a.gamma - 1 - r % a.gamma);
+  if (a.tickets && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < H; i += blockDim.x) a.tickets[(size_t)r * H + i] = 0u;
+  if (j0 >= P_r) return;
+  const int n_used = L > 0 ? min((L + a.S - 1) / a.S, P_r) : 0;
+  const int tail = n_used - 1;
+  const int jlast = max(n_used, 1) - 1;
+  const bool appending = a.k_new != nullptr && L > 0;
+  const int off = appending ? (L - 1) % a.S : 0;
+  const int lim = a.row_stride ? min(P_r, a.row_stride) : P_r;   // stay inside the row
+  const char* sum_base = reinterpret_cast<const char*>(a.summary);
+  uint4* my = tile[w];
+
+  uint4 A1[8];
+  if constexpr (ONE_HEAD) load_a<G>(a, r, w % H, col, quad, A1);
+
+  for (int t0 = w; t0 < ntasks; t0 += kMfmaWaves * T) {
+    // page table, then records: every load unconditional (tasks past the
+    // end repeat the last one, pages past the used ones are clamped to a
+    // page of the request, and their results are dropped)
+    int hh[T], jj[T], pp[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      const int t = min(t0 + u * kMfmaWaves, ntasks - 1);
+      hh[u] = t % H;
+      jj[u] = j0 + 16 * (t / H) + col;
+      pp[u] = a.page_indices[pbeg + min(jj[u], jlast)];
+    }
+    uint4 raw[T][8];
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int pj = __shfl(pp[u], 2 * s + half, kWave);   // lane j < 16 holds page j
+        raw[u][s] = load16(sum_base + (((size_t)pj * H + hh[u]) * 2 * D) * BYTES + unit * 16);
+      }
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      // transpose through the wave's LDS tile into the operand layout
+      uint4 b[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) my[(2 * s + half) * kMfmaUnits + unit] = raw[u][s];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) b[s] = my[col * kMfmaUnits + 4 * s + quad];
+      const bool valid = t0 + u * kMfmaWaves < ntasks;
+      // fused append on the tail page's four lanes: K/V row, then min/max
+      // (the token alone when it opens the page: the -inf/+inf start)
+      if (appending && valid && jj[u] == tail) {
+        const int h = hh[u];
+        const size_t o = (((size_t)r * H + h) * D) * BYTES + quad * 16;
+        const char* kn = reinterpret_cast<const char*>(a.k_new) + o;
+        const char* vn = reinterpret_cast<const char*>(a.v_new) + o;
+        char* sum = reinterpret_cast<char*>(a.summary) +
+                    (((size_t)pp[u] * H + h) * 2 * D) * BYTES + quad * 16;
+        const size_t row = ((((size_t)pp[u] * H + h) * a.S + off) * D) * BYTES + quad * 16;
+        char* kr = reinterpret_cast<char*>(a.k_pool) + row;
+        char* vr = reinterpret_cast<char*>(a.v_pool) + row;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint4 kw = load16(kn + s * 64), vw = load16(vn + s * 64);
+          b[s] = off == 0 ? kw : minmax16<DT, false>(b[s], kw);
+          b[s + 4] = off == 0 ? kw : minmax16<DT, true>(b[s + 4], kw);
+          *reinterpret_cast<uint4*>(sum + s * 64) = b[s];
+          *reinterpret_cast<uint4*>(sum + D * BYTES + s * 64) = b[s + 4];
+          *reinterpret_cast<uint4*>(kr + s * 64) = kw;
+          *reinterpret_cast<uint4*>(vr + s * 64) = vw;
+        }
+      }
+      uint4 At[8];
+      if constexpr (!ONE_HEAD) load_a<G>(a, r, hh[u], col, quad, At);
+      const uint4* A = ONE_HEAD ? A1 : At;
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) acc = mfma_16x16x32<DT>(A[s], b[s], acc);
+      // lane l holds rows 4 (l / 16) + [0, 4) of page column l % 16
+      float best = acc[0];
+#pragma unroll
+      for (int i = 1; i < (G < 4 ? G : 4); ++i) best = fmaxf(best, acc[i]);
+      if constexpr (G == 8) best = fmaxf(best, __shfl_xor(best, 16, kWave));
+      const int j = jj[u];
+      if (quad == 0 && valid && j < lim) {
+        float* srow = a.row_stride ? a.scores + ((size_t)r * H + hh[u]) * a.row_stride
+                                   : a.scores + (size_t)pbeg * H + (size_t)hh[u] * P_r;
+        srow[j] = j < n_used ? best : -INFINITY;
+        if (a.phys_out && hh[u] == 0) a.phys_out[(size_t)r * a.row_stride + j] = pp[u];
+      }
+    }
+  }
+}
+
 template <int DT, int D, int G>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
+  if constexpr (D == kMfmaD && G >= 2 && DT != kF32) {
+    if (!a.summary_fp8) {
+      const int per = kMfmaWaves * kMfmaTasks;          // tasks of one pass of the waves
+      const int ng = a.H_kv >= per ? 1 : per / a.H_kv;  // 16-page groups per workgroup
+      dim3 grid((a.max_pages + 16 * ng - 1) / (16 * ng), a.B);
+      if (kMfmaWaves % a.H_kv == 0)
+        hipLaunchKernelGGL((score_mfma_kernel<DT, G, true>), grid, dim3(kMfmaWaves * kWave), 0, s,
+                           a, ng);
+      else
+        hipLaunchKernelGGL((score_mfma_kernel<DT, G, false>), grid, dim3(kMfmaWaves * kWave), 0,
+                           s, a, ng);
+      return hipGetLastError();
+    }
+  }
   if (a.summary_fp8) {
     const int lanes_pp = a.H_kv * (D / 16);
     const int threads = lanes_pp * a.pages_per_iter;

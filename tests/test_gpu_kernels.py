@@ -46,6 +46,14 @@ SCORE_CASES = {
     "stress_long_context-small": lambda: stress_long_context(B=2, L=4096, H_q=8, H_kv=2),
     "d64-bf16-g8": lambda: batched_gqa_append(B=2, L_min=100, L_max=700, H_q=16, H_kv=2, d=64,
                                    S=32, steps=0),
+    # matrix-core scores (d=128, 16-bit, g >= 2): g=8 joins two output
+    # quads; 3 and 16 KV heads do not divide the 8 waves, so the query
+    # operands change from task to task and tasks past the end are dropped
+    "d128-f16-g8": lambda: stress_long_context(B=2, L=3001, H_q=16, H_kv=2),
+    "d128-bf16-g2-h3": lambda: batched_gqa_append(B=3, L_min=200, L_max=1700, H_q=6, H_kv=3,
+                                                  steps=0),
+    "d128-bf16-g2-h16": lambda: batched_gqa_append(B=2, L_min=40, L_max=900, H_q=32, H_kv=16,
+                                                   steps=0),
 }
 
 
