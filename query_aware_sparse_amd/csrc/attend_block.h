@@ -7,7 +7,9 @@
 // token rows of the staged pages (a page contributes its first ntok rows);
 // the partial softmax states of the splits of a row are merged by
 // log-sum-exp (the QuantSpec post's flash-decoding chunk merge), and an
-// empty support gives out = 0 and lse = -inf.
+// empty support gives out = 0 and lse = -inf.  Groups of 4 or 8 query heads
+// with 16-bit K/V take attend_split_mfma (at the end of this file), whose
+// logits come from matrix cores; both end in attend_finish.
 //
 // Execution.  The workgroup's waves stream "token groups" (TPI token rows of
 // one page = one 16-byte load per lane for K and one for V), UNR groups per
@@ -84,6 +86,111 @@ struct AttendOut {
   int n_split, split;
 };
 
+// Merge of the lanes' online-softmax states (m_run, l_run, acc[G][epl]: lane
+// lane % (D / epl) holds dims [epl * that, +epl) of each query head's
+// accumulator) over the workgroup's waves, then over the row's splits, and
+// the output.  Every thread of the workgroup must call this.
+template <int DT, int D, int G, int NW>
+__device__ __forceinline__ void attend_finish(float* m_run, float* l_run,
+                                              float (*acc)[epl<DT>()], const AttendOut& o) {
+  using namespace attend_detail;
+  constexpr int NT = NW * kWave;
+  constexpr int EPL = epl<DT>();
+  constexpr int RL = D / EPL;                 // lanes per token row
+  __shared__ float red_m[NW][G];
+  __shared__ float red_l[NW][G];
+  __shared__ float red_acc[NW][G][D];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int c = lane % RL;
+
+  // ---- merge lanes of one dim chunk, then the waves ------------------------
+#pragma unroll
+  for (int off = RL; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float m2 = shfl_xor_f(m_run[gg], off);
+      const float l2 = shfl_xor_f(l_run[gg], off);
+      float acc2[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc2[e] = shfl_xor_f(acc[gg][e], off);
+      merge_state<EPL>(m_run[gg], l_run[gg], acc[gg], m2, l2, acc2);
+    }
+  }
+  if (lane < RL) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      if (lane == 0) {
+        red_m[wave][gg] = m_run[gg];
+        red_l[wave][gg] = l_run[gg];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red_acc[wave][gg][c * EPL + e] = acc[gg][e];
+    }
+  }
+  __syncthreads();
+  const bool single = o.n_split == 1;
+  for (int t = tid; t < G * D; t += NT) {
+    const int gg = t / D, dim = t - (t / D) * D;
+    float m = -INFINITY, l = 0.f, ov = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float one[1] = {red_acc[w][gg][dim]};
+      merge_state<1>(m, l, &ov, red_m[w][gg], red_l[w][gg], one);
+    }
+    const size_t rowq = o.rowq0 + gg;
+    if (single) {
+      store_rn<DT>(o.out, rowq * D + dim, m == -INFINITY ? 0.f : ov / l);
+      if (dim == 0 && o.lse)
+        o.lse[rowq] = m == -INFINITY ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
+      continue;
+    }
+    float* part = o.partials + (rowq * o.n_split + o.split) * (D + 2);
+    if (dim == 0) {
+      store_coherent(part, m);
+      store_coherent(part + 1, l);
+    }
+    store_coherent(part + 2 + dim, ov);
+  }
+  if (single) return;
+
+  // ---- the last split of the row merges all split states -----------------
+  __builtin_amdgcn_s_waitcnt(0);             // this thread's states are stored
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(o.ticket, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(o.n_split - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  constexpr int MB = 16;
+  for (int t = tid; t < G * D; t += NT) {
+    const int gg = t / D, dim = t - (t / D) * D;
+    const size_t rowq = o.rowq0 + gg;
+    const float* part = o.partials + rowq * o.n_split * (D + 2);
+    float M = -INFINITY, lsum = 0.f, ov = 0.f;
+    for (int sb = 0; sb < o.n_split; sb += MB) {
+      float ms[MB], ls[MB], os[MB];
+#pragma unroll
+      for (int k = 0; k < MB; ++k) {
+        const int sp = sb + k;
+        const bool in = sp < o.n_split;
+        ms[k] = in ? load_coherent(part + sp * (D + 2)) : -INFINITY;
+        ls[k] = in ? load_coherent(part + sp * (D + 2) + 1) : 0.f;
+        os[k] = in ? load_coherent(part + sp * (D + 2) + 2 + dim) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < MB; ++k) merge_state<1>(M, lsum, &ov, ms[k], ls[k], &os[k]);
+    }
+    store_rn<DT>(o.out, rowq * D + dim, M == -INFINITY ? 0.f : ov / lsum);
+    if (dim == 0 && o.lse)
+      o.lse[rowq] = M == -INFINITY ? -INFINITY : (M + log2f(lsum)) * 0.6931471805599453f;
+  }
+  // leave the counter at zero for the next call
+  if (tid == 0) __hip_atomic_store(o.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The workgroup (NW waves) attends over npg pages staged in s_phys / s_ntok
 // (physical page, token rows to read).  qraw holds this
 // lane's 16-byte chunk (lane % (D / epl)) of each query head of the group.
@@ -96,15 +203,10 @@ __device__ __forceinline__ void attend_split(const int* s_phys, const int* s_nto
                                              const uint4* qraw, float sm_scale,
                                              const AttendOut& o) {
   using namespace attend_detail;
-  constexpr int NT = NW * kWave;
   constexpr int EPL = epl<DT>();
   constexpr int RL = D / EPL;                 // lanes per token row
   constexpr int TPI = kWave / RL;             // token rows per wave load
   constexpr int BYTES = DType<DT>::bytes;
-  __shared__ float red_m[NW][G];
-  __shared__ float red_l[NW][G];
-  __shared__ float red_acc[NW][G][D];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int c = lane % RL;
@@ -194,91 +296,154 @@ __device__ __forceinline__ void attend_split(const int* s_phys, const int* s_nto
     }
   }
 
-  // ---- merge lanes of one dim chunk, then the waves ------------------------
-#pragma unroll
-  for (int off = RL; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float m2 = shfl_xor_f(m_run[gg], off);
-      const float l2 = shfl_xor_f(l_run[gg], off);
-      float acc2[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc2[e] = shfl_xor_f(acc[gg][e], off);
-      merge_state<EPL>(m_run[gg], l_run[gg], acc[gg], m2, l2, acc2);
-    }
-  }
-  if (lane < RL) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      if (lane == 0) {
-        red_m[wave][gg] = m_run[gg];
-        red_l[wave][gg] = l_run[gg];
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red_acc[wave][gg][c * EPL + e] = acc[gg][e];
-    }
-  }
-  __syncthreads();
-  const bool single = o.n_split == 1;
-  for (int t = tid; t < G * D; t += NT) {
-    const int gg = t / D, dim = t - (t / D) * D;
-    float m = -INFINITY, l = 0.f, ov = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float one[1] = {red_acc[w][gg][dim]};
-      merge_state<1>(m, l, &ov, red_m[w][gg], red_l[w][gg], one);
-    }
-    const size_t rowq = o.rowq0 + gg;
-    if (single) {
-      store_rn<DT>(o.out, rowq * D + dim, m == -INFINITY ? 0.f : ov / l);
-      if (dim == 0 && o.lse)
-        o.lse[rowq] = m == -INFINITY ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
-      continue;
-    }
-    float* part = o.partials + (rowq * o.n_split + o.split) * (D + 2);
-    if (dim == 0) {
-      store_coherent(part, m);
-      store_coherent(part + 1, l);
-    }
-    store_coherent(part + 2 + dim, ov);
-  }
-  if (single) return;
+  attend_finish<DT, D, G, NW>(m_run, l_run, acc, o);
+}
 
-  // ---- the last split of the row merges all split states -----------------
-  __builtin_amdgcn_s_waitcnt(0);             // this thread's states are stored
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(o.ticket, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (unsigned)(o.n_split - 1);
+// ---- grouped-query heads on matrix cores ----------------------------------
+// With G >= 4 query heads per KV head, the logits of a 16-token tile are a
+// small GEMM: D[i][t] = q_i . k_t over d = 128, four v_mfma_f32_16x16x32
+// steps (rows i >= G of the query operand are zero).  Products are exact and
+// summed in fp32; the logit is then scaled by sm_scale * log2(e) in fp32 (the
+// VALU stream scales the query first: the two differ by fp32 rounding only).
+// The value side stays on the VALU in the row layout of attend_split, so the
+// lanes' online-softmax states, and attend_finish, are the same: lane l
+// (row 4 j + l / 16 of the tile's load j, dims 8 (l % 16) + [0, 8)) fetches
+// the logit of its row and head from the lane that holds it in the MFMA
+// output (lane 16 (i / 4) + t, register i % 4) with a cross-lane read.
+//
+// Operand lanes (16x16x32: A lane l holds row l % 16, k = 8 (l / 16) + [0, 8)
+// of the step; B lane l those k of column l % 16): K step s of lane l reads
+// bytes [64 s + 16 (l / 16), +16) of tile row l % 16, so each load covers
+// 64 contiguous bytes of every row of the 4 KiB tile.  A tile never crosses
+// a page (S is a multiple of 16 here), so no row address is clamped: rows
+// past the page's tokens are read and their logits and values dropped.
+
+// Query operand of the group for attend_split_mfma: lane l takes head row
+// l % 16 of the group (zero for rows >= G), dims 32 s + 8 (l / 16) + [0, 8)
+// in qa[s].  qrow: the group's first query head, 128 16-bit values per head.
+template <int G>
+__device__ __forceinline__ void load_q_operand(const char* qrow, uint4* qa) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, quad = lane >> 4;
+  const char* q = qrow + (size_t)(i < G ? i : 0) * 256 + quad * 16;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qa[s] = load16(q + 64 * s);
+    if (i >= G) qa[s] = make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
-  if (!s_last) return;
-  constexpr int MB = 16;
-  for (int t = tid; t < G * D; t += NT) {
-    const int gg = t / D, dim = t - (t / D) * D;
-    const size_t rowq = o.rowq0 + gg;
-    const float* part = o.partials + rowq * o.n_split * (D + 2);
-    float M = -INFINITY, lsum = 0.f, ov = 0.f;
-    for (int sb = 0; sb < o.n_split; sb += MB) {
-      float ms[MB], ls[MB], os[MB];
+}
+
+typedef __bf16 attend_bf16x8_t __attribute__((ext_vector_type(8)));
+
+template <int DT>
+__device__ __forceinline__ float4_t attend_mfma(const uint4& a, const uint4& b,
+                                                const float4_t& c) {
+  if constexpr (DT == kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attend_bf16x8_t, a),
+                                                   __builtin_bit_cast(attend_bf16x8_t, b), c, 0,
+                                                   0, 0);
+}
+
+// As attend_split, for DT f16/bf16, d = 128, G in {4, 8} and S a multiple of
+// 16; UT tiles of 16 rows per wave in flight.  qa: load_q_operand's registers.
+template <int DT, int G, int UT, int NW>
+__device__ __forceinline__ void attend_split_mfma(const int* s_phys, const int* s_ntok, int npg,
+                                                  int S, const char* kbase, const char* vbase,
+                                                  size_t pstride, uint32_t hoff_head,
+                                                  const uint4* qa, float sm_scale,
+                                                  const AttendOut& o) {
+  constexpr int D = 128;
+  constexpr int EPL = 8;
+  constexpr int ROW = D * 2;                  // bytes of a token row
+  static_assert(DType<DT>::bytes == 2 && (G == 4 || G == 8), "16-bit K/V, 4 or 8 heads");
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int col = lane & 15, quad = lane >> 4;   // K operand: tile row, k quarter
+  const int c = lane & 15, trow = lane >> 4;     // V: dim chunk, row of a load
+  const int TPP = S >> 4;                     // tiles per page (a power of two)
+  const int ltp = __ffs(TPP) - 1;
+  const int units = npg * TPP;
+  const float qscale = sm_scale * kLog2e;     // logits in log2 units
+  float m_run[G], l_run[G], acc[G][EPL];
 #pragma unroll
-      for (int k = 0; k < MB; ++k) {
-        const int sp = sb + k;
-        const bool in = sp < o.n_split;
-        ms[k] = in ? load_coherent(part + sp * (D + 2)) : -INFINITY;
-        ls[k] = in ? load_coherent(part + sp * (D + 2) + 1) : 0.f;
-        os[k] = in ? load_coherent(part + sp * (D + 2) + 2 + dim) : 0.f;
-      }
+  for (int gg = 0; gg < G; ++gg) {
+    m_run[gg] = -INFINITY;
+    l_run[gg] = 0.f;
 #pragma unroll
-      for (int k = 0; k < MB; ++k) merge_state<1>(M, lsum, &ov, ms[k], ls[k], &os[k]);
+    for (int e = 0; e < EPL; ++e) acc[gg][e] = 0.f;
+  }
+
+  for (int u0 = wave; u0 < units; u0 += NW * UT) {
+    // Every load is unconditional: a tile past the end repeats the last one
+    // and its rows are dropped.  K first, so the logits start while V is in
+    // flight.
+    size_t tb[UT];
+    int nrow[UT];
+#pragma unroll
+    for (int b = 0; b < UT; ++b) {
+      const int u = min(u0 + b * NW, units - 1);
+      const int pi = u >> ltp, ti = u & (TPP - 1);
+      nrow[b] = u0 + b * NW < units ? s_ntok[pi] - 16 * ti : 0;   // rows kept: t < nrow
+      tb[b] = (size_t)(uint32_t)s_phys[pi] * pstride + (hoff_head + (uint32_t)(16 * ti * ROW));
     }
-    store_rn<DT>(o.out, rowq * D + dim, M == -INFINITY ? 0.f : ov / lsum);
-    if (dim == 0 && o.lse)
-      o.lse[rowq] = M == -INFINITY ? -INFINITY : (M + log2f(lsum)) * 0.6931471805599453f;
+    uint4 kr[UT][4], vr[UT][4];
+#pragma unroll
+    for (int b = 0; b < UT; ++b)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kr[b][s] = load16(kbase + tb[b] + (col * ROW + 64 * s + 16 * quad));
+#pragma unroll
+    for (int b = 0; b < UT; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vr[b][j] = load16(vbase + tb[b] + ((4 * j + trow) * ROW + 16 * c));
+    float4_t lg[UT];
+#pragma unroll
+    for (int b = 0; b < UT; ++b) {
+      lg[b] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) lg[b] = attend_mfma<DT>(qa[s], kr[b][s], lg[b]);
+    }
+    // every head's logits and new running max first, then each V row is
+    // unpacked once and added to every head's accumulator
+    float z[G][UT][4], zm[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      float zmax = m_run[gg];
+#pragma unroll
+      for (int b = 0; b < UT; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float dot = __shfl(lg[b][gg & 3], 16 * (gg >> 2) + 4 * j + trow, kWave);
+          z[gg][b][j] = 4 * j + trow < nrow[b] ? dot * qscale : -INFINITY;
+          zmax = fmaxf(zmax, z[gg][b][j]);
+        }
+      // as in attend_split: no branch on the batch's content
+      zm[gg] = zmax == -INFINITY ? 0.f : zmax;
+      const float alpha = fast_exp2(m_run[gg] - zm[gg]);
+      l_run[gg] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[gg][e] *= alpha;
+      m_run[gg] = zmax;
+    }
+#pragma unroll
+    for (int b = 0; b < UT; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = 4 * j + trow < nrow[b];
+        const uint4 w = ok ? vr[b][j] : make_uint4(0, 0, 0, 0);
+        float vf[EPL];
+        unpack16<DT>(w, vf);
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float p = ok ? fast_exp2(z[gg][b][j] - zm[gg]) : 0.f;
+          l_run[gg] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[gg][e] += p * vf[e];
+        }
+      }
   }
-  // leave the counter at zero for the next call
-  if (tid == 0) __hip_atomic_store(o.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  attend_finish<DT, D, G, NW>(m_run, l_run, acc, o);
 }
 
 }  // namespace qas

@@ -62,12 +62,13 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* scratch, int* to
 }
 
 // TPT = 0: the caller's lists; TPT > 0: select the top-K pages in the
-// workgroup from the page scores, TPT scores per thread at most.
-template <int DT, int D, int G, int TPT>
+// workgroup from the page scores, TPT scores per thread at most.  MF: the
+// logits on matrix cores (attend_split_mfma; 16-bit K/V, d = 128, 4 or 8
+// query heads per KV head, S >= 16).
+template <int DT, int D, int G, int TPT, bool MF>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   constexpr int EPL = epl<DT>();
   constexpr int RL = D / EPL;                 // lanes per token row
-  constexpr int TPI = kWave / RL;             // token rows per wave load
   constexpr int BYTES = DType<DT>::bytes;
   extern __shared__ int s_row[];              // staged row prefix (dedupe only)
   __shared__ int s_phys[kDecMaxList];
@@ -86,13 +87,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   if constexpr (TPT > 0)
     t.issue_x4(a.scores + ((size_t)r * H + h) * a.score_stride,
                a.phys_rows + (size_t)r * a.score_stride, cap);
-  // this lane's 16-byte slice of each query head of the group, loaded now so
-  // that it lands during the selection instead of before the K/V stream
-  uint4 qraw[G];
+  // this lane's 16-byte slice of each query head of the group (or its query
+  // operand for the matrix cores), loaded now so that it lands during the
+  // selection instead of before the K/V stream
+  uint4 qraw[MF ? 4 : G];
+  if constexpr (MF) {
+    load_q_operand<G>(reinterpret_cast<const char*>(a.q) + ((size_t)r * a.H_q + h * G) * D * BYTES,
+                      qraw);
+  } else {
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg)
-    qraw[gg] = load16(reinterpret_cast<const char*>(a.q) +
-                      (((size_t)r * a.H_q + h * G + gg) * D + (lane % RL) * EPL) * BYTES);
+    for (int gg = 0; gg < G; ++gg)
+      qraw[gg] = load16(reinterpret_cast<const char*>(a.q) +
+                        (((size_t)r * a.H_q + h * G + gg) * D + (lane % RL) * EPL) * BYTES);
+  }
   // row r: a request, or draft position r % gamma of request r / gamma whose
   // causal limit is its own position (length seq_lens - (gamma - 1 - i))
   const int req = r / a.gamma;
@@ -178,10 +185,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   o.rowq0 = (size_t)r * a.H_q + h * G;
   o.n_split = a.n_split;
   o.split = split;
-  attend_split<DT, D, G, dec_unroll<DT, G>(), kDecWaves>(
-      s_phys, s_ntok, npg, S, reinterpret_cast<const char*>(a.k_pool),
-      reinterpret_cast<const char*>(a.v_pool), (size_t)H * S * D * BYTES,
-      (uint32_t)(h * S * D * BYTES), qraw, a.sm_scale, o);
+  if constexpr (MF)
+    attend_split_mfma<DT, G, G == 4 ? 2 : 1, kDecWaves>(
+        s_phys, s_ntok, npg, S, reinterpret_cast<const char*>(a.k_pool),
+        reinterpret_cast<const char*>(a.v_pool), (size_t)H * S * D * BYTES,
+        (uint32_t)(h * S * D * BYTES), qraw, a.sm_scale, o);
+  else
+    attend_split<DT, D, G, dec_unroll<DT, G>(), kDecWaves>(
+        s_phys, s_ntok, npg, S, reinterpret_cast<const char*>(a.k_pool),
+        reinterpret_cast<const char*>(a.v_pool), (size_t)H * S * D * BYTES,
+        (uint32_t)(h * S * D * BYTES), qraw, a.sm_scale, o);
+}
+
+// The matrix-core stream where it applies (16-bit K/V, d = 128, g = 4 or 8,
+// pages of at least 16 tokens), else the VALU stream.
+template <int DT, int D, int G, int TPT>
+void launch_kernel(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  if constexpr (DT != kF32 && D == 128 && (G == 4 || G == 8)) {
+    if (a.S >= 16) {
+      hipLaunchKernelGGL((decode_kernel<DT, D, G, TPT, true>), grid, dim3(kDecThreads), lds, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<DT, D, G, TPT, false>), grid, dim3(kDecThreads), lds, s, a);
 }
 
 template <int DT, int D, int G>
@@ -189,14 +215,14 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.H_kv, a.B);
   if (a.scores) {
     if (a.max_pages <= kDecThreads * 4)
-      hipLaunchKernelGGL((decode_kernel<DT, D, G, 4>), grid, dim3(kDecThreads), 0, s, a);
+      launch_kernel<DT, D, G, 4>(a, grid, 0, s);
     else if (a.max_pages <= kDecThreads * kDecFusedTopkPT)
-      hipLaunchKernelGGL((decode_kernel<DT, D, G, kDecFusedTopkPT>), grid, dim3(kDecThreads), 0, s, a);
+      launch_kernel<DT, D, G, kDecFusedTopkPT>(a, grid, 0, s);
     else
       return hipErrorInvalidValue;
   } else {
     const size_t lds = a.dedupe ? (size_t)a.sel_len * sizeof(int) : 0;
-    hipLaunchKernelGGL((decode_kernel<DT, D, G, 0>), grid, dim3(kDecThreads), lds, s, a);
+    launch_kernel<DT, D, G, 0>(a, grid, lds, s);
   }
   return hipGetLastError();
 }

@@ -47,8 +47,9 @@ SCORE_CASES = {
     "d64-bf16-g8": lambda: batched_gqa_append(B=2, L_min=100, L_max=700, H_q=16, H_kv=2, d=64,
                                    S=32, steps=0),
     # matrix-core scores (d=128, 16-bit, g >= 2): g=8 joins two output
-    # quads; 3 and 16 KV heads do not divide the 8 waves, so the query
-    # operands change from task to task and tasks past the end are dropped
+    # quads; 2 KV heads divide the kernel's 4 waves (one head per wave),
+    # 3 and 16 do not, so the query operands change from task to task and
+    # tasks past the end are dropped
     "d128-f16-g8": lambda: stress_long_context(B=2, L=3001, H_q=16, H_kv=2),
     "d128-bf16-g2-h3": lambda: batched_gqa_append(B=3, L_min=200, L_max=1700, H_q=6, H_kv=3,
                                                   steps=0),
@@ -232,6 +233,14 @@ SPARSE_CASES = {
     "llama2_7b_layer-small": lambda: llama2_7b_layer(L=5000, H=4, K=40),
     "batched_gqa_append-small": lambda: batched_gqa_append(B=3, L_min=900, L_max=3000, steps=0, K=37),
     "stress_long_context-small": lambda: stress_long_context(B=4, L=6000, H_q=8, H_kv=2, K=12),
+    # logits on matrix cores (16-bit K/V, d=128, g = 4 or 8, S >= 16), with
+    # partial last pages and tiles past a page's tokens
+    "g8-f16-S32": lambda: stress_long_context(B=3, L=5001, H_q=16, H_kv=2, K=14),
+    "g8-bf16-S16": lambda: batched_gqa_append(B=3, L_min=700, L_max=2600, H_q=16, H_kv=2,
+                                              steps=0, K=29),
+    "g4-bf16-S64": lambda: batched_gqa_append(B=2, L_min=1500, L_max=4000, H_q=8, H_kv=2, S=64,
+                                              steps=0, K=9),
+    "g4-f16-S256": lambda: stress_long_context(B=2, L=3001, H_q=8, H_kv=2, S=256, K=3),
 }
 
 

@@ -185,14 +185,16 @@ def test_batched_gqa_with_append(qas):
         assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
 
 
-@pytest.mark.parametrize("S", [1, 2, 8, 64, 128, 256])
-def test_page_sizes(qas, S):
+@pytest.mark.parametrize("S,H_q", [(1, 4), (2, 4), (8, 4), (64, 4), (128, 4), (256, 4),
+                                   (8, 8), (16, 8), (64, 16), (256, 8)])
+def test_page_sizes(qas, S, H_q):
     """Page sizes beyond the workloads' 4, 16 and 32, up to the largest the
     library takes: decode-layer calls with one append each (S = 1: every
     token opens a page; S = 256: 64 KiB of K per page and head), checked
-    against the oracle, and every summary after the last append."""
-    case = batched_gqa_append(seed=60 + S, B=2, L_min=1100, L_max=2100, H_q=4, H_kv=2, d=128,
-                              S=S, K=max(2, 256 // S), steps=3)
+    against the oracle, and every summary after the last append.  Groups of
+    4 and 8 query heads take the matrix-core logits from S = 16 on."""
+    case = batched_gqa_append(seed=60 + S + H_q, B=2, L_min=1100, L_max=2100, H_q=H_q, H_kv=2,
+                              d=128, S=S, K=max(2, 256 // S), steps=3)
     say(f"[e2e] page size {S}: lengths={case.seq_lens.tolist()} K={case.K}")
     lay = Layer(qas, case)
     decoded = {r: oracle.decoded_kv(case, r) for r in range(case.B)}
