@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   o.n_split = a.n_split;
   o.split = split;
   if constexpr (MF)
-    attend_split_mfma<DT, G, G == 4 ? 2 : 1, kDecWaves>(
+    attend_split_mfma<DT, G, kDecWaves>(
         s_phys, s_ntok, npg, S, reinterpret_cast<const char*>(a.k_pool),
         reinterpret_cast<const char*>(a.v_pool), (size_t)H * S * D * BYTES,
         (uint32_t)(h * S * D * BYTES), qraw, a.sm_scale, o);
