@@ -399,22 +399,25 @@ __device__ __forceinline__ void sign_split(const uint4& x, uint4& neg, uint4& po
   pos = make_uint4(p[0], p[1], p[2], p[3]);
 }
 
-// A operands of KV head h for this lane: its query row (lane % 16; zero when
-// it is not one of the G rows), split by sign into the 8 k steps.
+// This lane's query row (lane % 16; row 0 when it is not one of the G rows,
+// zeroed by split_a) of KV head h: dims 32 s + 8 (lane / 16) + [0, 8) in
+// raw[s], s < 4.
 template <int G>
-__device__ __forceinline__ void load_a(const ScoreArgs& a, int r, int h, int col, int quad,
-                                       uint4* A) {
-  uint4 raw[4];
+__device__ __forceinline__ void load_q_rows(const ScoreArgs& a, int r, int h, int col, int quad,
+                                            uint4* raw) {
   const int i = col < G ? col : 0;
   const char* q = reinterpret_cast<const char*>(a.q) +
                   (((size_t)r * a.H_q + h * G + i) * kMfmaD) * 2 + quad * 16;
 #pragma unroll
   for (int s = 0; s < 4; ++s) raw[s] = load16(q + s * 64);
+}
+
+// A operands of the 8 k steps from load_q_rows' registers, split by sign.
+template <int G>
+__device__ __forceinline__ void split_a(const uint4* raw, int col, uint4* A) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (col >= G) raw[s] = make_uint4(0, 0, 0, 0);
-    sign_split(raw[s], A[s], A[s + 4]);
-  }
+  for (int s = 0; s < 4; ++s)
+    sign_split(col < G ? raw[s] : make_uint4(0, 0, 0, 0), A[s], A[s + 4]);
 }
 
 template <int DT, int G, bool ONE_HEAD>
@@ -450,20 +453,29 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void score_mfma_kernel(ScoreArg
   uint4* my = tile[w];
 
   uint4 A1[8];
-  if constexpr (ONE_HEAD) load_a<G>(a, r, w % H, col, quad, A1);
+  if constexpr (ONE_HEAD) {
+    uint4 q1[4];
+    load_q_rows<G>(a, r, w % H, col, quad, q1);
+    split_a<G>(q1, col, A1);
+  }
 
   for (int t0 = w; t0 < ntasks; t0 += kMfmaWaves * T) {
     // page table, then records: every load unconditional (tasks past the
     // end repeat the last one, pages past the used ones are clamped to a
     // page of the request, and their results are dropped)
     int hh[T], jj[T], pp[T];
+    uint4 qr[T][4];                           // query rows when the head varies
 #pragma unroll
     for (int u = 0; u < T; ++u) {
       const int t = min(t0 + u * kMfmaWaves, ntasks - 1);
       hh[u] = t % H;
       jj[u] = j0 + 16 * (t / H) + col;
+      if constexpr (!ONE_HEAD) load_q_rows<G>(a, r, hh[u], col, quad, qr[u]);
       pp[u] = a.page_indices[pbeg + min(jj[u], jlast)];
     }
+    // every task's page-table and query loads are issued before the first
+    // wait (the records' addresses need the page indices of other lanes)
+    __builtin_amdgcn_sched_barrier(0);
     uint4 raw[T][8];
 #pragma unroll
     for (int u = 0; u < T; ++u)
@@ -505,7 +517,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void score_mfma_kernel(ScoreArg
         }
       }
       uint4 At[8];
-      if constexpr (!ONE_HEAD) load_a<G>(a, r, hh[u], col, quad, At);
+      if constexpr (!ONE_HEAD) split_a<G>(qr[u], col, At);
       const uint4* A = ONE_HEAD ? A1 : At;
       float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
