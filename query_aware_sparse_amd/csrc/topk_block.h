@@ -7,8 +7,11 @@
 // A workgroup of NT threads (kTkThreads in the standalone kernel, the
 // attention kernel's workgroup inside it) holds the row in registers: thread t
 // keeps the run of scores j in [t*PT, t*PT + PT) and their physical pages.
-// Per-element steps are branch-free (invalid elements go to a dummy
-// histogram bin), block-uniform values live in scalar registers, and
+// Per-element steps are branch-free (invalid elements get the bin past the
+// last one and count in no bin: their LDS atomics are masked off, as
+// thousands of them on one spare bin serialised on its address in rows much
+// shorter than the workgroup's capacity), block-uniform values live in
+// scalar registers, and
 // reductions within a wave use DPP, so one select costs a few thousand
 // cycles (a wave64 vector instruction occupies its SIMD for four cycles, so
 // the instruction count is the cost).  Selection narrows a closed score
@@ -45,7 +48,7 @@ constexpr int kTkCand = 512;         // candidates ranked from LDS
 constexpr float kTkMinRange = 1e-30f;
 
 struct TopkShared {
-  __align__(16) int hist[kTkBins + 4];   // + a dummy bin for skipped elements
+  __align__(16) int hist[kTkBins + 4];
   int cidx[kTkCand];
   float cval[kTkCand];
   int scan[2][kTkMaxWaves];
@@ -311,8 +314,8 @@ struct TopkRow {
         for (int b = tid; b < kTkBins + 4; b += NT) sh.hist[b] = 0;
         __syncthreads();
       }
-      // skipped elements go to the dummy bin; out-of-range values may map
-      // anywhere, the select discards them
+      // skipped elements get bin kTkBins and are not counted; out-of-range
+      // values may map anywhere, the select discards them
       if (bin.by_key) {
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
@@ -330,7 +333,8 @@ struct TopkRow {
         }
       }
 #pragma unroll
-      for (int k = 0; k < PT; ++k) atomicAdd(&sh.hist[bk[k]], 1);
+      for (int k = 0; k < PT; ++k)
+        if (bk[k] < kTkBins) atomicAdd(&sh.hist[bk[k]], 1);
       __syncthreads();
       {
         // every wave walks the histogram itself, so no barrier publishes the
