@@ -322,6 +322,11 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   // so the loads fly during the softmax and the MFMAs; the last page's
   // loads repeat it and are not used.
   v8i_t kop[NT][2], vop[4];
+  // A operand whose row 0 is all ones (e4m3 1.0 = 0x38) and the rest zero:
+  // lanes 0 and 32 hold row 0's two k halves
+  v8i_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (lane & 31) == 0 ? 0x38383838 : 0;
   if (wave < U) {
     load_k(wave, kop);
     load_v(wave, vop);
@@ -371,7 +376,6 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
     const float m_use = grow ? zmax : m_run;
     const bool live = m_use != -INFINITY;
     uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T operand: 32 e4m3 bytes
-    float lsum = 0.f;
     if (member && live) {
       const float off = 8.f - m_use;
 #pragma unroll
@@ -385,15 +389,16 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
           const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           pw[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
         }
-      // the row sum over the quantised values (the ones the PV product uses)
-#pragma unroll
-      for (int w = 0; w < 4 * NT; ++w) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
-        lsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
-      }
     }
-    lsum = lane_rowsum(lsum);
+    const v8i_t pop = *reinterpret_cast<const v8i_t*>(pw);
+    // the row sum over the quantised values (the ones the PV product uses),
+    // on the matrix cores: a product with an all-ones row 0 sums each P^T
+    // column, i.e. each row's p over the page, into output row 0 (register 0
+    // of lanes 0-31, lane = row); lanes 32-63 take their row's from there
+    const v16f_t rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pop, v16f_t{}, 0, 0,
+                                                                      0, 0, 0, 0);
+    const float rs_up = __shfl_xor(rs[0], 32, kWave);
+    const float lsum = hf ? rs_up : rs[0];
     const float alpha = grow ? fast_exp2(m_run - m_use) : 1.f;   // 0 on a row's first page
     if (live) {
       l_run = l_run * alpha + lsum * (1.f / 256.f);
@@ -405,7 +410,6 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
     }
-    const v8i_t pop = *reinterpret_cast<const v8i_t*>(pw);
     // O^T += V^T P^T: lane (dim 32 dt + lane%32, hf) holds the same k slots
     // (tokens 32 tau + 8 (e/4) + 4 hf + e%4) as its P bytes
 #pragma unroll
