@@ -75,16 +75,17 @@ PMC_TRAFFIC = {
 # line times), the same scaling.  MFMA busy is a fraction of the SIMD cycles
 # while the kernel runs: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x
 # GRBM_GUI_ACTIVE / 8 XCDs, the counter's sum over the XCDs); executed fp8
-# flops are MOPS_F8 x 512 (98.30 GFLOP, the union accounting's figure).
+# flops are MOPS_F8 x 512 (110.6 GFLOP: the union accounting's 98.30 GFLOP
+# plus one row-sum MFMA per page, which that accounting leaves out).
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "a4ddbf1243e37c1de21df0d3ead4ba21a6fc1234a07b511244938144bbb27872",
-    "fetch_kib": 152101.9,
-    "write_kib": 4224.6,
-    "mfma_busy_frac": 0.2033,
-    "valu_insts_per_mfma": 36.36,
-    "mfma_insts": 749984,
+    "sources_sha256": "b5f41532f03cf7cfe9221d358484e51802f2cea7d3c0f96a04eb475975bc4a25",
+    "fetch_kib": 150847.5,
+    "write_kib": 4224.8,
+    "mfma_busy_frac": 0.2331,
+    "valu_insts_per_mfma": 26.56,
+    "mfma_insts": 843732,
 }
 
 

@@ -375,21 +375,25 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
     const bool grow = zmax > m_run + kULazy;    // same for both lanes of a row
     const float m_use = grow ? zmax : m_run;
     const bool live = m_use != -INFINITY;
-    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T operand: 32 e4m3 bytes
-    if (member && live) {
-      const float off = 8.f - m_use;
+    // P^T operand: 32 e4m3 bytes.  No branch on the row: a row that is not
+    // a member of the page, or has no logit yet, takes an offset of -inf, so
+    // all its p are exp2(-inf) = 0 (the logits are finite or -inf).
+    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const float off = member && live ? 8.f - m_use : -INFINITY;
 #pragma unroll
-      for (int tau = 0; tau < NT; ++tau)
+    for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-          const int k = 16 * tau + e;
-          float p[4];
+      for (int e = 0; e < 16; e += 4) {
+        const int k = 16 * tau + e;
+        float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(st[tau][e + i], zscale, off));
-          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          pw[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
-        }
-    }
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(st[tau][e + i], zscale, off));
+        // the first conversion keeps the high half of its third operand,
+        // which the second one overwrites: a logit no longer needed will do
+        const int lo =
+            __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(st[tau][e]), false);
+        pw[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+      }
     const v8i_t pop = *reinterpret_cast<const v8i_t*>(pw);
     // the row sum over the quantised values (the ones the PV product uses),
     // on the matrix cores: a product with an all-ones row 0 sums each P^T
