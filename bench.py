@@ -80,11 +80,11 @@ PMC_TRAFFIC = {
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "b5f41532f03cf7cfe9221d358484e51802f2cea7d3c0f96a04eb475975bc4a25",
-    "fetch_kib": 150847.5,
-    "write_kib": 4224.8,
-    "mfma_busy_frac": 0.2331,
-    "valu_insts_per_mfma": 26.56,
+    "sources_sha256": "11a0f80a2d7213c988dc90691161d23a8083c8aef0986b52fc5a656a2c1a569c",
+    "fetch_kib": 145153.6,
+    "write_kib": 4225.0,
+    "mfma_busy_frac": 0.2437,
+    "valu_insts_per_mfma": 24.64,
     "mfma_insts": 843732,
 }
 

@@ -193,14 +193,7 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   return total;
 }
 
-__device__ __forceinline__ float lane_rowsum(float v) { return v + __shfl_xor(v, 32, kWave); }
 __device__ __forceinline__ float lane_rowmax(float v) { return fmaxf(v, __shfl_xor(v, 32, kWave)); }
-
-// e4m3 byte of x (|x| <= 448 after the clamp; the conversion does not saturate)
-__device__ __forceinline__ uint32_t to_e4m3(float x) {
-  x = fminf(fmaxf(x, -448.f), 448.f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xffu;
-}
 
 template <int G, int NT>
 __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
@@ -251,16 +244,22 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(qf[e]));
   amax = lane_rowmax(amax);
   const float qs = amax > 0.f ? amax / 448.f : 1.f;
+  // q / qs as q times one reciprocal (within an ulp of the quotient, far
+  // below the e4m3 step), clamped to +-448 (the conversion does not
+  // saturate), four codes per word from two packed conversions
+  const float rqs = 1.f / qs;
   v8i_t qop[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     uint32_t w[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      uint32_t v = 0;
+      float x[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v |= to_e4m3(qf[ks * 32 + 4 * b + k] / qs) << (8 * k);
-      w[b] = v;
+      for (int k = 0; k < 4; ++k)
+        x[k] = __builtin_amdgcn_fmed3f(qf[ks * 32 + 4 * b + k] * rqs, -448.f, 448.f);
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[2]), false);
+      w[b] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
     }
     qop[ks] = *reinterpret_cast<v8i_t*>(w);
   }
