@@ -80,11 +80,11 @@ PMC_TRAFFIC = {
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "11a0f80a2d7213c988dc90691161d23a8083c8aef0986b52fc5a656a2c1a569c",
-    "fetch_kib": 145153.6,
-    "write_kib": 4225.0,
-    "mfma_busy_frac": 0.2437,
-    "valu_insts_per_mfma": 24.64,
+    "sources_sha256": "d2a9eebb54091e0f2245250b4aea89849f92bf90d37543cbb8c555861edb3531",
+    "fetch_kib": 146563.1,
+    "write_kib": 4225.3,
+    "mfma_busy_frac": 0.2405,
+    "valu_insts_per_mfma": 24.75,
     "mfma_insts": 843732,
 }
 

@@ -103,11 +103,21 @@ __device__ GroupInfo find_group(const int32_t* q_indptr, int B, int group, int g
   return gr;
 }
 
+constexpr int kUEpt = kUMaxUnion / kUThreads;   // set entries per thread
+
+// A group's set entries and causal limits loaded ahead of the union build
+// (ok: they belong to the group being built).
+struct PreSets {
+  int v[kUEpt];   // entry tid + k * kUThreads of the group's concatenated sets
+  int cpos;       // threads < kUMaxGroup: causal limit of that query
+  bool ok;
+};
+
 // Union of the group's page sets in ascending order with membership bits
 // and physical pages (the PageWeaver notes, SS2BST9I / AWLR3K97).  Returns
 // the union size; the lists are in `sh`.
 __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo& gr, int h,
-                           int n_pages, int pbeg) {
+                           int n_pages, int pbeg, const PreSets& pre) {
   const int tid = threadIdx.x;
   const int words = (n_pages + 31) / 32;
   for (int i = tid; i < kUMaxGroup * words; i += kUThreads) sh.bm[i / words][i % words] = 0;
@@ -123,16 +133,22 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   // entries <= kUMaxUnion: every set entry's load is issued before any is
   // used, and the slots' causal limits (the union preparation alone has
   // none) are loaded beside them
-  constexpr int EPT = kUMaxUnion / kUThreads;
+  constexpr int EPT = kUEpt;
   const int entries = gr.nq * a.kq;
   int ids[EPT];
+  if (pre.ok) {
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int e = min(tid + k * kUThreads, entries - 1);
-    const int i = e / a.kq;
-    ids[k] = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
+    for (int k = 0; k < EPT; ++k) ids[k] = pre.v[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = min(tid + k * kUThreads, entries - 1);
+      const int i = e / a.kq;
+      ids[k] = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
+    }
   }
-  if (tid < kUMaxGroup) sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? a.q_pos[my_qid] : -1;
+  if (tid < kUMaxGroup)
+    sh.cpos[tid] = (a.q_pos && tid < gr.nq) ? (pre.ok ? pre.cpos : a.q_pos[my_qid]) : -1;
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = tid + k * kUThreads;
@@ -140,19 +156,25 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
     if (e < entries && id >= 0 && id < n_pages) atomicOr(&sh.bm[e / a.kq][id >> 5], 1u << (id & 31));
   }
   __syncthreads();
-  // each thread owns up to WPT consecutive bitmap words, whose per-query
-  // words it reads once into registers (all in flight together)
-  constexpr int WPT = kUMaxWords / kUThreads;
-  const int per = (words + kUThreads - 1) / kUThreads;   // <= WPT
-  const int w0 = tid * per;
+  // each thread owns bpt consecutive bits of the bitmaps (pages), 4 to 64
+  // so that the union is spread over as many threads as it has 4-page
+  // slices: a slice of one word (bpt <= 32) or two whole words (bpt = 64);
+  // its per-query words are read once into registers, masked to the slice
+  constexpr int WPT = kUMaxWords / kUThreads;   // words of the widest slice
+  static_assert(WPT == 2, "slices are one word or two");
+  const int bpt = words <= 32 ? 4 : words <= 64 ? 8 : words <= 128 ? 16 : words <= 256 ? 32 : 64;
+  const int b0 = tid * bpt;
+  const int w0 = b0 >> 5;
+  const uint32_t smask = bpt >= 32 ? ~0u : ((1u << bpt) - 1u) << (b0 & 31);
   uint32_t qw[WPT][kUMaxGroup];
   int mine = 0;
 #pragma unroll
   for (int k = 0; k < WPT; ++k) {
     const int w = w0 + k;
-    const bool in = k < per && w < words;
+    const bool in = (k == 0 || bpt == 64) && w < words;
 #pragma unroll
-    for (int i = 0; i < kUMaxGroup; ++i) qw[k][i] = (in && i < gr.nq) ? sh.bm[i][in ? w : 0] : 0u;
+    for (int i = 0; i < kUMaxGroup; ++i)
+      qw[k][i] = (in && i < gr.nq) ? sh.bm[i][in ? w : 0] & smask : 0u;
     uint32_t u = 0;
 #pragma unroll
     for (int i = 0; i < kUMaxGroup; ++i) u |= qw[k][i];
@@ -204,23 +226,51 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   const int H = a.H_kv;
   const int h = blockIdx.x % H;
   const int gi = blockIdx.x / H;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  // ---- per-lane row: row = query * G + head (S^T / O^T column = lane % 32)
+  const int row = lane % 32, hf = lane / 32;
+  const int qi = row / G, hq = row % G;
+
+  // In identity order the group's slots are guessed to start at gi * group
+  // (one request whose queries start at 0, or requests whose query counts
+  // are multiples of the group): the guess's set entries, causal limits and
+  // query rows are loaded before the group is known, so that their latency
+  // overlaps the request-bound loads.  Slots are clamped to N - 1 (every
+  // load stays in bounds); a group the guess misses loads them again.
+  const int sq0 = gi * a.group;
+  PreSets pre;
+  uint4 qraw[8];
+  if (a.ids == nullptr) {
+    const int gkq = a.group * a.kq;
+#pragma unroll
+    for (int k = 0; k < kUEpt; ++k) {
+      const int e = min(tid + k * kUThreads, gkq - 1);
+      const int i = e / a.kq;
+      const int qid = min(sq0 + i, a.N - 1);
+      pre.v[k] = a.sets[((size_t)qid * H + h) * a.kq + (e - i * a.kq)];
+    }
+    pre.cpos = a.q_pos[min(sq0 + (tid < kUMaxGroup ? tid : 0), a.N - 1)];
+    const int qid = min(sq0 + qi, a.N - 1);
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   const GroupInfo gr = find_group(a.q_indptr, a.B, a.group, gi);
   if (gr.nq == 0) return;                     // uniform: no such group
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int L = a.seq_lens[gr.r];
   const int pbeg = a.page_indptr[gr.r];
   const int P_r = a.page_indptr[gr.r + 1] - pbeg;
   const int n_pages = L > 0 ? min(min((L + S - 1) / S, P_r), kUMaxWords * 32) : 0;
-
-  // ---- per-lane row: row = query * G + head (S^T / O^T column = lane % 32)
-  const int row = lane % 32, hf = lane / 32;
-  const int qi = row / G, hq = row % G;
   const bool row_ok = qi < gr.nq;
-  // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row.
-  // Its 16-byte loads are issued now, so they land during the union build (a
-  // row past the group reads the first query's row and is zeroed).
-  uint4 qraw[8];
-  {
+  pre.ok = a.ids == nullptr && gr.q0 == sq0;   // uniform
+  // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row
+  // (a row past the group is zeroed)
+  if (!pre.ok) {
     const int slot = gr.q0 + (row_ok ? qi : 0);
     const int qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
     const char* qp = reinterpret_cast<const char*>(a.q) +
@@ -231,7 +281,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
       for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
   }
 
-  const int U = build_union(sh, a, gr, h, n_pages, pbeg);
+  const int U = build_union(sh, a, gr, h, n_pages, pbeg, pre);
   const int cq = row_ok ? sh.cpos[qi] : -1;
   float qf[64];
 #pragma unroll
@@ -490,7 +540,9 @@ __global__ __launch_bounds__(kUThreads) void union_prep_kernel(UnionArgs a) {
     const int pbeg = a.page_indptr[gr.r];
     const int P_r = a.page_indptr[gr.r + 1] - pbeg;
     const int n_pages = L > 0 ? min(min((L + a.S - 1) / a.S, P_r), kUMaxWords * 32) : 0;
-    U = build_union(sh, a, gr, h, n_pages, pbeg);
+    PreSets none;
+    none.ok = false;
+    U = build_union(sh, a, gr, h, n_pages, pbeg, none);
   }
   for (int i = threadIdx.x; i < cap; i += kUThreads) {
     ul[i] = i < U ? sh.ulist[i] : -1;

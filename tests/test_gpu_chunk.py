@@ -57,27 +57,26 @@ def _corrupt(case, seed):
     return case
 
 
-def test_union_pages_match_oracle(qas):
-    from query_aware_sparse_amd.staging import ChunkBatch
-    case = _corrupt(multiquery_chunk(L=8192, N=61), 1)
-    cb = ChunkBatch([case])
-    G = qas.qas_chunk_groups(cb.N, 1, case.group)
-    cap = case.group * case.kq
-    ul = torch.full((G, case.H_kv, cap), -9, dtype=torch.int32, device="cuda")
-    uc = torch.full((G, case.H_kv), -9, dtype=torch.int32, device="cuda")
-    um = torch.zeros((G, case.H_kv, cap), dtype=torch.uint8, device="cuda")
-    qas.qas_union_pages(cb.db.batch, cb.q_indptr, cb.sets, case.group, case.S, ul, uc, um)
+def _union_pages_check(qas, batch, q_indptr, sets, N, H, kq, group, S, P):
+    """qas_union_pages of one request's N queries against the oracle's union
+    with membership, group by group and head by head."""
+    G = qas.qas_chunk_groups(N, 1, group)
+    cap = group * kq
+    ul = torch.full((G, H, cap), -9, dtype=torch.int32, device="cuda")
+    uc = torch.full((G, H), -9, dtype=torch.int32, device="cuda")
+    um = torch.zeros((G, H, cap), dtype=torch.uint8, device="cuda")
+    qas.qas_union_pages(batch, q_indptr, sets, group, S, ul, uc, um)
     torch.cuda.synchronize()
     ul, uc, um = ul.cpu().numpy(), uc.cpu().numpy(), um.cpu().numpy()
-    P = -(-case.L // case.S)
-    n_groups = -(-case.N // case.group)
+    sets = sets.cpu().numpy()
+    n_groups = -(-N // group)
     for gi in range(G):
-        for h in range(case.H_kv):
+        for h in range(H):
             if gi >= n_groups:
                 assert uc[gi, h] == 0 and np.all(ul[gi, h] == -1)
                 continue
-            qs = range(gi * case.group, min(case.N, (gi + 1) * case.group))
-            valid = [[int(p) for p in case.sets[n, h] if 0 <= p < P] for n in qs]
+            qs = range(gi * group, min(N, (gi + 1) * group))
+            valid = [[int(p) for p in sets[n, h] if 0 <= p < P] for n in qs]
             union, member = quest.union_with_membership(valid)
             U = len(union)
             assert uc[gi, h] == U
@@ -86,6 +85,40 @@ def test_union_pages_match_oracle(qas):
             for i in range(len(valid)):
                 bits |= member[i].astype(np.int64) << i
             assert np.array_equal(um[gi, h, :U], bits)
+
+
+def test_union_pages_match_oracle(qas):
+    from query_aware_sparse_amd.staging import ChunkBatch
+    case = _corrupt(multiquery_chunk(L=8192, N=61), 1)
+    cb = ChunkBatch([case])
+    _union_pages_check(qas, cb.db.batch, cb.q_indptr, cb.sets, cb.N, case.H_kv, case.kq,
+                       case.group, case.S, -(-case.L // case.S))
+
+
+@pytest.mark.parametrize("P", [1025, 1500, 3000, 6000, 8200, 16384])
+def test_union_pages_long_rows(qas, P):
+    """Rows of 1025 to 16384 pages (the union build spreads a row's bitmaps
+    over the workgroup in slices of 8 to 64 pages; 4 up to 1024 pages):
+    seeded sets over the whole row, with its first and last pages, slice
+    and word edges, duplicates and invalid IDs, against the oracle's union
+    with membership.  Only page tables and sets are needed."""
+    from query_aware_sparse_amd.staging import DeviceBatch
+    rng = np.random.default_rng(70 + P)
+    S, H, group, kq, N = 64, 2, 8, 128, 13
+    L = P * S - 5
+    db = DeviceBatch([L], [rng.permutation(P + 37)[:P].astype(np.int32)], S)
+    sets = rng.integers(0, P, size=(N, H, kq)).astype(np.int32)
+    edges = [0, 1, 31, 32, 63, 64, P // 2, P - 33, P - 32, P - 2, P - 1]
+    for n in range(N):
+        for h in range(H):
+            k = int(rng.integers(1, len(edges)))
+            sets[n, h, :k] = rng.choice(edges, k, replace=False)
+    sets[0, 0, 20:24] = [P, -1, 2**31 - 1, sets[0, 0, 19]]   # invalid IDs and a duplicate
+    sets[5, 1, :] = sets[4, 1, ::-1]                         # same set, other order
+    q_indptr = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    say(f"union pages, one request of {P} pages, {N} queries, kq {kq}")
+    _union_pages_check(qas, db.batch, q_indptr, torch.from_numpy(sets).cuda(), N, H, kq, group,
+                       S, P)
 
 
 def test_chunk_attention_small_all_queries(qas):
