@@ -80,11 +80,11 @@ PMC_TRAFFIC = {
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "d2a9eebb54091e0f2245250b4aea89849f92bf90d37543cbb8c555861edb3531",
-    "fetch_kib": 146563.1,
-    "write_kib": 4225.3,
-    "mfma_busy_frac": 0.2405,
-    "valu_insts_per_mfma": 24.75,
+    "sources_sha256": "7ba9efe26fb8947b09834125e45d0f8a41b574f8b298e7bddb2c179e38f6b773",
+    "fetch_kib": 69079.7,
+    "write_kib": 4224.0,
+    "mfma_busy_frac": 0.2548,
+    "valu_insts_per_mfma": 25.95,
     "mfma_insts": 843732,
 }
 

@@ -6,13 +6,18 @@
 //
 // A group is `group` consecutive queries of one request; with g query heads
 // per KV head its rows form one 32-row MFMA tile (rows = query * g + head).
-// One workgroup per (group, KV head), mapped so that all groups of one KV
-// head land on the same XCD (their page unions overlap, so neighbours hit
-// in that XCD's L2):
-//   1. union preparation: each query's valid page IDs set bits in a per-query
-//      bitmap in LDS; OR-ing them gives the union, emitted in ascending page
-//      order with an 8-bit membership mask per page and its physical page;
-//   2. each wave streams its share of the union pages.  S^T = K Q^T with
+// One workgroup per (pair of consecutive groups, KV head), 8 waves, mapped
+// so that all groups of one KV head land on the same XCD (their page unions
+// overlap, so neighbours hit in that XCD's L2):
+//   1. union preparation, one half of the workgroup per group: each query's
+//      valid page IDs set bits in a per-query bitmap in LDS; OR-ing them
+//      gives the union, emitted in ascending page order with an 8-bit
+//      membership mask per page and its physical page;
+//   2. four waves per group (two of the first four and two of the last
+//      four, so that neither group's waves are all the younger ones on
+//      their SIMDs) stream its union pages, each claiming its next page
+//      from the group's LDS counter, so that the group's waves and both
+//      groups end together.  S^T = K Q^T with
 //      the fp8 K tile as A straight from HBM/L2 and Q quantised per row to
 //      e4m3 as B (v_mfma 32x32x64 f8f6f4); each lane then owns one row's
 //      logits, so the mask (membership, t <= c_i, t < L) and the online
@@ -22,8 +27,8 @@
 //      each block holding one 16-byte piece of every lane's A (K) or B (V^T,
 //      tokens in the order of the MFMA's k slots) operand, so a wave load
 //      reads 1 KiB of consecutive bytes: no LDS staging or byte gathers;
-//   3. the four waves' states are merged in LDS and written at the queries'
-//      own output rows.
+//   3. each group's four wave states are merged in LDS and written at the
+//      queries' own output rows.
 #include "qas_device.h"
 #include "qas_internal.h"
 
@@ -57,10 +62,11 @@ struct UnionShared {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Exclusive prefix sum over the workgroup (thread order), one barrier after
-// the per-wave totals are published; *total gets the sum.
-__device__ __forceinline__ int block_excl(int v, int* scratch, int* total) {
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+// Exclusive prefix sum over kUThreads threads (order of the local index
+// tid), one workgroup barrier after the per-wave totals are published;
+// *total gets the sum.
+__device__ __forceinline__ int block_excl(int v, int tid, int* scratch, int* total) {
+  const int lane = lane_id(), wave = tid / kWave;
   int incl = v;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -103,6 +109,30 @@ __device__ GroupInfo find_group(const int32_t* q_indptr, int B, int group, int g
   return gr;
 }
 
+// Groups gi and gi + 1 of the launch (as find_group), from one pass over the
+// request bounds.
+__device__ void find_group_pair(const int32_t* q_indptr, int B, int group, int gi,
+                                GroupInfo* gr) {
+  gr[0] = GroupInfo{0, 0, 0};
+  gr[1] = GroupInfo{0, 0, 0};
+  int base = 0;
+  for (int r = 0; r < B; ++r) {
+    const int a = q_indptr[r], n = q_indptr[r + 1] - a;
+    const int ng = (n + group - 1) / group;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int local = gi + k - base;
+      if (local >= 0 && local < ng) {
+        gr[k].r = r;
+        gr[k].q0 = a + local * group;
+        gr[k].nq = min(group, n - local * group);
+      }
+    }
+    base += ng;
+    if (gi + 1 < base) break;
+  }
+}
+
 constexpr int kUEpt = kUMaxUnion / kUThreads;   // set entries per thread
 
 // A group's set entries and causal limits loaded ahead of the union build
@@ -114,11 +144,12 @@ struct PreSets {
 };
 
 // Union of the group's page sets in ascending order with membership bits
-// and physical pages (the PageWeaver notes, SS2BST9I / AWLR3K97).  Returns
-// the union size; the lists are in `sh`.
+// and physical pages (the PageWeaver notes, SS2BST9I / AWLR3K97), built by
+// kUThreads threads (local index tid) while every thread of the workgroup
+// takes the same barriers.  Returns the union size; the lists are in `sh`.
+// A group with no queries gets an empty union.
 __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo& gr, int h,
-                           int n_pages, int pbeg, const PreSets& pre) {
-  const int tid = threadIdx.x;
+                           int n_pages, int pbeg, const PreSets& pre, int tid) {
   const int words = (n_pages + 31) / 32;
   for (int i = tid; i < kUMaxGroup * words; i += kUThreads) sh.bm[i / words][i % words] = 0;
   // the original query of every slot (an execution order from the regroup,
@@ -142,7 +173,7 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
   } else {
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const int e = min(tid + k * kUThreads, entries - 1);
+      const int e = max(0, min(tid + k * kUThreads, entries - 1));
       const int i = e / a.kq;
       ids[k] = a.sets[((size_t)sh.qid[i] * a.H_kv + h) * a.kq + (e - i * a.kq)];
     }
@@ -181,7 +212,7 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
     mine += __popc(u);
   }
   int total;
-  int pos = block_excl(mine, sh.wave_tot, &total);
+  int pos = block_excl(mine, tid, sh.wave_tot, &total);
 #pragma unroll
   for (int k = 0; k < WPT; ++k) {
     const int w = w0 + k;
@@ -217,40 +248,61 @@ __device__ int build_union(UnionShared& sh, const UnionArgs& a, const GroupInfo&
 
 __device__ __forceinline__ float lane_rowmax(float v) { return fmaxf(v, __shfl_xor(v, 32, kWave)); }
 
+constexpr int kUPair = 2;                          // groups per workgroup
+constexpr int kUPairThreads = kUPair * kUThreads;  // 8 waves, two per SIMD
+
+// Wave w of the workgroup computes group (w ^ (w >> 2)) & 1 of its pair as
+// that group's wave w >> 1: each group gets two of the first four waves and
+// two of the last four, one per SIMD when the waves are dealt out to the
+// SIMDs in turn, so that the issue priority of older waves favours neither
+// group.
+__device__ __forceinline__ int pair_unit(int wave) { return (wave ^ (wave >> 2)) & 1; }
+
 template <int G, int NT>
-__global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
+__global__ __launch_bounds__(kUPairThreads, 2) void union_attn_kernel(UnionArgs a) {
   constexpr int S = 32 * NT;                  // page size
-  __shared__ UnionShared sh;
-  __shared__ __align__(16) float red_buf[2][32][kUD + 2];   // wave merge
+  __shared__ UnionShared shu[kUPair];
+  __shared__ __align__(16) float red_buf[kUPair][2][32][kUD + 2];   // wave merge per group
+  __shared__ int next_page[kUPair];
 
   const int H = a.H_kv;
   const int h = blockIdx.x % H;
-  const int gi = blockIdx.x / H;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int pair = blockIdx.x / H;
+  // the wave index as a uniform value, so that everything derived from it
+  // (the groups, their bounds) stays in scalar registers and scalar loads
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // each half of the workgroup builds the union of one group of the pair ...
+  const int bh = wave / kUWaves, btid = threadIdx.x % kUThreads;
+  const int gb = kUPair * pair + bh;
+  // ... and each wave computes one group's pages
+  const int unit = pair_unit(wave), lw = wave >> 1;
+  const int gc = kUPair * pair + unit;
+  UnionShared& sh = shu[unit];
   // ---- per-lane row: row = query * G + head (S^T / O^T column = lane % 32)
   const int row = lane % 32, hf = lane / 32;
   const int qi = row / G, hq = row % G;
 
-  // In identity order the group's slots are guessed to start at gi * group
-  // (one request whose queries start at 0, or requests whose query counts
-  // are multiples of the group): the guess's set entries, causal limits and
-  // query rows are loaded before the group is known, so that their latency
-  // overlaps the request-bound loads.  Slots are clamped to N - 1 (every
-  // load stays in bounds); a group the guess misses loads them again.
-  const int sq0 = gi * a.group;
+  // In identity order a group's slots are guessed to start at group index *
+  // group size (one request whose queries start at 0, or requests whose
+  // query counts are multiples of the group): the guess's set entries and
+  // causal limits (built group) and query rows (computed group) are loaded
+  // before the groups are known, so that their latency overlaps the
+  // request-bound loads.  Slots are clamped to N - 1 (every load stays in
+  // bounds); a group the guess misses loads them again.
+  const int sqb = gb * a.group, sqc = gc * a.group;
   PreSets pre;
   uint4 qraw[8];
   if (a.ids == nullptr) {
     const int gkq = a.group * a.kq;
 #pragma unroll
     for (int k = 0; k < kUEpt; ++k) {
-      const int e = min(tid + k * kUThreads, gkq - 1);
+      const int e = min(btid + k * kUThreads, gkq - 1);
       const int i = e / a.kq;
-      const int qid = min(sq0 + i, a.N - 1);
+      const int qid = min(sqb + i, a.N - 1);
       pre.v[k] = a.sets[((size_t)qid * H + h) * a.kq + (e - i * a.kq)];
     }
-    pre.cpos = a.q_pos[min(sq0 + (tid < kUMaxGroup ? tid : 0), a.N - 1)];
-    const int qid = min(sq0 + qi, a.N - 1);
+    pre.cpos = a.q_pos[min(sqb + (btid < kUMaxGroup ? btid : 0), a.N - 1)];
+    const int qid = min(sqc + qi, a.N - 1);
     const char* qp = reinterpret_cast<const char*>(a.q) +
                      (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
 #pragma unroll
@@ -260,18 +312,22 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const GroupInfo gr = find_group(a.q_indptr, a.B, a.group, gi);
-  if (gr.nq == 0) return;                     // uniform: no such group
-  const int L = a.seq_lens[gr.r];
-  const int pbeg = a.page_indptr[gr.r];
-  const int P_r = a.page_indptr[gr.r + 1] - pbeg;
-  const int n_pages = L > 0 ? min(min((L + S - 1) / S, P_r), kUMaxWords * 32) : 0;
-  const bool row_ok = qi < gr.nq;
-  pre.ok = a.ids == nullptr && gr.q0 == sq0;   // uniform
-  // Q row slice: dims 64*ks + 32*hf + [0, 32) for ks = 0, 1, quantised per row
-  // (a row past the group is zeroed)
-  if (!pre.ok) {
-    const int slot = gr.q0 + (row_ok ? qi : 0);
+  GroupInfo grp[kUPair];
+  find_group_pair(a.q_indptr, a.B, a.group, kUPair * pair, grp);
+  if (grp[0].nq == 0) return;                 // uniform: no group in the pair
+  const GroupInfo grb = bh ? grp[1] : grp[0], grc = unit ? grp[1] : grp[0];
+  // built group: its request's pages (none for a group with no queries)
+  const int Lb = grb.nq > 0 ? a.seq_lens[grb.r] : 0;
+  const int pbeg = a.page_indptr[grb.r];
+  const int P_r = a.page_indptr[grb.r + 1] - pbeg;
+  const int n_pages = Lb > 0 ? min(min((Lb + S - 1) / S, P_r), kUMaxWords * 32) : 0;
+  pre.ok = a.ids == nullptr && grb.q0 == sqb;
+  // computed group: Q row slice, dims 64*ks + 32*hf + [0, 32) for ks = 0, 1,
+  // quantised per row (a row past the group is zeroed)
+  const int L = a.seq_lens[grc.r];
+  const bool row_ok = qi < grc.nq;
+  if (!(a.ids == nullptr && grc.q0 == sqc)) {
+    const int slot = grc.q0 + (row_ok ? qi : 0);
     const int qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
     const char* qp = reinterpret_cast<const char*>(a.q) +
                      (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
@@ -281,7 +337,12 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
       for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
   }
 
-  const int U = build_union(sh, a, gr, h, n_pages, pbeg, pre);
+  // the first kUWaves pages of a union go to its waves by index; the rest
+  // are claimed one at a time (the counters are read after the build's
+  // barriers)
+  if (threadIdx.x < kUPair) next_page[threadIdx.x] = kUWaves;
+  build_union(shu[bh], a, grb, h, n_pages, pbeg, pre, btid);
+  const int U = sh.count;
   const int cq = row_ok ? sh.cpos[qi] : -1;
   float qf[64];
 #pragma unroll
@@ -376,14 +437,24 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   v8i_t ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (lane & 31) == 0 ? 0x38383838 : 0;
-  if (wave < U) {
-    load_k(wave, kop);
-    load_v(wave, vop);
+  // A wave claims its next page one page ahead, so that the claim's
+  // round trip hides under the current page's work; pages go to whichever
+  // wave of the group asks first, so the group's waves end together
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_page[unit], 1);
+    return __shfl(v, 0, kWave);
+  };
+  int u = lw;
+  int un = u < U ? claim() : U;
+  if (u < U) {
+    load_k(u, kop);
+    load_v(u, vop);
   }
-  for (int u = wave; u < U; u += kUWaves) {
+  while (u < U) {
     const int id = sh.ulist[u];
     const unsigned char mk = sh.umask[u];
-    const int un = min(u + kUWaves, U - 1);
+    const int ul = min(un, U - 1);          // next operands (the last page repeats itself)
     // S^T = K Q^T: lane holds row `row`, tokens 32 tau + 8 (e/4) + 4 hf + e%4
     v16f_t st[NT];
 #pragma unroll
@@ -395,7 +466,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
         st[tau] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[tau][ks], qop[ks], st[tau],
                                                                   0, 0, 0, 0, 0, 0);
     }
-    load_k(un, kop);
+    load_k(ul, kop);
     // mask + online softmax, lane-local per row.  Pages that every row of
     // the wave sees whole (all but those at a causal limit or the sequence
     // end) skip the per-token mask; element k = 16 tau + e of a lane is
@@ -469,18 +540,20 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
     for (int dt = 0; dt < 4; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[dt], pop, acc[dt], 0, 0, 0, 0,
                                                                 0, 0);
-    load_v(un, vop);
+    load_v(ul, vop);
+    u = un;
+    if (u < U) un = claim();
   }
 
-  // ---- merge the waves: 2,3 -> 0,1 then 1 -> 0 ------------------------------
-  float* red = &red_buf[0][0][0];            // [2][32 rows][130]
+  // ---- merge each group's waves: 2,3 -> 0,1 then 1 -> 0 ---------------------
+  float* red = &red_buf[unit][0][0][0];      // [2][32 rows][130]
   constexpr int RS = kUD + 2;
   __syncthreads();
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
     const int lo_w = step == 0 ? 2 : 1;       // waves >= lo_w publish
-    if (wave >= lo_w && wave < 2 * lo_w) {
-      float* dst = red + (size_t)(wave - lo_w) * kURows * RS + row * RS;
+    if (lw >= lo_w && lw < 2 * lo_w) {
+      float* dst = red + (size_t)(lw - lo_w) * kURows * RS + row * RS;
       if (hf == 0) {
         dst[0] = m_run;
         dst[1] = l_run;
@@ -491,8 +564,8 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
         for (int e = 0; e < 16; ++e) dst[2 + 32 * dt + 8 * (e / 4) + 4 * hf + (e % 4)] = acc[dt][e];
     }
     __syncthreads();
-    if (wave < lo_w) {
-      const float* src = red + (size_t)wave * kURows * RS + row * RS;
+    if (lw < lo_w) {
+      const float* src = red + (size_t)lw * kURows * RS + row * RS;
       const float m2 = src[0], l2 = src[1];
       const float mm = fmaxf(m_run, m2);
       if (mm != -INFINITY) {
@@ -510,7 +583,7 @@ __global__ __launch_bounds__(kUThreads, 2) void union_attn_kernel(UnionArgs a) {
   }
 
   // ---- outputs at the queries' own rows ----------------------------------------
-  if (wave == 0 && row_ok) {
+  if (lw == 0 && row_ok) {
     const size_t orow = (size_t)sh.qid[qi] * a.H_q + h * G + hq;
     const float oscale = l_run > 0.f ? a.v_scale[h] / (256.f * l_run) : 0.f;
 #pragma unroll
@@ -542,7 +615,7 @@ __global__ __launch_bounds__(kUThreads) void union_prep_kernel(UnionArgs a) {
     const int n_pages = L > 0 ? min(min((L + a.S - 1) / a.S, P_r), kUMaxWords * 32) : 0;
     PreSets none;
     none.ok = false;
-    U = build_union(sh, a, gr, h, n_pages, pbeg, none);
+    U = build_union(sh, a, gr, h, n_pages, pbeg, none, threadIdx.x);
   }
   for (int i = threadIdx.x; i < cap; i += kUThreads) {
     ul[i] = i < U ? sh.ulist[i] : -1;
@@ -562,11 +635,11 @@ bool union_supported(int kv_dtype, int q_dtype, int d, int S, int g, int group, 
 int union_max_pages() { return kUMaxWords * 32; }
 
 hipError_t launch_union_attn(const UnionArgs& a, hipStream_t s) {
-  dim3 grid(a.max_groups * a.H_kv);
-#define QAS_UNION_CASE(GG, NT)                                                        \
-  if (a.g == GG && a.S == 32 * NT) {                                                  \
-    hipLaunchKernelGGL((union_attn_kernel<GG, NT>), grid, dim3(kUThreads), 0, s, a); \
-    return hipGetLastError();                                                         \
+  dim3 grid((a.max_groups + kUPair - 1) / kUPair * a.H_kv);
+#define QAS_UNION_CASE(GG, NT)                                                            \
+  if (a.g == GG && a.S == 32 * NT) {                                                      \
+    hipLaunchKernelGGL((union_attn_kernel<GG, NT>), grid, dim3(kUPairThreads), 0, s, a); \
+    return hipGetLastError();                                                             \
   }
   QAS_UNION_CASE(1, 1) QAS_UNION_CASE(1, 2) QAS_UNION_CASE(2, 1) QAS_UNION_CASE(2, 2)
   QAS_UNION_CASE(4, 1) QAS_UNION_CASE(4, 2) QAS_UNION_CASE(8, 1) QAS_UNION_CASE(8, 2)
