@@ -252,8 +252,8 @@ __device__ __forceinline__ void attend_split(const int* s_phys, const int* s_nto
   // Wave w starts with batch w and then claims the lowest unclaimed batch
   // from an LDS counter, one batch ahead (the claim's round trip hides under
   // the current batch): the SIMDs favour the older of their two waves, so
-  // with fixed shares the first four waves finished ~3 us before the last
-  // four, which then streamed alone with half the loads in flight.
+  // with fixed shares of several batches the first four waves would finish
+  // well before the last four.
   __shared__ int s_next;
   if (tid == 0) s_next = NW;
   __syncthreads();
