@@ -248,24 +248,7 @@ __device__ __forceinline__ void attend_split(const int* s_phys, const int* s_nto
     for (int e = 0; e < EPL; ++e) acc[gg][e] = 0.f;
   }
 
-  // Batch k is units u0(k) + b NW, b < UNR, u0(k) = k % NW + (k / NW) NW UNR.
-  // Wave w starts with batch w and then claims the lowest unclaimed batch
-  // from an LDS counter, one batch ahead (the claim's round trip hides under
-  // the current batch): the SIMDs favour the older of their two waves, so
-  // with fixed shares of several batches the first four waves would finish
-  // well before the last four.
-  __shared__ int s_next;
-  if (tid == 0) s_next = NW;
-  __syncthreads();
-  auto batch_u0 = [&](int k) { return k % NW + (k / NW) * (NW * UNR); };
-  auto claim = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&s_next, 1);
-    return __shfl(v, 0, kWave);
-  };
-  int u0 = batch_u0(wave);
-  int kn = u0 < units ? claim() : 0;
-  while (u0 < units) {
+  for (int u0 = wave; u0 < units; u0 += NW * UNR) {
     uint4 kr[UNR], vr[UNR];
     bool ok[UNR];
     // Every load is unconditional: a unit past the end is clamped to the last
@@ -325,8 +308,6 @@ __device__ __forceinline__ void attend_split(const int* s_phys, const int* s_nto
       l_run[gg] = l;
       m_run[gg] = zmax;
     }
-    u0 = batch_u0(kn);
-    if (u0 < units) kn = claim();
   }
 
   attend_finish<DT, D, G, NW>(m_run, l_run, acc, o);
