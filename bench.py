@@ -80,11 +80,11 @@ PMC_TRAFFIC = {
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "7ba9efe26fb8947b09834125e45d0f8a41b574f8b298e7bddb2c179e38f6b773",
-    "fetch_kib": 69079.7,
+    "sources_sha256": "94fe1fdb0155d8bd3c5be11b560a31afedbb802e1ea0210e6e1b31443fefcc42",
+    "fetch_kib": 77628.8,
     "write_kib": 4224.0,
-    "mfma_busy_frac": 0.2548,
-    "valu_insts_per_mfma": 25.95,
+    "mfma_busy_frac": 0.2495,
+    "valu_insts_per_mfma": 24.49,
     "mfma_insts": 843732,
 }
 

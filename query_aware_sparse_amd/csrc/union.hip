@@ -15,9 +15,10 @@
 //      membership mask per page and its physical page;
 //   2. four waves per group (two of the first four and two of the last
 //      four, so that neither group's waves are all the younger ones on
-//      their SIMDs) stream its union pages, each claiming its next page
-//      from the group's LDS counter, so that the group's waves and both
-//      groups end together.  S^T = K Q^T with
+//      their SIMDs) stream its union pages, the older two taking 7 of
+//      every 24 pages each and the younger two 5, so that the group's
+//      waves and both groups end together (a fixed share keeps the result
+//      bitwise repeatable).  S^T = K Q^T with
 //      the fp8 K tile as A straight from HBM/L2 and Q quantised per row to
 //      e4m3 as B (v_mfma 32x32x64 f8f6f4); each lane then owns one row's
 //      logits, so the mask (membership, t <= c_i, t < L) and the online
@@ -250,6 +251,9 @@ __device__ __forceinline__ float lane_rowmax(float v) { return fmaxf(v, __shfl_x
 
 constexpr int kUPair = 2;                          // groups per workgroup
 constexpr int kUPairThreads = kUPair * kUThreads;  // 8 waves, two per SIMD
+// pages of a group: per kUCycle, kUOld to each older and kUYoung to each
+// younger wave (7:5, measured against 4:3, 5:4, 3:2 and an even split)
+constexpr int kUOld = 7, kUYoung = 5, kUCycle = 2 * (kUOld + kUYoung);
 
 // Wave w of the workgroup computes group (w ^ (w >> 2)) & 1 of its pair as
 // that group's wave w >> 1: each group gets two of the first four waves and
@@ -263,7 +267,6 @@ __global__ __launch_bounds__(kUPairThreads, 2) void union_attn_kernel(UnionArgs 
   constexpr int S = 32 * NT;                  // page size
   __shared__ UnionShared shu[kUPair];
   __shared__ __align__(16) float red_buf[kUPair][2][32][kUD + 2];   // wave merge per group
-  __shared__ int next_page[kUPair];
 
   const int H = a.H_kv;
   const int h = blockIdx.x % H;
@@ -337,10 +340,6 @@ __global__ __launch_bounds__(kUPairThreads, 2) void union_attn_kernel(UnionArgs 
       for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
   }
 
-  // the first kUWaves pages of a union go to its waves by index; the rest
-  // are claimed one at a time (the counters are read after the build's
-  // barriers)
-  if (threadIdx.x < kUPair) next_page[threadIdx.x] = kUWaves;
   build_union(shu[bh], a, grb, h, n_pages, pbeg, pre, btid);
   const int U = sh.count;
   const int cq = row_ok ? sh.cpos[qi] : -1;
@@ -437,16 +436,19 @@ __global__ __launch_bounds__(kUPairThreads, 2) void union_attn_kernel(UnionArgs 
   v8i_t ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (lane & 31) == 0 ? 0x38383838 : 0;
-  // A wave claims its next page one page ahead, so that the claim's
-  // round trip hides under the current page's work; pages go to whichever
-  // wave of the group asks first, so the group's waves end together
-  auto claim = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&next_page[unit], 1);
-    return __shfl(v, 0, kWave);
+  // Union pages per group wave, fixed so that the result does not depend
+  // on timing: of every kUCycle consecutive pages the group's two older
+  // waves (lw 0, 1: among the first four of the workgroup, favoured by
+  // their SIMDs' issue arbitration) take kUOld each and the two younger
+  // ones kUYoung each, interleaved, so that all four end together.
+  auto page_of = [&](int k) {
+    const int per = lw < 2 ? kUOld : kUYoung;
+    const int c = k / per, j = k - c * per;
+    return c * kUCycle + (lw < 2 ? 2 * j + lw : 2 * kUOld + 2 * j + (lw - 2));
   };
-  int u = lw;
-  int un = u < U ? claim() : U;
+  int kk = 0;
+  int u = page_of(0);
+  int un = page_of(1);
   if (u < U) {
     load_k(u, kop);
     load_v(u, vop);
@@ -542,7 +544,8 @@ __global__ __launch_bounds__(kUPairThreads, 2) void union_attn_kernel(UnionArgs 
                                                                 0, 0);
     load_v(ul, vop);
     u = un;
-    if (u < U) un = claim();
+    ++kk;
+    un = page_of(kk + 1);
   }
 
   // ---- merge each group's waves: 2,3 -> 0,1 then 1 -> 0 ---------------------

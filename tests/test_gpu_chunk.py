@@ -182,6 +182,28 @@ def test_chunk_attention_full_size(qas):
     assert np.all(np.isfinite(got))
 
 
+def test_chunk_attention_repeatable(qas):
+    """Bitwise repeatability: the full-size chunk call, ten times in a row,
+    gives the same output and LSE bits every time (each union page goes to
+    a fixed wave, and waves and groups merge in a fixed order)."""
+    from query_aware_sparse_amd.staging import ChunkBatch
+    case = multiquery_chunk()
+    cb = ChunkBatch([case])
+    first = None
+    for it in range(10):
+        out = torch.full((cb.N, case.H_q, case.d), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        lse = torch.full((cb.N, case.H_q), float("nan"), device="cuda")
+        qas.qas_chunk_attention(cb.cache, cb.db.batch, cb.q_indptr, cb.q_pos, cb.q, cb.sets,
+                                cb.group, 1.0 / np.sqrt(case.d), out, lse)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), f"call {it}"
+            assert torch.equal(lse.view(torch.int32), first[1].view(torch.int32)), f"call {it}"
+
+
 # ------------------------------------------------------------- regroup ----
 
 REGROUP_CAPACITY = 1024     # pages a request may have and still be regrouped
