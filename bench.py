@@ -431,7 +431,7 @@ def bench_chunk(args, NL=4, emit=True):
         call, event-timed us per call, calls)."""
         steps = max(NL, args.chunk_steps)
         ms, us = graph_time(torch, [lambda i=i: fn(i) for i in range(NL)], steps,
-                            max(NL, min(args.warmup, 8)))
+                            max(NL, min(args.warmup, 8)), out)
         return ms, us, steps
 
     # original order (the line's value), then the windowed regroup
