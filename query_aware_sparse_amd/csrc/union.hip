@@ -276,69 +276,58 @@ __global__ __launch_bounds__(kUPairThreads, 2) void union_attn_kernel(UnionArgs 
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // each half of the workgroup builds the union of one group of the pair ...
   const int bh = wave / kUWaves, btid = threadIdx.x % kUThreads;
-  const int gb = kUPair * pair + bh;
   // ... and each wave computes one group's pages
   const int unit = pair_unit(wave), lw = wave >> 1;
-  const int gc = kUPair * pair + unit;
   UnionShared& sh = shu[unit];
   // ---- per-lane row: row = query * G + head (S^T / O^T column = lane % 32)
   const int row = lane % 32, hf = lane / 32;
   const int qi = row / G, hq = row % G;
 
-  // In identity order a group's slots are guessed to start at group index *
-  // group size (one request whose queries start at 0, or requests whose
-  // query counts are multiples of the group): the guess's set entries and
-  // causal limits (built group) and query rows (computed group) are loaded
-  // before the groups are known, so that their latency overlaps the
-  // request-bound loads.  Slots are clamped to N - 1 (every load stays in
-  // bounds); a group the guess misses loads them again.
-  const int sqb = gb * a.group, sqc = gc * a.group;
+  GroupInfo grp[kUPair];
+  find_group_pair(a.q_indptr, a.B, a.group, kUPair * pair, grp);
+  if (grp[0].nq == 0) return;                 // uniform: no group in the pair
+  const GroupInfo grb = bh ? grp[1] : grp[0], grc = unit ? grp[1] : grp[0];
+  const bool row_ok = qi < grc.nq;
+  // Everything the union build and the query rows need is loaded together
+  // as soon as the groups are known: in identity order the built group's
+  // set entries and causal limits (with an execution order they follow
+  // the order's entries inside the build), the computed group's query rows,
+  // and the request bounds.  Slots are clamped to N - 1, so a group with
+  // fewer queries (or none) stays in bounds.
   PreSets pre;
+  pre.ok = a.ids == nullptr;
   uint4 qraw[8];
-  if (a.ids == nullptr) {
+  // computed group: Q row slice, dims 64*ks + 32*hf + [0, 32) for ks = 0, 1,
+  // quantised per row (a row past the group is zeroed)
+  auto load_q = [&](int qid) {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
+  };
+  // the query rows first: with an execution order their address waits for
+  // the order's entry, and that wait must not cover the set loads
+  const int cslot = min(grc.q0 + (row_ok ? qi : 0), a.N - 1);
+  load_q(a.ids ? a.ids[(size_t)h * a.N + cslot] : cslot);
+  if (pre.ok) {
     const int gkq = a.group * a.kq;
 #pragma unroll
     for (int k = 0; k < kUEpt; ++k) {
       const int e = min(btid + k * kUThreads, gkq - 1);
       const int i = e / a.kq;
-      const int qid = min(sqb + i, a.N - 1);
+      const int qid = min(grb.q0 + i, a.N - 1);
       pre.v[k] = a.sets[((size_t)qid * H + h) * a.kq + (e - i * a.kq)];
     }
-    pre.cpos = a.q_pos[min(sqb + (btid < kUMaxGroup ? btid : 0), a.N - 1)];
-    const int qid = min(sqc + qi, a.N - 1);
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
+    pre.cpos = a.q_pos[min(grb.q0 + (btid < kUMaxGroup ? btid : 0), a.N - 1)];
   }
-  __builtin_amdgcn_sched_barrier(0);
-
-  GroupInfo grp[kUPair];
-  find_group_pair(a.q_indptr, a.B, a.group, kUPair * pair, grp);
-  if (grp[0].nq == 0) return;                 // uniform: no group in the pair
-  const GroupInfo grb = bh ? grp[1] : grp[0], grc = unit ? grp[1] : grp[0];
   // built group: its request's pages (none for a group with no queries)
   const int Lb = grb.nq > 0 ? a.seq_lens[grb.r] : 0;
   const int pbeg = a.page_indptr[grb.r];
   const int P_r = a.page_indptr[grb.r + 1] - pbeg;
   const int n_pages = Lb > 0 ? min(min((Lb + S - 1) / S, P_r), kUMaxWords * 32) : 0;
-  pre.ok = a.ids == nullptr && grb.q0 == sqb;
-  // computed group: Q row slice, dims 64*ks + 32*hf + [0, 32) for ks = 0, 1,
-  // quantised per row (a row past the group is zeroed)
   const int L = a.seq_lens[grc.r];
-  const bool row_ok = qi < grc.nq;
-  if (!(a.ids == nullptr && grc.q0 == sqc)) {
-    const int slot = grc.q0 + (row_ok ? qi : 0);
-    const int qid = a.ids ? a.ids[(size_t)h * a.N + slot] : slot;
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((size_t)qid * a.H_q + h * G + hq) * kUD) * 2;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = load16(qp + (64 * ks + 32 * hf + 8 * c) * 2);
-  }
 
   build_union(shu[bh], a, grb, h, n_pages, pbeg, pre, btid);
   const int U = sh.count;
