@@ -80,10 +80,10 @@ PMC_TRAFFIC = {
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "94fe1fdb0155d8bd3c5be11b560a31afedbb802e1ea0210e6e1b31443fefcc42",
-    "fetch_kib": 77628.8,
+    "sources_sha256": "5e22704cb6f429ba432a08563ecbb5433917d851b9a2ef1df834cb7a28c7b44d",
+    "fetch_kib": 83017.5,
     "write_kib": 4224.0,
-    "mfma_busy_frac": 0.2495,
+    "mfma_busy_frac": 0.2491,
     "valu_insts_per_mfma": 24.49,
     "mfma_insts": 843732,
 }
