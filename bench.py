@@ -773,6 +773,91 @@ def bench_decode_case(torch, qas, args, case, copies, steps_per_copy=1, corrupt=
     return res
 
 
+SWEEP_LENGTHS = (2048, 4096, 8192, 16384, 32768, 65536)
+
+
+def bench_length_sweep(torch, qas, args, lengths=SWEEP_LENGTHS):
+    """Context-length scan of one decode layer of the headline shape (32
+    query = 32 KV heads, d = 128, S = 16, budget K = 256 pages, f16): per
+    length, full attention over every page (qas_sparse_decode on the whole
+    page list) against the Quest call (qas_decode_layer) and its stages
+    (qas_score_pages, qas_topk_pages, qas_sparse_decode on the selected
+    pages), each replayed from a HIP graph over enough cache copies that the
+    calls read at least 1 GiB of K/V between two visits of one copy.  K/V and
+    queries are N(0, 1) fp16 from a seeded device generator, identity page
+    table, summaries built by qas_append.  Below K * S tokens the budget
+    covers every page.  Lengths run from 2K to twice the headline context
+    (full attention through qas_sparse_decode takes rows of up to 4096
+    pages)."""
+    from query_aware_sparse_amd.staging import DeviceBatch, PagedCache
+    H, d, S, K = 32, 128, 16, 256
+    scale = 1.0 / math.sqrt(d)
+    gen = torch.Generator(device="cuda")
+    res = {"lengths": list(lengths), "quest_us": [], "dense_us": [], "score_us": [],
+           "topk_us": [], "attention_us": [], "copies": []}
+    for L in lengths:
+        P = L // S
+        kv_bytes = 2 * L * H * d * 2
+        NL = int(min(16, max(2, -(-(1 << 30) // kv_bytes))))
+        gen.manual_seed(1000 + L)
+        pcs = [PagedCache(P, H, S, d, "f16", poison=False)]
+        db = DeviceBatch([L], [np.arange(P, dtype=np.int32)], S)
+        empty = DeviceBatch([0], [np.arange(P, dtype=np.int32)], S)
+        before = qas.make_batch(empty.seq_lens, db.page_indptr, db.page_indices, db.total_pages,
+                                db.max_pages)
+        k = torch.randn((L, H, d), generator=gen, device="cuda").half()
+        v = torch.randn((L, H, d), generator=gen, device="cuda").half()
+        qas.qas_append(pcs[0].cache, before, torch.tensor([0, L], dtype=torch.int32,
+                                                          device="cuda"), L, L, k, v)
+        del k, v
+        for _ in range(1, NL):
+            pc = PagedCache(P, H, S, d, "f16", poison=False)
+            pc.k_pool.copy_(pcs[0].k_pool)
+            pc.v_pool.copy_(pcs[0].v_pool)
+            pc.summary.copy_(pcs[0].summary)
+            pcs.append(pc)
+        q = torch.randn((NL, 1, H, d), generator=gen, device="cuda").half()
+        out = torch.empty((NL, 1, H, d), dtype=torch.float16, device="cuda")
+        lse = torch.empty((NL, 1, H), device="cuda")
+        kk = min(K, P)
+        wsl = qas.make_workspace(qas.QAS_OP_DECODE_LAYER, pcs[0].cache, db.batch, H, kk)
+        wsd = qas.make_workspace(qas.QAS_OP_SPARSE_DECODE, pcs[0].cache, db.batch, H, P)
+        full = torch.arange(P, dtype=torch.int32, device="cuda").repeat(1, H, 1).contiguous()
+        scores = torch.empty((NL, P * H), device="cuda")
+        sel = torch.empty((NL, 1, H, kk), dtype=torch.int32, device="cuda")
+        quest = [lambda i=i: qas.qas_decode_layer(pcs[i].cache, db.batch, q[i], kk, scale,
+                                                  out[i], lse[i], wsl) for i in range(NL)]
+        dense = [lambda i=i: qas.qas_sparse_decode(pcs[i].cache, db.batch, q[i], full, P, scale,
+                                                   out[i], lse[i], wsd) for i in range(NL)]
+        score = [lambda i=i: qas.qas_score_pages(pcs[i].cache, db.batch, q[i], scores[i])
+                 for i in range(NL)]
+        topk = [lambda i=i: qas.qas_topk_pages(scores[i], db.batch, H, S, kk, sel[i])
+                for i in range(NL)]
+        attn = [lambda i=i: qas.qas_sparse_decode(pcs[i].cache, db.batch, q[i], sel[i], kk,
+                                                  scale, out[i], lse[i], wsd)
+                for i in range(NL)]
+        steps = max(NL, 64)
+        us = {}
+        for name, calls, chk in (("quest", quest, out), ("dense", dense, out),
+                                 ("score", score, scores), ("topk", topk, sel),
+                                 ("attention", attn, out)):
+            _, us[name] = graph_time(torch, calls, steps, NL, chk)
+            res[name + "_us"].append(round(us[name], 3))
+        res["copies"].append(NL)
+        log(f"[bench] length {L}: quest {us['quest']:.2f} us (score {us['score']:.2f}, top-k "
+            f"{us['topk']:.2f}, attention {us['attention']:.2f}), full attention "
+            f"{us['dense']:.2f} us, {NL} copies")
+        del pcs, db, empty, before, q, out, lse, wsl, wsd, full, scores, sel
+        _free(torch)
+    faster = [L for L, a, b in zip(lengths, res["quest_us"], res["dense_us"]) if a < b]
+    res["quest_faster_from"] = faster[0] if faster else None
+    res["note"] = ("per length: full attention = qas_sparse_decode over every page; quest = "
+                   "qas_decode_layer (score + top-K + attention) with K = 256 pages (4096 "
+                   "tokens; all pages below that); stages through their own entry points; "
+                   "graph replays over cache copies, event-timed")
+    return res
+
+
 def bench_stages(torch, qas, args, case, exact, db, qs, NL):
     """Stages of the headline call timed through their own entry points over
     the same layer caches: page scores (qas_score_pages), top-K
@@ -829,7 +914,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", choices=("all", "decode", "chunk", "config1", "config3",
-                                           "config5"), default="all",
+                                           "config5", "sweep"), default="all",
                     help="all: the headline line with every workload; the others time "
                          "one workload alone (profiling passes)")
     ap.add_argument("--micro", action="store_true",
@@ -882,6 +967,10 @@ def main():
                         "batched GQA decode with append (8 requests, 8K-64K, 32/8 heads, bf16)"),
             "config5": (lambda: stress_long_context(), 2,
                         "stress: 16 requests x 131072 tokens, 32/8 heads, S32, K41, fp16")}
+    if args.workload == "sweep":
+        res = bench_length_sweep(torch, qas, args)
+        print(json.dumps({"workload": "sweep", **res}), flush=True)
+        return
     if args.workload in subs:
         make, copies, what = subs[args.workload]
         res = bench_decode_case(torch, qas, args, make(), copies,
@@ -967,6 +1056,7 @@ def main():
         f"{call_us:.2f} us/call (events), {value:.1f} GB/s")
     del layers, exact, out, lse, ws, qs
     _free(torch)
+    sweep = bench_length_sweep(torch, qas, args) if args.workload == "all" else None
 
     # the other workloads, each with its own roofline fraction
     workloads = {}
@@ -1001,6 +1091,7 @@ def main():
                    "bytes_per_call": total, "bytes_parts": nbytes,
                    "single_call_p50_us": round(p50c, 3), "single_call_p95_us": round(p95c, 3),
                    "stages": stages,
+                   "length_sweep": sweep,
                    "fp8_summary_copy": {
                        "us_per_call": round(us_fp8, 3), "bytes_per_call": bytes_fp8,
                        "GB/s": round(bytes_fp8 / (us_fp8 * 1e-6) / 1e9, 1),
