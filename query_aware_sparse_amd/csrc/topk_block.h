@@ -49,8 +49,9 @@ constexpr float kTkMinRange = 1e-30f;
 
 struct TopkShared {
   __align__(16) int hist[kTkBins + 4];
-  int cidx[kTkCand];
-  float cval[kTkCand];
+  // candidates as 64-bit keys: order key of the score above the complement
+  // of the page index, so a larger key ranks higher (ties to the lower index)
+  __align__(16) uint64_t ckey[kTkCand];
   int scan[2][kTkMaxWaves];
   float mm[2 * kTkMaxWaves];
   int nslot, tj;
@@ -411,8 +412,12 @@ struct TopkRow {
       Ts = lo;
       Tj = uniform_i(sh.tj);
     } else {
-      // at most kTkCand (= ncand) candidates: gather them in any order (one
-      // LDS atomic per wave), rank each exactly by (score desc, index asc)
+      // at most kTkCand (= ncand) candidates: gather their keys in any order
+      // (one LDS atomic per wave) and rank each exactly by (score desc, index
+      // asc); the keys are distinct, so the ranks are 0 .. ncand - 1
+      const int total = ncand;
+      const int padded = (total + 7) & ~7;    // <= kTkCand; zero keys rank below all
+      for (int i = total + tid; i < padded; i += NT) sh.ckey[i] = 0ull;
       int mine = 0;
 #pragma unroll
       for (int k = 0; k < PT; ++k) mine += is_cand(k) ? 1 : 0;
@@ -426,26 +431,36 @@ struct TopkRow {
 #pragma unroll
           for (int k = 0; k < PT; ++k) {
             if (is_cand(k)) {
-              sh.cidx[at] = j0 + k;
-              sh.cval[at] = v[k];
+              sh.ckey[at] = ((uint64_t)order_key(v[k]) << 32) | (uint32_t)~(uint32_t)(j0 + k);
               ++at;
             }
           }
         }
       }
       __syncthreads();
-      const int total = ncand;
-      for (int i = tid; i < total; i += NT) {
-        const float si = sh.cval[i];
-        const int ji = sh.cidx[i];
-        int rank = 0;
-        for (int t = 0; t < total; ++t) {
-          const float st = sh.cval[t];
-          rank += ((st > si) | ((st == si) & (sh.cidx[t] < ji))) ? 1 : 0;
+      // two candidates per thread share every 16-byte broadcast read of the
+      // key list (a real key's order half is at least order_key(-inf) > 0,
+      // so the zero padding counts for none)
+      for (int i0 = tid; i0 < total; i0 += 2 * NT) {
+        const int i1 = i0 + NT;
+        const uint64_t ka = sh.ckey[i0];
+        const uint64_t kb = i1 < total ? sh.ckey[i1] : ~0ull;
+        int ra = 0, rb = 0;
+        for (int t = 0; t < padded; t += 8) {
+          const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(sh.ckey + t);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const ulonglong2 x = kp[u];
+            ra += (x.x > ka ? 1 : 0) + (x.y > ka ? 1 : 0);
+            rb += (x.x > kb ? 1 : 0) + (x.y > kb ? 1 : 0);
+          }
         }
-        if (rank == kk - 1) {
-          sh.ts = si;
-          sh.tj = ji;
+        const bool hit_a = ra == kk - 1, hit_b = i1 < total && rb == kk - 1;
+        if (hit_a | hit_b) {
+          const uint64_t key = hit_a ? ka : kb;
+          const uint32_t ok = (uint32_t)(key >> 32);
+          sh.ts = __uint_as_float((ok & 0x80000000u) ? (ok ^ 0x80000000u) : ~ok);
+          sh.tj = (int)~(uint32_t)key;
         }
       }
       __syncthreads();
