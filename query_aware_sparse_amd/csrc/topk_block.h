@@ -438,29 +438,36 @@ struct TopkRow {
         }
       }
       __syncthreads();
-      // two candidates per thread share every 16-byte broadcast read of the
-      // key list (a real key's order half is at least order_key(-inf) > 0,
-      // so the zero padding counts for none)
-      for (int i0 = tid; i0 < total; i0 += 2 * NT) {
-        const int i1 = i0 + NT;
-        const uint64_t ka = sh.ckey[i0];
-        const uint64_t kb = i1 < total ? sh.ckey[i1] : ~0ull;
-        int ra = 0, rb = 0;
+      // CPT candidates per thread (2 in a 256-thread workgroup, 1 in a
+      // 512-thread one) share every 16-byte broadcast read of the key list
+      // (a real key's order half is at least order_key(-inf) > 0, so the
+      // zero padding counts for none)
+      constexpr int CPT = (kTkCand + NT - 1) / NT;
+      for (int i0 = tid; i0 < total; i0 += CPT * NT) {
+        uint64_t kc[CPT];
+        int rk[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int i = i0 + c * NT;
+          kc[c] = i < total ? sh.ckey[i] : ~0ull;
+          rk[c] = 0;
+        }
         for (int t = 0; t < padded; t += 8) {
           const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(sh.ckey + t);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const ulonglong2 x = kp[u];
-            ra += (x.x > ka ? 1 : 0) + (x.y > ka ? 1 : 0);
-            rb += (x.x > kb ? 1 : 0) + (x.y > kb ? 1 : 0);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) rk[c] += (x.x > kc[c] ? 1 : 0) + (x.y > kc[c] ? 1 : 0);
           }
         }
-        const bool hit_a = ra == kk - 1, hit_b = i1 < total && rb == kk - 1;
-        if (hit_a | hit_b) {
-          const uint64_t key = hit_a ? ka : kb;
-          const uint32_t ok = (uint32_t)(key >> 32);
-          sh.ts = __uint_as_float((ok & 0x80000000u) ? (ok ^ 0x80000000u) : ~ok);
-          sh.tj = (int)~(uint32_t)key;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          if (i0 + c * NT < total && rk[c] == kk - 1) {
+            const uint32_t ok = (uint32_t)(kc[c] >> 32);
+            sh.ts = __uint_as_float((ok & 0x80000000u) ? (ok ^ 0x80000000u) : ~ok);
+            sh.tj = (int)~(uint32_t)kc[c];
+          }
         }
       }
       __syncthreads();
