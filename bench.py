@@ -57,11 +57,11 @@ DECODE_SOURCES = ("score.hip", "decode.hip", "decode_f32.hip", "decode_f16.hip",
                   "decode_bf16.hip", "decode_kernel.h", "attend_block.h", "topk_block.h",
                   "qas_device.h", "qas_internal.h", "qas_api.cpp")
 PMC_TRAFFIC = {
-    "sources_sha256": "b938b66ea0b2f772e773d22d16a6b913dc013094b04437193dbf01b4bb154725",
-    "fetch_kib": {"score_kernel": 16533.5, "decode_kernel": 34061.6},
-    "write_kib": {"score_kernel": 597.4, "decode_kernel": 173.3},
+    "sources_sha256": "d992bcc9e130fa29dc5ce6792659964230bc495f80d9e4d07fa9ce1ffec0783b",
+    "fetch_kib": {"score_kernel": 16532.9, "decode_kernel": 34066.5},
+    "write_kib": {"score_kernel": 597.9, "decode_kernel": 173.3},
     # the same passes, call on the e4m3 summary copy
-    "fetch_kib_fp8": {"score8_kernel": 8493.0, "decode_kernel": 34061.6},
+    "fetch_kib_fp8": {"score8_kernel": 8493.0, "decode_kernel": 34066.5},
     "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.3},
     "fetch_factor": 2.0,
     "write_factor": 1.0,

@@ -122,7 +122,9 @@ def _topk_scores(kind, total, rng):
 
 
 TOPK_KINDS = ["ints", "normal", "zeros", "cluster", "huge", "subnormal"]
-TOPK_ROWS = {"short": [1, 300, 2048, 1000, 77], "long": [4097, 16384, 9000]}
+TOPK_ROWS = {"short": [1, 300, 2048, 1000, 77], "long": [4097, 16384, 9000],
+             # around the 512 candidates ranked directly from LDS
+             "edge": [512, 511, 513, 65, 64]}
 
 
 @pytest.mark.parametrize("rows", list(TOPK_ROWS))

@@ -212,6 +212,26 @@ def test_page_sizes(qas, S, H_q):
         assert np.array_equal(summ[phys, :, 0], m) and np.array_equal(summ[phys, :, 1], M)
 
 
+@pytest.mark.parametrize("pages", [511, 512, 513])
+@pytest.mark.parametrize("H_q", [2, 8])
+def test_select_around_the_direct_rank(qas, pages, H_q):
+    """Rows of 511, 512 and 513 pages at K = 256, one KV head per query head
+    and groups of 4: the attention kernel ranks a row of at most 512 scores
+    directly and histograms a longer one first; both give the oracle's set,
+    before and after one append."""
+    case = batched_gqa_append(seed=90 + pages + H_q, B=2, L_min=pages * 16 - 15,
+                              L_max=pages * 16, H_q=H_q, H_kv=2, d=128, S=16, K=256, steps=1)
+    say(f"[e2e] {pages} pages, {H_q} query heads: lengths={case.seq_lens.tolist()}")
+    lay = Layer(qas, case)
+    decoded = {r: oracle.decoded_kv(case, r) for r in range(case.B)}
+    reqs = list(range(case.B))
+    for step in range(-1, case.steps):
+        out, lse, sel, db = lay.call(step=step, append=step >= 0)
+        ref = oracle.run_decode(case, step=step, requests=reqs, decoded=decoded)
+        compare(case, out, lse, sel, ref, reqs, lay.scores(db, step) if step == -1 else None,
+                db, step=step, decoded=decoded)
+
+
 def test_stress_long_context(qas):
     """16 requests at 131072 tokens, 32/8 heads, S=32, K=41, Student-t keys,
     fp16: decode-layer call checked on a seeded sample of requests; then
