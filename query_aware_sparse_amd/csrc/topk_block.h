@@ -23,7 +23,9 @@
 //     over that lane's bins the bin); scores in higher bins are taken and
 //     that bin's scores are the candidates (if still too many, [lo, hi]
 //     shrinks to their exact min/max and the step repeats; the bin misses
-//     lo or hi, so each repeat drops at least one distinct value);
+//     lo or hi, so each repeat drops at least one distinct value); a row
+//     of no more than kTkDirect scores skips the histogram, and one of up
+//     to kTkCand takes at most kTkSmallRounds rounds;
 //   * rank the candidates exactly by (score desc, index asc).  The last one
 //     taken is the threshold (T_s, T_j): page j is selected iff s_j > T_s,
 //     or s_j == T_s and j <= T_j.
@@ -45,6 +47,11 @@ constexpr int kTkThreads = 256;      // workgroup of the standalone top-K kernel
 constexpr int kTkMaxWaves = 8;       // largest workgroup a row select runs in
 constexpr int kTkBins = 1024;
 constexpr int kTkCand = 512;         // candidates ranked from LDS
+// Ranking n candidates costs each thread ~n / 2 broadcast reads, so rows
+// whose candidates number more than kTkDirect take histogram rounds first
+// (at most kTkSmallRounds of them while they number no more than kTkCand).
+constexpr int kTkDirect = 64;
+constexpr int kTkSmallRounds = 2;
 constexpr float kTkMinRange = 1e-30f;
 
 struct TopkShared {
@@ -309,7 +316,11 @@ struct TopkRow {
     int cbin = -1;                             // bin of the candidates (last round)
     int bk[PT];                                // element bins of the last round
     int round = 0;
-    while (ncand > kTkCand && lo < hi) {
+    // more rounds pay while the candidates are many (the rank is quadratic)
+    auto narrow = [&](int nc, int r) {
+      return nc > kTkCand || (nc > kTkDirect && r < kTkSmallRounds);
+    };
+    while (narrow(ncand, round) && lo < hi) {
       bin.init(lo, hi);
       if (round > 0) {
         for (int b = tid; b < kTkBins + 4; b += NT) sh.hist[b] = 0;
@@ -375,7 +386,7 @@ struct TopkRow {
         ncand = __builtin_amdgcn_readlane(ci, at);
       }
       ++round;
-      if (ncand <= kTkCand) break;
+      if (!narrow(ncand, round)) break;
       // too many left: shrink [lo, hi] to the crossing bin's exact extremes
       // (it misses lo or hi, so every round drops at least one value)
       float nlo = FLT_MAX, nhi = -FLT_MAX;
