@@ -57,11 +57,11 @@ DECODE_SOURCES = ("score.hip", "decode.hip", "decode_f32.hip", "decode_f16.hip",
                   "decode_bf16.hip", "decode_kernel.h", "attend_block.h", "topk_block.h",
                   "qas_device.h", "qas_internal.h", "qas_api.cpp")
 PMC_TRAFFIC = {
-    "sources_sha256": "2c9d037b7152644bfe39e047e7b585981f94ff63894d6106e0dac207010616f5",
-    "fetch_kib": {"score_kernel": 16532.9, "decode_kernel": 34066.9},
-    "write_kib": {"score_kernel": 597.9, "decode_kernel": 173.3},
+    "sources_sha256": "5cf883cfe4fb445a17a33b65db9369b240935f5e2461ce6f8bdf94b2d1d27184",
+    "fetch_kib": {"score_kernel": 16533.4, "decode_kernel": 34067.4},
+    "write_kib": {"score_kernel": 597.1, "decode_kernel": 173.3},
     # the same passes, call on the e4m3 summary copy
-    "fetch_kib_fp8": {"score8_kernel": 8492.9, "decode_kernel": 34066.9},
+    "fetch_kib_fp8": {"score8_kernel": 8492.9, "decode_kernel": 34067.4},
     "write_kib_fp8": {"score8_kernel": 304.3, "decode_kernel": 173.3},
     "fetch_factor": 2.0,
     "write_factor": 1.0,
@@ -80,10 +80,10 @@ PMC_TRAFFIC = {
 # Valid only for CHUNK_SOURCES.
 CHUNK_SOURCES = ("union.hip", "qas_device.h", "qas_internal.h", "qas_api.cpp")
 CHUNK_PMC_TRAFFIC = {
-    "sources_sha256": "5e22704cb6f429ba432a08563ecbb5433917d851b9a2ef1df834cb7a28c7b44d",
-    "fetch_kib": 83017.5,
+    "sources_sha256": "f73f478306270a4102acb4715cc6b9938f952540c24e251c3af787d2d2a81d55",
+    "fetch_kib": 83799.2,
     "write_kib": 4224.0,
-    "mfma_busy_frac": 0.2491,
+    "mfma_busy_frac": 0.2516,
     "valu_insts_per_mfma": 24.49,
     "mfma_insts": 843732,
 }

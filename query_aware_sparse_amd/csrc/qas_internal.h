@@ -53,7 +53,7 @@ struct TopkArgs {
   int sel_stride;            // row stride of sel / sel_phys (>= the row's count)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-constexpr int kTopkMaxPages = 16384;  // 256 threads x 64 scores held in registers
+constexpr int kTopkMaxPages = 16384;  // 512 threads x 32 scores held in registers
 
 struct AppendArgs {
   void* k_pool;

@@ -2,8 +2,8 @@
 // second stage ("3.1.1 · Quest", §1 and Fig. 1), ordered by (score
 // descending, page index ascending), joined with the fixed sink and
 // local-window pages when asked (§3.2), written in ascending page order and
-// padded with -1.  One workgroup per row runs the register-resident
-// histogram select of topk_block.h.
+// padded with -1.  One 512-thread workgroup per row runs the
+// register-resident histogram select of topk_block.h.
 #include "qas_device.h"
 #include "qas_internal.h"
 #include "topk_block.h"
@@ -56,14 +56,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int m = a.max_pages > 0 ? a.max_pages : 1;
   dim3 grid(a.B * a.H_kv);
   dim3 block(kTkThreads);
-  if (m <= kTkThreads * 8) {
+  if (m <= kTkThreads * 4) {
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
+  } else if (m <= kTkThreads * 8) {
     hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
   } else if (m <= kTkThreads * 16) {
     hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a);
   } else if (m <= kTkThreads * 32) {
     hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, a);
-  } else if (m <= kTkThreads * 64) {
-    hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -43,7 +43,7 @@
 
 namespace qas {
 
-constexpr int kTkThreads = 256;      // workgroup of the standalone top-K kernel
+constexpr int kTkThreads = 512;      // workgroup of the standalone top-K kernel
 constexpr int kTkMaxWaves = 8;       // largest workgroup a row select runs in
 constexpr int kTkBins = 1024;
 constexpr int kTkCand = 512;         // candidates ranked from LDS
